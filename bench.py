@@ -1,0 +1,292 @@
+"""Benchmark: one verification step of tree attention on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+tree_attn_build_mask -> tree_attn_forward -> tree_verify_greedy.  The default
+workload is the Llama-3-8B-shaped layer (B=1, Hq=32, Hkv=8, D=128, prefix
+L=4096, a 64-node draft tree of depth <= 6 and branching <= 4, bf16), with
+greedy verification over a 64 x 128256 bf16 logits block (draft token equal to
+the target argmax with probability 0.6).
+
+Inputs are resident in HBM before timing starts.  To keep the 256 MB Infinity
+Cache from serving repeated reads, the step rotates over --sets copies of every
+input (16 x ~35 MB by default), so each step reads cold data.
+
+Prints ONE JSON line: tree-tokens/s of the whole step (value), plus per-call
+device times from HIP events on the launch stream, the roofline of the
+dominant kernel, and the fp64 CPU oracle timed on a bounded sample of the same
+workload (cpu_baseline).
+
+    python bench.py [--steps K] [--warmup W] [--config llama3_8b] [--sets 16]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="llama3_8b")
+    p.add_argument("--sets", type=int, default=16)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "tree_masked_attention_forward_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, current_hash):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, or None
+    when absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, "pmc_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != current_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path: sequences, KV heads or prefix chunks would shard across GPUs "
+              "with an LSE merge, which is not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synthetic
+    import tree_masked_attention_forward_amd as ta
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = synthetic.make_config_case(args.config, with_logits=True)
+    B, Hq, Hkv, D = case.B, case.Hq, case.Hkv, case.D
+    sum_n, sum_l = case.total_nodes, case.total_prefix
+    max_nodes, max_prefix = case.max_nodes, case.max_prefix
+    V = case.vocab
+    W = ta.mask_words(max_nodes)
+
+    # --- resident inputs, rotated over `sets` copies --------------------------------------
+    base = {
+        "parents": torch.from_numpy(case.parents).to(dev),
+        "noffs": torch.from_numpy(case.node_offsets).to(dev),
+        "poffs": torch.from_numpy(case.prefix_offsets).to(dev),
+        "q": case.q.to(dev), "kt": case.k_tree.to(dev), "vt": case.v_tree.to(dev),
+        "kp": case.k_prefix.to(dev), "vp": case.v_prefix.to(dev),
+        "logits": case.logits.to(dev), "draft": torch.from_numpy(case.draft).to(dev),
+    }
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(args.sets - 1)]
+    mask = torch.empty((sum_n, W), dtype=torch.uint64, device=dev)
+    depth = torch.empty(sum_n, dtype=torch.int32, device=dev)
+    status = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty_like(base["q"])
+    fws = torch.empty(max(ta.forward_workspace_size(case.dtype, B, sum_n, max_nodes, Hq, Hkv, D,
+                                                    sum_l, max_prefix), 16),
+                      dtype=torch.uint8, device=dev)
+    vws = torch.empty(max(ta.verify_workspace_size(sum_n, max_nodes, V), 16), dtype=torch.uint8,
+                      device=dev)
+    pred = torch.empty(sum_n, dtype=torch.int32, device=dev)
+    alen = torch.empty(B, dtype=torch.int32, device=dev)
+    anodes = torch.empty((B, max_nodes), dtype=torch.int32, device=dev)
+    atok = torch.empty((B, max_nodes), dtype=torch.int32, device=dev)
+
+    def do_mask(s):
+        ta.build_mask(s["parents"], s["noffs"], max_nodes, mask=mask, depth=depth, status=status)
+
+    def do_forward(s):
+        ta.forward(s["q"], s["kt"], s["vt"], s["kp"], s["vp"], s["poffs"], s["noffs"], mask,
+                   max_nodes, max_prefix, case.scale, out=out, workspace=fws)
+
+    def do_verify(s):
+        ta.verify_greedy(s["logits"], s["draft"], mask, s["noffs"], max_nodes, workspace=vws,
+                         target_argmax=pred, accept_len=alen, accept_nodes=anodes,
+                         accept_tokens=atok)
+
+    def step(i):
+        s = sets[i % len(sets)]
+        do_mask(s)
+        do_forward(s)
+        do_verify(s)
+
+    # --- whole-step timing ----------------------------------------------------------------
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = sum_n * args.steps / elapsed
+    print(f"[bench] {args.steps} steps in {elapsed:.4f} s", file=sys.stderr, flush=True)
+
+    # --- per-call device time with HIP events on the launch stream ------------------------
+    stream = torch.cuda.current_stream(dev)
+
+    def event_time(fn, n):
+        for i in range(3):
+            fn(sets[i % len(sets)])
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(n):
+            fn(sets[i % len(sets)])
+        end.record(stream)
+        end.synchronize()
+        return start.elapsed_time(end) * 1e3 / n   # microseconds per call
+
+    do_mask(sets[0])
+    t_mask = event_time(do_mask, args.steps)
+    t_fwd = event_time(do_forward, args.steps)
+    t_ver = event_time(do_verify, args.steps)
+    print(f"[bench] per call us: mask {t_mask:.2f} forward {t_fwd:.2f} verify {t_ver:.2f}",
+          file=sys.stderr, flush=True)
+
+    # --- algorithmic bytes / flops --------------------------------------------------------
+    depth_h = depth.cpu().numpy().astype(np.int64)
+    kv_bytes = 2 * sum_l * Hkv * D * 2 + 2 * sum_n * Hkv * D * 2
+    fwd_bytes = kv_bytes + 2 * sum_n * Hq * D * 2 + sum_n * W * 8
+    lens = np.diff(case.prefix_offsets).astype(np.int64)
+    nn = np.diff(case.node_offsets).astype(np.int64)
+    fwd_flops = 4 * Hq * D * (int((nn * lens).sum()) + int((depth_h + 1).sum()))
+    ver_bytes = sum_n * V * 2 + sum_n * 4 + sum_n * W * 8 + sum_n * 4 + B * (1 + 2 * max_nodes) * 4
+    fwd_hash = src_hash("attn_fwd.hip")
+    ver_hash = src_hash("verify.hip")
+
+    fwd_gbs = fwd_bytes / (t_fwd * 1e-6) / 1e9
+    fwd_tfs = fwd_flops / (t_fwd * 1e-6) / 1e12
+    t_roof_fwd = max(fwd_bytes / (HBM_PEAK_GBS * 1e9), fwd_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    ver_gbs = ver_bytes / (t_ver * 1e-6) / 1e9
+    fwd_bound = "hbm" if fwd_bytes / (HBM_PEAK_GBS * 1e9) >= fwd_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma"
+
+    def roof(kind):
+        if kind == "forward":
+            if fwd_bound == "hbm":
+                r = {"bound": "hbm", "achieved": round(fwd_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(fwd_gbs / HBM_PEAK_GBS, 4)}
+            else:
+                r = {"bound": "mfma", "achieved": round(fwd_tfs, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fwd_tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
+            r["traffic"] = load_traffic("tree_attn_forward", fwd_hash)
+            r["kernel"] = "tree_attn_forward"
+            return r
+        r = {"bound": "hbm", "achieved": round(ver_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(ver_gbs / HBM_PEAK_GBS, 4),
+             "traffic": load_traffic("tree_verify_greedy", ver_hash), "kernel": "tree_verify_greedy"}
+        return r
+
+    dominant = "forward" if t_fwd >= t_ver else "verify"
+    other = "verify" if dominant == "forward" else "forward"
+
+    # --- CPU baseline: the fp64 oracle on a bounded sample ----------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, args.cpu_seconds)
+
+    line = {
+        "metric": "tree-tokens/s and achieved KV GB/s (% roofline), Llama-3-8B shape, N=64, L=4096",
+        "value": round(value, 1),
+        "unit": "tree-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.config}: B={B} Hq={Hq} Hkv={Hkv} D={D} L={max_prefix} N={max_nodes} "
+                        f"(sum_L={sum_l}, sum_N={sum_n}); greedy verify over V={V} bf16 logits",
+            "step": "build_mask + forward + verify_greedy, inputs rotated over "
+                    f"{args.sets} resident copies",
+            "global_batch": B, "seq_len": max_prefix, "tree_nodes": sum_n,
+        },
+        "roofline": roof(dominant),
+        "cpu_baseline": cpu,
+        "detail": {
+            "us_per_call": {"build_mask": round(t_mask, 3), "forward": round(t_fwd, 3),
+                            "verify": round(t_ver, 3)},
+            "forward": {"tree_tokens_per_s": round(sum_n / (t_fwd * 1e-6), 1),
+                        "kv_GBps": round(kv_bytes / (t_fwd * 1e-6) / 1e9, 1),
+                        "alg_GBps": round(fwd_gbs, 1), "alg_TFLOPs": round(fwd_tfs, 2),
+                        "alg_bytes": fwd_bytes, "alg_flops": fwd_flops,
+                        "t_roof_us": round(t_roof_fwd * 1e6, 3),
+                        "roofline_frac": round(t_roof_fwd / (t_fwd * 1e-6), 4)},
+            "verify": {"alg_bytes": ver_bytes, "alg_GBps": round(ver_gbs, 1)},
+            "roofline_other": roof(other),
+            "source_hash": {"attn_fwd.hip": fwd_hash, "verify.hip": ver_hash},
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(case, seconds):
+    """The fp64 oracle as it stands, on whole steps of the same workload
+    (mask + attention of every node + greedy verification), repeated until
+    about `seconds` of CPU work; tree-tokens per second."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_info = threadpool_limits = None
+    share = min(len(os.sched_getaffinity(0)), 16)
+    limiter = threadpool_limits(limits=share) if threadpool_limits else None
+    reps, t0 = 0, time.perf_counter()
+    try:
+        while True:
+            oracle.build_mask(case.parents, case.node_offsets, case.max_nodes)
+            oracle.tree_attention(case.q, case.k_tree, case.v_tree, case.k_prefix, case.v_prefix,
+                                  case.parents, case.node_offsets, case.prefix_offsets, case.scale)
+            oracle.verify_greedy(case.logits, case.draft, case.parents, case.node_offsets,
+                                 case.max_nodes)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or reps >= 20:
+                break
+        threads = share
+        if threadpool_info:
+            infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+            if infos:
+                threads = max(i["num_threads"] for i in infos)
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
+    return {"value": round(case.total_nodes * reps / el, 2), "unit": "tree-tokens/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} whole step(s) of {case.name} (all {case.total_nodes} nodes, mask + "
+                      f"fp64 attention + greedy verify over V={case.vocab}) in {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+/*
+ * tree_attn.h - C ABI of libtreeattn.so: tree attention and greedy tree
+ * verification on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (the pages it follows):
+ *   - "Tree Attention", inferensys.com glossary, section "Key Mechanisms of
+ *     Tree Attention" (Modified Causal Attention Mask; Speculative KV Cache
+ *     Reuse; Multi-Token Acceptance & Rollback).
+ *   - "Tree Attention", zhongzhoutan-coder.github.io glossary term, sections
+ *     "How It Works" and "Common Confusions".
+ *   - "Speculative Tree Attention: How Multi-Candidate Draft Models and
+ *     Parallel Verification Deliver 4x LLM Speedups", news.premlal.in, its
+ *     code listing (build_tree_attention_mask, verify_candidate_tree).
+ *
+ * A draft tree is flattened into one token sequence in topological order: in
+ * sequence b, node i (local index 0..N_b-1) has parent[i] = -1 (a root; more
+ * than one root makes a forest) or 0 <= parent[i] < i.  Every node attends to
+ * the sequence's whole verified prefix (the KV cache), to itself and to its
+ * ancestors, and to nothing else: no sibling, no node of another branch or
+ * another tree.
+ *
+ * Conventions shared by every call:
+ *   - Array arguments are DEVICE pointers unless marked [host].  Every buffer is
+ *     allocated and owned by the caller; the library allocates nothing, keeps
+ *     no state between calls, and never synchronises the stream.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     All work is enqueued on it; the call returns before the work finishes.
+ *   - Return value: TA_OK, or an error code for anything the host can check
+ *     (null pointers, bad sizes, unsupported shapes, short workspace).  On an
+ *     error nothing is enqueued.  Problems only visible in device data (a
+ *     malformed parent array, offsets that do not fit the stated sizes) are
+ *     reported per sequence in `tree_status` by tree_attn_build_mask; the other
+ *     kernels clamp such offsets so that they never read or write out of
+ *     bounds, and skip the sequence.
+ *   - Tensors are contiguous, row-major in the layouts given, 16-byte aligned.
+ *   - sum_N = total_nodes = node_offsets[B]; sum_L = total_prefix =
+ *     prefix_offsets[B]; W = ceil(max_nodes / 64) mask words per node.
+ *   - Limits: 1 <= max_nodes <= TA_MAX_NODES; bf16 attention needs D == 128;
+ *     fp32 attention needs 1 <= D <= 256; Hq % Hkv == 0.
+ */
+#ifndef TREE_ATTN_H
+#define TREE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TA_MAX_NODES 1024
+
+#if defined(__GNUC__) || defined(__clang__)
+#define TA_API __attribute__((visibility("default")))
+#else
+#define TA_API
+#endif
+
+typedef enum {
+  TA_OK = 0,
+  TA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad offsets */
+  TA_ERR_INVALID_TREE = 2,  /* parent array is not a topologically ordered forest */
+  TA_ERR_UNSUPPORTED = 3,   /* head size / dtype / node count outside the limits */
+  TA_ERR_WORKSPACE = 4,     /* workspace missing or smaller than the size query */
+  TA_ERR_HIP = 5            /* a HIP runtime call failed */
+} ta_status;
+
+typedef enum { TA_F32 = 0, TA_BF16 = 1 } ta_dtype;
+
+/*
+ * Ancestor bitmask and depth from a parent array.
+ *
+ * Follows: inferensys "Tree Attention", Modified Causal Attention Mask (a node
+ * sees its ancestral path and itself, never a sibling branch); premlal listing,
+ * build_tree_attention_mask (mark self, then walk parent pointers to the root),
+ * here packed to bits instead of a dense N x N boolean matrix.
+ *
+ *   parents       int32 [sum_N]   local parent index, -1 for a root.
+ *   node_offsets  int32 [B+1]     sequence b owns nodes node_offsets[b] ..
+ *                                 node_offsets[b+1]-1; node_offsets[0] == 0.
+ *   B, total_nodes, max_nodes [host]; every N_b <= max_nodes.
+ *   mask   out uint64 [sum_N][W]: bit t (LSB = 0) of word w of node i's row is
+ *          set iff local node 64*w + t is i or an ancestor of i; unused high
+ *          bits are 0.
+ *   depth  out int32 [sum_N], nullable: root = 0.
+ *   tree_status out int32 [B], nullable: per sequence TA_OK;
+ *          TA_ERR_INVALID_TREE if some parent is outside {-1} U [0, i) (then the
+ *          sequence's mask rows are 0 and its depths -1); TA_ERR_INVALID_ARG if
+ *          its offsets are decreasing, exceed max_nodes or total_nodes (then
+ *          its rows are not written).
+ * The mask is computed once per verification step and reused by every layer.
+ */
+TA_API int tree_attn_build_mask(const int32_t* parents, const int32_t* node_offsets, int32_t B,
+                         int32_t total_nodes, int32_t max_nodes, uint64_t* mask,
+                         int32_t* depth, int32_t* tree_status, void* stream);
+
+/*
+ * Bytes of device workspace tree_attn_forward needs for these host sizes
+ * (0 is a valid answer).  Pure host arithmetic; calls no HIP function.
+ */
+TA_API size_t tree_attn_forward_workspace_size(int dtype, int32_t B, int32_t total_nodes,
+                                        int32_t max_nodes, int32_t Hq, int32_t Hkv, int32_t D,
+                                        int64_t total_prefix, int64_t max_prefix);
+
+/*
+ * Tree attention forward: for every node i of sequence b and query head h,
+ *   keys(i)   = prefix rows of b (all of them) + tree rows of i's ancestors and i,
+ *   out[i][h] = softmax(scale * q[i][h] . keys(i)) @ values(i),
+ *   lse[i][h] = log(sum(exp(scale * q[i][h] . keys(i))))   (natural log),
+ * with KV head g = h / (Hq / Hkv).
+ *
+ * Follows: inferensys "Tree Attention", Modified Causal Attention Mask and
+ * Speculative KV Cache Reuse (the tree's own K/V rows are inputs, reused from
+ * the draft or recomputed by the caller); zhongzhoutan "Tree Attention", How It
+ * Works (every node also sees the verified prefix).
+ *
+ *   dtype          TA_BF16 (q/k/v/out bf16, fp32 accumulation; D == 128) or
+ *                  TA_F32 (everything fp32; 1 <= D <= 256).
+ *   q              [sum_N][Hq][D]   queries of the tree nodes (already rotated).
+ *   k_tree, v_tree [sum_N][Hkv][D]  keys/values of the tree nodes.
+ *   k_prefix, v_prefix [sum_L][Hkv][D] verified-prefix KV cache, sequences
+ *                  packed back to back.
+ *   prefix_offsets int64 [B+1]  sequence b's prefix rows are
+ *                  prefix_offsets[b] .. prefix_offsets[b+1]-1 (L_b may be 0).
+ *   node_offsets   int32 [B+1]  as for tree_attn_build_mask.
+ *   mask           uint64 [sum_N][W] from tree_attn_build_mask.
+ *   B, total_nodes, max_nodes, total_prefix, max_prefix, Hq, Hkv, D, scale [host].
+ *   out            out [sum_N][Hq][D], dtype as the inputs.
+ *   lse            out fp32 [sum_N][Hq], nullable.
+ *   workspace      device buffer of at least tree_attn_forward_workspace_size()
+ *                  bytes (may be NULL when that size is 0); contents on entry
+ *                  do not matter; calls sharing one workspace must be ordered
+ *                  on one stream.
+ */
+TA_API int tree_attn_forward(int dtype, const void* q, const void* k_tree, const void* v_tree,
+                      const void* k_prefix, const void* v_prefix,
+                      const int64_t* prefix_offsets, const int32_t* node_offsets,
+                      const uint64_t* mask, int32_t B, int32_t total_nodes, int32_t max_nodes,
+                      int64_t total_prefix, int64_t max_prefix, int32_t Hq, int32_t Hkv,
+                      int32_t D, float scale, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace tree_verify_greedy needs.  Pure host arithmetic.
+ */
+TA_API size_t tree_verify_greedy_workspace_size(int32_t total_nodes, int32_t max_nodes, int32_t V);
+
+/*
+ * Greedy tree verification: target argmax per node, then the longest
+ * root-to-node path whose draft tokens all equal the target's argmax.
+ *
+ * Follows: inferensys "Tree Attention", Multi-Token Acceptance & Rollback and
+ * Integration with Speculative Decoding (accept the longest verified branch
+ * from the root); premlal listing, verify_candidate_tree (argmax of the target
+ * logits, draft compared with prediction node by node), walked along tree
+ * paths instead of the flat order, which coincide on a chain.
+ *
+ *   logits_dtype   TA_BF16 or TA_F32.
+ *   logits         [sum_N][V]; row i is the target's distribution for the
+ *                  token at node i (the caller gathers it from the target
+ *                  output at the node's parent, or at the prefix's last
+ *                  position for a root).
+ *   draft_tokens   int32 [sum_N].
+ *   mask           uint64 [sum_N][W] from tree_attn_build_mask.
+ *   node_offsets   int32 [B+1].
+ *   B, total_nodes, max_nodes, V [host].
+ *   target_argmax  out int32 [sum_N], nullable: lowest index of the row max
+ *                  (values compared exactly; -0 equals +0).
+ *   accept_len     out int32 [B]: nodes on the accepted path (0 if the root
+ *                  itself is rejected).  Among accepted paths of equal length
+ *                  the one ending at the lowest node index wins.
+ *   accept_nodes   out int32 [B][max_nodes]: local node ids, root first, padded
+ *                  with -1.
+ *   accept_tokens  out int32 [B][max_nodes]: their draft tokens, padded with -1.
+ *   workspace      at least tree_verify_greedy_workspace_size() bytes.
+ */
+TA_API int tree_verify_greedy(int logits_dtype, const void* logits, const int32_t* draft_tokens,
+                       const uint64_t* mask, const int32_t* node_offsets, int32_t B,
+                       int32_t total_nodes, int32_t max_nodes, int32_t V,
+                       int32_t* target_argmax, int32_t* accept_len, int32_t* accept_nodes,
+                       int32_t* accept_tokens, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Static text for a status code; never NULL. */
+TA_API const char* tree_attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H */

@@ -1,0 +1,96 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any HIP call (CPU only: no kernels run)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tree_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"TA_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from tree_masked_attention_forward_amd import _binding
+    return _binding.load_library()
+
+
+def test_header_declares_the_three_calls():
+    names = _declared_functions()
+    for n in ("tree_attn_build_mask", "tree_attn_forward", "tree_verify_greedy"):
+        assert n in names
+    assert len(names) == 6, names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    from tree_masked_attention_forward_amd import _binding as b
+    for code in range(6):
+        assert b.status_string(code)
+    assert b.status_string(99) == "unknown status"
+
+
+def _fwd(lib, **kw):
+    args = dict(dtype=1, q=1 << 20, kt=1 << 20, vt=1 << 20, kp=1 << 20, vp=1 << 20, po=1 << 20,
+                no=1 << 20, mask=1 << 20, B=1, total=64, maxn=64, tp=4096, mp=4096, Hq=32, Hkv=8,
+                D=128, scale=0.088, out=1 << 20, lse=None, ws=None, wsb=0, stream=None)
+    args.update(kw)
+    a = args
+    return lib.tree_attn_forward(a["dtype"], a["q"], a["kt"], a["vt"], a["kp"], a["vp"], a["po"],
+                                 a["no"], a["mask"], a["B"], a["total"], a["maxn"], a["tp"],
+                                 a["mp"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["out"],
+                                 a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_forward_host_validation(lib):
+    assert _fwd(lib, dtype=7) == 3                 # unknown dtype
+    assert _fwd(lib, B=0) == 1
+    assert _fwd(lib, Hq=30, Hkv=8) == 1            # Hq % Hkv != 0
+    assert _fwd(lib, D=64) == 3                    # bf16 path needs D == 128
+    assert _fwd(lib, dtype=0, D=300) == 3          # fp32 path: D <= 256
+    assert _fwd(lib, maxn=2000) == 3               # above TA_MAX_NODES
+    assert _fwd(lib, q=None) == 1
+    assert _fwd(lib, kp=None) == 1                 # prefix rows but no prefix pointer
+    assert _fwd(lib, q=(1 << 20) + 2) == 1         # misaligned bf16 pointer
+    assert _fwd(lib, mp=5000) == 1                 # max_prefix > total_prefix
+    assert _fwd(lib, scale=float("nan")) == 1
+    assert _fwd(lib, ws=None, wsb=0) == 4          # this shape needs split partials
+    assert _fwd(lib, total=0) == 0                 # nothing to do, nothing launched
+
+
+def test_workspace_queries_are_pure_host(lib):
+    from tree_masked_attention_forward_amd import _binding as b
+    import torch
+    n = b.forward_workspace_size(torch.bfloat16, 1, 64, 64, 32, 8, 128, 4096, 4096)
+    assert n > 0 and n % 16 == 0
+    assert b.forward_workspace_size(torch.float32, 1, 5, 5, 1, 1, 64, 16, 16) == 0
+    assert b.verify_workspace_size(64, 64, 128256) >= 64 * 8
+    assert b.verify_workspace_size(0, 1, 10) == 0
+
+
+def test_build_mask_and_verify_host_validation(lib):
+    assert lib.tree_attn_build_mask(1 << 20, 1 << 20, 0, 5, 5, 1 << 20, None, None, None) == 1
+    assert lib.tree_attn_build_mask(1 << 20, 1 << 20, 1, 5, 4096, 1 << 20, None, None, None) == 3
+    assert lib.tree_attn_build_mask(None, 1 << 20, 1, 5, 5, 1 << 20, None, None, None) == 1
+    v = lib.tree_verify_greedy
+    ok = [1, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1, 64, 64, 1000, None, 1 << 20, 1 << 20,
+          1 << 20, 1 << 20, 1 << 20, None]
+    bad_dtype = list(ok); bad_dtype[0] = 5
+    assert v(*bad_dtype) == 3
+    no_ws = list(ok); no_ws[14] = 0
+    assert v(*no_ws) == 4
+    no_len = list(ok); no_len[10] = None
+    assert v(*no_len) == 1
+    big = list(ok); big[7] = 5000
+    assert v(*big) == 3

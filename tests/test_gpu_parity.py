@@ -1,0 +1,241 @@
+"""GPU parity: the HIP library, called through its C ABI, against the fp64
+oracle on the same seeded inputs.
+
+Masks, depths, statuses, argmax and accepted paths must be bit-exact; bf16
+attention must meet max-abs <= 1e-2 and relative RMS <= 5e-3, fp32 attention
+max-abs <= 2e-5 and relative RMS <= 1e-5.  Small cases are checked in full
+(several 32-key tiles, ragged tails, several row tiles); the full-size
+workloads are checked on every node where the oracle is quick (the 8B-shaped
+layer) and on sampled nodes elsewhere.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from helpers import DevCase, check_attention, config_case, gpu_forward, gpu_mask, lib
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ta():
+    return lib()
+
+
+def _oracle_attn(c, nodes=None):
+    return oracle.tree_attention(c.q, c.k_tree, c.v_tree, c.k_prefix, c.v_prefix, c.parents,
+                                 c.node_offsets, c.prefix_offsets, c.scale, nodes=nodes)
+
+
+def _check_mask(ta, c):
+    dc = DevCase(c)
+    mask, depth, status = gpu_mask(ta, dc)
+    rm, rd, rs = oracle.build_mask(c.parents, c.node_offsets, dc.max_nodes)
+    np.testing.assert_array_equal(status.cpu().numpy(), rs)
+    np.testing.assert_array_equal(mask.cpu().numpy(), rm)
+    np.testing.assert_array_equal(depth.cpu().numpy(), rd)
+    return dc, mask
+
+
+# ------------------------------------------------------------------- masks
+
+@pytest.mark.parametrize("name", list(synthetic.CONFIGS))
+def test_mask_configs_bit_exact(ta, name):
+    print(f"[mask] config={name}", flush=True)
+    c = config_case(name)
+    _check_mask(ta, c)
+
+
+def test_mask_every_tiny_tree(ta):
+    trees = []
+    for n in range(1, 7):
+        trees += [list(p) for p in itertools.product(*[range(-1, i) for i in range(n)])]
+    c = synthetic.make_case("alltrees", prefix_lens=[0] * len(trees), trees=trees, Hq=1, Hkv=1,
+                            D=8, dtype=torch.float32, seed=0)
+    _check_mask(ta, c)
+
+
+def test_mask_max_size_chain_and_forest(ta):
+    rng = np.random.default_rng(5)
+    trees = [[-1] + list(range(1023)),
+             synthetic.random_tree(rng, 1024, 7, None, None).tolist(),
+             synthetic.random_tree(rng, 700, 1, 20, 3).tolist(), [-1]]
+    c = synthetic.make_case("big", prefix_lens=[0] * 4, trees=trees, Hq=1, Hkv=1, D=8,
+                            dtype=torch.float32, seed=1)
+    _check_mask(ta, c)
+
+
+def test_mask_invalid_trees_and_offsets(ta):
+    trees = [[-1, 0, 1], [-1, 2, 0], [-1, 0, 3], [0, -1], [-1, -2]]
+    c = synthetic.make_case("bad", prefix_lens=[0] * 5, trees=trees, Hq=1, Hkv=1, D=8,
+                            dtype=torch.float32, seed=2)
+    _check_mask(ta, c)
+    dc = DevCase(c)
+    # node_offsets that exceed max_nodes: status INVALID_ARG, nothing written
+    mask, depth, status = ta.build_mask(dc.parents, dc.node_offsets, 2)
+    assert status.cpu().tolist() == [1, 1, 1, 2, 2]
+
+
+# ------------------------------------------------------------- attention
+
+def test_forward_tiny_fp32(ta):
+    c = synthetic.make_config_case("tiny", with_logits=False)
+    dc, mask = _check_mask(ta, c)
+    out, lse = gpu_forward(ta, dc, mask)
+    ro, rl = _oracle_attn(c)
+    check_attention(out, lse, ro, rl, fp32=True, what="tiny fp32")
+
+
+def test_forward_fp32_ragged_gqa(ta):
+    rng = np.random.default_rng(3)
+    trees = [synthetic.random_tree(rng, n, 1, 5, 3).tolist() for n in (1, 9, 40)]
+    c = synthetic.make_case("f32", prefix_lens=[0, 33, 150], trees=trees, Hq=6, Hkv=2, D=96,
+                            dtype=torch.float32, seed=3)
+    dc, mask = _check_mask(ta, c)
+    out, lse = gpu_forward(ta, dc, mask)
+    check_attention(out, lse, *_oracle_attn(c), fp32=True, what="f32 ragged")
+
+
+BF16_SHAPES = [
+    # (prefix lengths, node counts, roots, Hq, Hkv)
+    ([0], [1], 1, 8, 2),
+    ([5], [3], 1, 4, 4),
+    ([37, 0, 300], [17, 1, 70], 1, 8, 2),      # ragged tails, L=0, two row tiles
+    ([64], [64], 1, 32, 8),                   # exact tile multiples
+    ([1000], [9], 2, 16, 2),                  # G = 8, forest of 2
+    ([129, 2049], [130, 33], 3, 4, 1),         # G = 4, Hkv = 1, 3 row tiles
+]
+
+
+@pytest.mark.parametrize("shape", BF16_SHAPES, ids=lambda s: f"L{s[0]}-N{s[1]}-G{s[3]//s[4]}")
+def test_forward_bf16_small_full_check(ta, shape):
+    lens, ns, roots, Hq, Hkv = shape
+    rng = np.random.default_rng(sum(lens) + sum(ns))
+    trees = [synthetic.random_tree(rng, n, min(roots, n), 6, 4).tolist() for n in ns]
+    c = synthetic.make_case("bf16", prefix_lens=lens, trees=trees, Hq=Hq, Hkv=Hkv, D=128,
+                            seed=len(lens) * 7 + Hq)
+    print(f"[fwd bf16] lens={lens} ns={ns} Hq={Hq} Hkv={Hkv}", flush=True)
+    dc, mask = _check_mask(ta, c)
+    out, lse = gpu_forward(ta, dc, mask)
+    torch.cuda.synchronize()
+    check_attention(out, lse, *_oracle_attn(c), fp32=False, what=f"bf16 {lens}/{ns}")
+
+
+def test_forward_llama3_8b_full_check(ta):
+    """The benchmarked workload (one 8B-shaped layer, N=64, L=4096), every
+    node and head, in the same launch configuration the benchmark times."""
+    c = config_case("llama3_8b")
+    dc, mask = _check_mask(ta, c)
+    out, lse = gpu_forward(ta, dc, mask)
+    check_attention(out, lse, *_oracle_attn(c), fp32=False, what="llama3_8b")
+
+
+@pytest.mark.parametrize("name,per_seq", [("batched", 2), ("llama3_70b", 3), ("forest", 3)])
+def test_forward_full_size_sampled(ta, name, per_seq):
+    c = config_case(name)
+    print(f"[fwd sampled] config={name}", flush=True)
+    dc, mask = _check_mask(ta, c)
+    out, lse = gpu_forward(ta, dc, mask)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(77)
+    nodes = []
+    seqs = range(c.B) if c.B <= 4 else sorted(rng.choice(c.B, 4, replace=False))
+    for b in seqs:
+        lo, hi = int(c.node_offsets[b]), int(c.node_offsets[b + 1])
+        nodes += [lo, hi - 1] + sorted(rng.choice(np.arange(lo, hi), per_seq - 2 if per_seq > 2 else 0,
+                                                  replace=False).tolist())
+    nodes = sorted(set(nodes))
+    ro, rl = _oracle_attn(c, nodes=nodes)
+    check_attention(out[nodes], lse[nodes], ro, rl, fp32=False, what=f"{name} sampled {nodes}")
+
+
+def test_forward_hidden_rows_do_not_change_output_bitwise(ta):
+    rng = np.random.default_rng(8)
+    parents = synthetic.random_tree(rng, 60, 2, 6, 4)
+    c = synthetic.make_case("sib", prefix_lens=[200], trees=[parents.tolist()], Hq=8, Hkv=2,
+                            D=128, seed=8)
+    dc, mask = _check_mask(ta, c)
+    out, lse = gpu_forward(ta, dc, mask)
+    vis = oracle.ancestor_mask_dense(parents)
+    i = 45
+    hidden = torch.from_numpy(np.flatnonzero(~vis[i]))
+    d2 = DevCase(c)
+    d2.k_tree[hidden.cuda()] = (d2.k_tree[hidden.cuda()].float() * -3.0 + 1.0).to(torch.bfloat16)
+    d2.v_tree[hidden.cuda()] = (d2.v_tree[hidden.cuda()].float() + 5.0).to(torch.bfloat16)
+    out2, lse2 = gpu_forward(ta, d2, mask)
+    assert torch.equal(out2[i], out[i]) and torch.equal(lse2[i], lse[i])
+
+
+def test_forward_empty_prefix_root_is_its_value_row(ta):
+    c = synthetic.make_case("root", prefix_lens=[0, 0], trees=[[-1, 0], [-1, -1, 1]], Hq=4,
+                            Hkv=2, D=128, seed=9)
+    dc, mask = _check_mask(ta, c)
+    out, _ = gpu_forward(ta, dc, mask)
+    for gi in (0, 2, 3):
+        expect = c.v_tree[gi].repeat_interleave(2, dim=0)
+        assert torch.equal(out[gi].cpu(), expect), gi
+
+
+# ------------------------------------------------------------ verification
+
+def _check_verify(ta, c, dc, mask):
+    pred, alen, anodes, atok = ta.verify_greedy(dc.logits, dc.draft, mask, dc.node_offsets,
+                                                dc.max_nodes)
+    rp, rlen, rnodes, rtok = oracle.verify_greedy(c.logits, c.draft, c.parents, c.node_offsets,
+                                                  dc.max_nodes)
+    np.testing.assert_array_equal(pred.cpu().numpy(), rp)
+    np.testing.assert_array_equal(alen.cpu().numpy(), rlen)
+    np.testing.assert_array_equal(anodes.cpu().numpy(), rnodes)
+    np.testing.assert_array_equal(atok.cpu().numpy(), rtok)
+    return rlen
+
+
+def test_verify_tiny_example(ta):
+    c = synthetic.make_config_case("tiny")
+    dc, mask = _check_mask(ta, c)
+    rlen = _check_verify(ta, c, dc, mask)
+    assert rlen.tolist() == [3]
+
+
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 50000), (torch.float32, 1001),
+                                     (torch.bfloat16, 77), (torch.float32, 4096)])
+def test_verify_random_trees(ta, dtype, V):
+    rng = np.random.default_rng(V)
+    trees = [synthetic.random_tree(rng, n, r, 8, 3).tolist() for n, r in
+             ((1, 1), (30, 1), (200, 4), (64, 1), (5, 5))]
+    c = synthetic.make_case("ver", prefix_lens=[0] * 5, trees=trees, Hq=1, Hkv=1, D=8,
+                            dtype=dtype, seed=V, vocab=V, p_match=0.9)
+    dc, mask = _check_mask(ta, c)
+    _check_verify(ta, c, dc, mask)
+
+
+def test_verify_forced_ties_across_chunks(ta):
+    V = 128256
+    trees = [[-1, 0, 1, 1, 2, 0]]
+    c = synthetic.make_case("ties", prefix_lens=[0], trees=trees, Hq=1, Hkv=1, D=8, seed=4,
+                            vocab=V, p_match=1.0)
+    lg = c.logits
+    lg[0, 100] = lg[0, 90000] = 20.0        # tie in different vocab chunks
+    lg[1, :] = 0.0                          # all equal: index 0
+    lg[2, :] = -1.0
+    lg[2, 70000] = -0.0
+    lg[2, 5] = 0.0                          # -0 == +0: index 5
+    lg[3, V - 1] = 30.0                     # maximum in the last entry
+    lg[4, :] = float("-inf")                # all -inf: index 0
+    c.draft = torch.argmax(lg.float(), 1).numpy().astype(np.int32)
+    c.draft[5] = (c.draft[5] + 1) % V
+    dc, mask = _check_mask(ta, c)
+    rlen = _check_verify(ta, c, dc, mask)
+    assert rlen.tolist() == [4]
+
+
+def test_verify_forest_full_size(ta):
+    c = synthetic.make_config_case("forest", with_logits=True)
+    print(f"[verify] forest logits {tuple(c.logits.shape)}", flush=True)
+    dc, mask = _check_mask(ta, c)
+    rlen = _check_verify(ta, c, dc, mask)
+    print(f"[verify] accept_len={rlen.tolist()}", flush=True)

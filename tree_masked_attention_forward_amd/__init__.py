@@ -1,0 +1,35 @@
+"""Tree attention and greedy tree verification on AMD Instinct MI355X (gfx950).
+
+The computation lives in ``libtreeattn.so`` (hand-written HIP kernels behind
+the C ABI of ``include/tree_attn.h``); this package is its Python binding.
+Importing the package loads the library and raises ImportError when it has not
+been built (``python -m tree_masked_attention_forward_amd.build``).
+"""
+from ._binding import (  # noqa: F401
+    LIBRARY_PATH,
+    TA_BF16,
+    TA_ERR_HIP,
+    TA_ERR_INVALID_ARG,
+    TA_ERR_INVALID_TREE,
+    TA_ERR_UNSUPPORTED,
+    TA_ERR_WORKSPACE,
+    TA_F32,
+    TA_MAX_NODES,
+    TA_OK,
+    TreeAttnError,
+    build_mask,
+    forward,
+    forward_workspace_size,
+    load_library,
+    mask_words,
+    status_string,
+    verify_greedy,
+    verify_workspace_size,
+)
+
+load_library()
+
+# The C names, for readers who know the ABI.
+tree_attn_build_mask = build_mask
+tree_attn_forward = forward
+tree_verify_greedy = verify_greedy

@@ -1,0 +1,68 @@
+"""Build libtreeattn.so in-tree with hipcc for gfx950.
+
+    python -m tree_masked_attention_forward_amd.build
+
+Each source is compiled to an object file in parallel, then linked into
+``tree_masked_attention_forward_amd/libtreeattn.so``.  Packed-fp32 VALU
+instructions are switched off for all device code.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libtreeattn.so")
+SOURCES = ["api.cpp", "mask_build.hip", "attn_fwd.hip", "verify.hip"]
+ARCH = os.environ.get("TREE_ATTN_ARCH", "gfx950")
+
+
+def _hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP toolchain is required to build libtreeattn.so")
+
+
+def compile_flags():
+    return ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+            "-Wall", "-Wno-unused-function", "-Wno-unused-result",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = _hipcc()
+    with tempfile.TemporaryDirectory(prefix="treeattn_build_") as tmp:
+        def one(src):
+            obj = os.path.join(tmp, src + ".o")
+            cmd = [hipcc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+            if verbose:
+                noise = [l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l]
+                if noise:
+                    print("\n".join(noise), file=sys.stderr)
+            return obj
+
+        with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+            objs = list(ex.map(one, SOURCES))
+        tmp_lib = LIB + ".tmp"
+        cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stderr}")
+        os.replace(tmp_lib, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,141 @@
+// Host side of the C ABI declared in include/tree_attn.h: argument checks that
+// need no GPU, workspace sizing, and kernel launches on the caller's stream.
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing and touches no device state.
+#include <math.h>
+
+#include "internal.h"
+
+namespace {
+
+constexpr int kMaxF32HeadDim = 256;
+
+bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TA_OK : TA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* tree_attn_status_string(int status) {
+  switch (status) {
+    case TA_OK: return "ok";
+    case TA_ERR_INVALID_ARG: return "invalid argument";
+    case TA_ERR_INVALID_TREE: return "invalid tree (a parent is not -1 or an earlier node)";
+    case TA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case TA_ERR_WORKSPACE: return "workspace missing or too small";
+    case TA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int tree_attn_build_mask(const int32_t* parents, const int32_t* node_offsets, int32_t B,
+                         int32_t total_nodes, int32_t max_nodes, uint64_t* mask,
+                         int32_t* depth, int32_t* tree_status, void* stream) {
+  if (B <= 0 || total_nodes < 0 || max_nodes < 1 || !node_offsets) return TA_ERR_INVALID_ARG;
+  if (max_nodes > TA_MAX_NODES) return TA_ERR_UNSUPPORTED;
+  if (total_nodes > 0 && (!parents || !mask)) return TA_ERR_INVALID_ARG;
+  return hip_status(ta::launch_build_mask(parents, node_offsets, B, total_nodes, max_nodes, mask,
+                                          depth, tree_status,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+size_t tree_attn_forward_workspace_size(int dtype, int32_t B, int32_t total_nodes,
+                                        int32_t max_nodes, int32_t Hq, int32_t Hkv, int32_t D,
+                                        int64_t total_prefix, int64_t max_prefix) {
+  if (dtype != TA_BF16 || B <= 0 || total_nodes <= 0 || max_nodes < 1 || Hq <= 0 ||
+      Hkv <= 0 || Hq % Hkv != 0 || D != 128 || total_prefix < 0 || max_prefix < 0)
+    return 0;
+  return ta::plan_forward_bf16(B, total_nodes, max_nodes, Hq, Hkv, total_prefix, max_prefix)
+      .ws_bytes;
+}
+
+int tree_attn_forward(int dtype, const void* q, const void* k_tree, const void* v_tree,
+                      const void* k_prefix, const void* v_prefix,
+                      const int64_t* prefix_offsets, const int32_t* node_offsets,
+                      const uint64_t* mask, int32_t B, int32_t total_nodes, int32_t max_nodes,
+                      int64_t total_prefix, int64_t max_prefix, int32_t Hq, int32_t Hkv,
+                      int32_t D, float scale, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (dtype != TA_BF16 && dtype != TA_F32) return TA_ERR_UNSUPPORTED;
+  if (B <= 0 || total_nodes < 0 || max_nodes < 1 || Hq <= 0 || Hkv <= 0 || D <= 0 ||
+      total_prefix < 0 || max_prefix < 0 || max_prefix > total_prefix)
+    return TA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return TA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return TA_ERR_INVALID_ARG;
+  if (max_nodes > TA_MAX_NODES) return TA_ERR_UNSUPPORTED;
+  if (dtype == TA_BF16 && D != 128) return TA_ERR_UNSUPPORTED;
+  if (dtype == TA_F32 && D > kMaxF32HeadDim) return TA_ERR_UNSUPPORTED;
+  if (!prefix_offsets || !node_offsets) return TA_ERR_INVALID_ARG;
+  if (total_nodes == 0) return TA_OK;
+  if (!q || !k_tree || !v_tree || !mask || !out) return TA_ERR_INVALID_ARG;
+  if (total_prefix > 0 && (!k_prefix || !v_prefix)) return TA_ERR_INVALID_ARG;
+  if (dtype == TA_BF16 &&
+      (misaligned16(q) || misaligned16(k_tree) || misaligned16(v_tree) ||
+       misaligned16(k_prefix) || misaligned16(v_prefix) || misaligned16(out)))
+    return TA_ERR_INVALID_ARG;
+  // Element offsets must fit the kernels' 64-bit index arithmetic comfortably
+  // and row counts their 32-bit node/row indices.
+  if ((long long)max_nodes * (Hq / Hkv) > (1LL << 30) || total_prefix > (1LL << 40))
+    return TA_ERR_UNSUPPORTED;
+
+  ta::FwdArgs a{};
+  a.q = q;
+  a.k_tree = k_tree;
+  a.v_tree = v_tree;
+  a.k_prefix = k_prefix;
+  a.v_prefix = v_prefix;
+  a.prefix_offsets = prefix_offsets;
+  a.node_offsets = node_offsets;
+  a.mask = mask;
+  a.B = B;
+  a.total_nodes = total_nodes;
+  a.max_nodes = max_nodes;
+  a.total_prefix = total_prefix;
+  a.max_prefix = max_prefix;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.W = (max_nodes + 63) / 64;
+  a.scale = scale;
+  a.out = out;
+  a.lse = lse;
+  a.workspace = workspace;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == TA_F32) return hip_status(ta::launch_forward_f32(a, s));
+
+  const ta::FwdPlan p =
+      ta::plan_forward_bf16(B, total_nodes, max_nodes, Hq, Hkv, total_prefix, max_prefix);
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes || misaligned16(workspace)))
+    return TA_ERR_WORKSPACE;
+  return hip_status(ta::launch_forward_bf16(a, p, s));
+}
+
+size_t tree_verify_greedy_workspace_size(int32_t total_nodes, int32_t max_nodes, int32_t V) {
+  (void)max_nodes;
+  if (total_nodes <= 0 || V <= 0) return 0;
+  return ta::plan_verify(total_nodes, V).ws_bytes;
+}
+
+int tree_verify_greedy(int logits_dtype, const void* logits, const int32_t* draft_tokens,
+                       const uint64_t* mask, const int32_t* node_offsets, int32_t B,
+                       int32_t total_nodes, int32_t max_nodes, int32_t V,
+                       int32_t* target_argmax, int32_t* accept_len, int32_t* accept_nodes,
+                       int32_t* accept_tokens, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (logits_dtype != TA_BF16 && logits_dtype != TA_F32) return TA_ERR_UNSUPPORTED;
+  if (B <= 0 || total_nodes < 0 || max_nodes < 1 || V <= 0) return TA_ERR_INVALID_ARG;
+  if (max_nodes > TA_MAX_NODES) return TA_ERR_UNSUPPORTED;
+  if (!node_offsets || !accept_len || !accept_nodes || !accept_tokens) return TA_ERR_INVALID_ARG;
+  if (total_nodes > 0 && (!logits || !draft_tokens || !mask)) return TA_ERR_INVALID_ARG;
+  const ta::VerifyPlan p = ta::plan_verify(total_nodes, V);
+  if (total_nodes > 0 && (!workspace || workspace_bytes < p.ws_bytes || misaligned16(workspace)))
+    return TA_ERR_WORKSPACE;
+  return hip_status(ta::launch_verify(logits_dtype == TA_BF16, logits, draft_tokens, mask,
+                                      node_offsets, B, total_nodes, max_nodes, V, target_argmax,
+                                      accept_len, accept_nodes, accept_tokens, workspace, p,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Internal declarations shared by the host API (api.cpp) and the kernel
+// translation units.  Not part of the public ABI (include/tree_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tree_attn.h"
+
+namespace ta {
+
+// Work decomposition of one tree_attn_forward call on the bf16 MFMA path.
+// Derived from host scalars only, so the workspace query and the call agree.
+struct FwdPlan {
+  int nwaves;      // waves per workgroup; each wave owns 32 query rows
+  int rows_wg;     // query rows per workgroup = 32 * nwaves
+  int R;           // row tiles per (sequence, KV head) = ceil(max_nodes*G / rows_wg)
+  int S;           // key splits per row tile (upper bound over sequences)
+  int chunk;       // keys per split, a multiple of the 32-key tile
+  long long n_items;   // B * Hkv * S * R
+  size_t ws_bytes;     // partial (O, m, l) storage; 0 when S == 1
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k_tree;
+  const void* v_tree;
+  const void* k_prefix;
+  const void* v_prefix;
+  const int64_t* prefix_offsets;
+  const int32_t* node_offsets;
+  const uint64_t* mask;
+  int B, total_nodes, max_nodes;
+  long long total_prefix, max_prefix;
+  int Hq, Hkv, D, W;
+  float scale;
+  void* out;
+  float* lse;
+  void* workspace;
+};
+
+FwdPlan plan_forward_bf16(int B, int total_nodes, int max_nodes, int Hq, int Hkv,
+                          long long total_prefix, long long max_prefix);
+
+hipError_t launch_build_mask(const int32_t* parents, const int32_t* node_offsets, int B,
+                             int total_nodes, int max_nodes, uint64_t* mask, int32_t* depth,
+                             int32_t* status, hipStream_t stream);
+
+hipError_t launch_forward_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t stream);
+hipError_t launch_forward_f32(const FwdArgs& a, hipStream_t stream);
+
+struct VerifyPlan {
+  int cpr;          // vocabulary chunks per logits row
+  int chunk;        // vocabulary entries per chunk (multiple of 8)
+  size_t ws_bytes;  // one (value, index) pair per (row, chunk)
+};
+
+VerifyPlan plan_verify(int total_nodes, int V);
+
+hipError_t launch_verify(bool bf16, const void* logits, const int32_t* draft,
+                         const uint64_t* mask, const int32_t* node_offsets, int B,
+                         int total_nodes, int max_nodes, int V, int32_t* target_argmax,
+                         int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
+                         void* workspace, const VerifyPlan& p, hipStream_t stream);
+
+}  // namespace ta

@@ -1,0 +1,260 @@
+// Greedy tree verification.
+//
+// Follows "Tree Attention" (inferensys.com glossary), Multi-Token Acceptance &
+// Rollback and Integration with Speculative Decoding: after the verification
+// pass, the longest branch from the root whose draft tokens the target agrees
+// with is accepted.  The premlal listing (verify_candidate_tree) takes the
+// target's argmax per position and compares it with the draft token; it scans
+// the flattened order, which is a root path only for a chain.  Here every node
+// is tested on its own root path instead.
+//
+// Two kernels:
+//   argmax_partial_kernel  streams the [sum_N][V] logits once (the only large
+//       input; bound by HBM bandwidth).  Each workgroup scans one vocabulary
+//       chunk of one row with 16-byte loads and leaves (max value, lowest index
+//       holding it).  Values are compared as floats, so -0 and +0 tie.
+//   path_select_kernel  one workgroup per sequence: merges the chunk results
+//       (ties -> lowest index), forms the match bit set with wavefront ballots,
+//       accepts node i iff mask[i] is a subset of the match set (every node on
+//       its root path matches), and picks the accepted node with the most mask
+//       bits (the longest path), lowest index on ties.  The accepted path is
+//       the set bits of that node's mask in increasing order, which is root to
+//       leaf because parents precede children.
+#include "internal.h"
+
+#include <algorithm>
+
+namespace ta {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ inline bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__device__ inline void wave_best(float& bv, int& bi) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    if (better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+}
+
+// VEC: elements per 16-byte load (8 for bf16, 4 for fp32), or 1 for scalar
+// loads when the row start is not 16-byte aligned.
+template <bool BF16, int VEC>
+__global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const void* __restrict__ logits,
+                                                                  int V, int cpr, int chunk,
+                                                                  float2* __restrict__ ws) {
+  const long long row = blockIdx.x / cpr;
+  const int c = blockIdx.x % cpr;
+  const int lo = c * chunk;
+  const int hi = min(V, lo + chunk);
+  float bv = kNegInf;
+  int bi = 0x7fffffff;
+  if (VEC > 1) {
+    for (int e = lo + threadIdx.x * VEC; e < hi; e += kThreads * VEC) {
+      uint4 u;
+      if (BF16)
+        u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(logits) + row * V + e);
+      else
+        u = *reinterpret_cast<const uint4*>(static_cast<const float*>(logits) + row * V + e);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (BF16) {
+          const float a = __uint_as_float(w[j] << 16);
+          const float b = __uint_as_float(w[j] & 0xffff0000u);
+          if (better(a, e + 2 * j, bv, bi)) { bv = a; bi = e + 2 * j; }
+          if (better(b, e + 2 * j + 1, bv, bi)) { bv = b; bi = e + 2 * j + 1; }
+        } else {
+          const float a = __uint_as_float(w[j]);
+          if (better(a, e + j, bv, bi)) { bv = a; bi = e + j; }
+        }
+      }
+    }
+  } else {
+    for (int e = lo + threadIdx.x; e < hi; e += kThreads) {
+      float a;
+      if (BF16)
+        a = __uint_as_float((uint32_t)static_cast<const uint16_t*>(logits)[row * V + e] << 16);
+      else
+        a = static_cast<const float*>(logits)[row * V + e];
+      if (better(a, e, bv, bi)) { bv = a; bi = e; }
+    }
+  }
+  // Ties (including -0 == +0 and rows of -inf) resolve to the lower index at
+  // every level: in-thread, across lanes, across waves, across chunks.
+  wave_best(bv, bi);
+  __shared__ float sv[kThreads / 64];
+  __shared__ int si[kThreads / 64];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sv[wave] = bv;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kThreads / 64; ++w)
+      if (better(sv[w], si[w], bv, bi)) {
+        bv = sv[w];
+        bi = si[w];
+      }
+    ws[row * cpr + c] = make_float2(bv, __int_as_float(bi));
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void path_select_kernel(
+    const float2* __restrict__ ws, int cpr, const int32_t* __restrict__ draft,
+    const uint64_t* __restrict__ mask, const int32_t* __restrict__ node_offsets,
+    int total_nodes, int max_nodes, int W, int32_t* __restrict__ target_argmax,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
+    int32_t* __restrict__ accept_tokens) {
+  __shared__ uint64_t match_w[(TA_MAX_NODES + 63) / 64];
+  __shared__ unsigned long long red[kThreads / 64];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n0 = node_offsets[b];
+  const int n1 = node_offsets[b + 1];
+  int nn = n1 - n0;
+  if (n0 < 0 || nn < 0 || nn > max_nodes || n1 > total_nodes) nn = -1;   // skip this sequence
+
+  for (int w = tid; w < W; w += kThreads) match_w[w] = 0ull;
+  __syncthreads();
+
+  const int rounds = nn > 0 ? (nn + kThreads - 1) / kThreads : 0;
+  for (int it = 0; it < rounds; ++it) {
+    const int i = it * kThreads + tid;
+    bool m = false;
+    if (i < nn) {
+      float bv = kNegInf;
+      int bi = 0x7fffffff;
+      const float2* pr = ws + (size_t)(n0 + i) * cpr;
+      for (int c = 0; c < cpr; ++c) {
+        const float2 x = pr[c];
+        const int xi = __float_as_int(x.y);
+        if (better(x.x, xi, bv, bi)) {
+          bv = x.x;
+          bi = xi;
+        }
+      }
+      if (target_argmax) target_argmax[n0 + i] = bi;
+      m = draft[n0 + i] == bi;
+    }
+    const unsigned long long bal = __ballot(m);
+    const int word = (it * kThreads + wave * 64) >> 6;
+    if (lane == 0 && word < W) match_w[word] = bal;
+  }
+  __syncthreads();
+
+  unsigned long long key = 0ull;
+  for (int i = tid; i < nn; i += kThreads) {
+    bool ok = true;
+    int len = 0;
+    for (int w = 0; w < W; ++w) {
+      uint64_t mw = mask[(size_t)(n0 + i) * W + w];
+      const int base = 64 * w;
+      if (base >= nn) mw = 0ull;
+      else if (nn - base < 64) mw &= (1ull << (nn - base)) - 1ull;
+      len += __popcll(mw);
+      if (mw & ~match_w[w]) ok = false;
+    }
+    if (ok && len > 0) {
+      const unsigned long long k = ((unsigned long long)len << 32) | (0xffffffffu - (uint32_t)i);
+      key = k > key ? k : key;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long ok2 = __shfl_xor(key, o);
+    key = ok2 > key ? ok2 : key;
+  }
+  if (lane == 0) red[wave] = key;
+  __syncthreads();
+  key = red[0];
+  for (int w = 1; w < kThreads / 64; ++w) key = red[w] > key ? red[w] : key;
+  const int len = (int)(key >> 32);
+  const int best = (int)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+
+  int32_t* an = accept_nodes + (size_t)b * max_nodes;
+  int32_t* at = accept_tokens + (size_t)b * max_nodes;
+  for (int pos = tid; pos < max_nodes; pos += kThreads)
+    if (pos >= len) {
+      an[pos] = -1;
+      at[pos] = -1;
+    }
+  if (len > 0) {
+    const uint64_t* brow = mask + (size_t)(n0 + best) * W;
+    for (int j = tid; j < nn; j += kThreads) {
+      const int wj = j >> 6;
+      const uint64_t mw = brow[wj];
+      if (!((mw >> (j & 63)) & 1ull)) continue;
+      int pos = __popcll(mw & ((1ull << (j & 63)) - 1ull));
+      for (int w = 0; w < wj; ++w) pos += __popcll(brow[w]);
+      an[pos] = j;
+      at[pos] = draft[n0 + j];
+    }
+  }
+  if (tid == 0) accept_len[b] = len;
+}
+
+}  // namespace
+
+VerifyPlan plan_verify(int total_nodes, int V) {
+  VerifyPlan p{};
+  // Enough workgroups to cover the chip (the logits scan is bound by HBM):
+  // split short batches' rows into vocabulary chunks of at least 4096 entries.
+  const int rows = std::max(total_nodes, 1);
+  int cpr = (2048 + rows - 1) / rows;
+  cpr = std::max(1, std::min(cpr, (V + 4095) / 4096));
+  int chunk = (V + cpr - 1) / cpr;
+  chunk = (chunk + 7) / 8 * 8;
+  p.cpr = (V + chunk - 1) / chunk;
+  p.chunk = chunk;
+  p.ws_bytes = (size_t)total_nodes * p.cpr * sizeof(float2);
+  return p;
+}
+
+hipError_t launch_verify(bool bf16, const void* logits, const int32_t* draft,
+                         const uint64_t* mask, const int32_t* node_offsets, int B,
+                         int total_nodes, int max_nodes, int V, int32_t* target_argmax,
+                         int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
+                         void* workspace, const VerifyPlan& p, hipStream_t stream) {
+  float2* ws = static_cast<float2*>(workspace);
+  const int W = (max_nodes + 63) / 64;
+  if (total_nodes > 0) {
+    const dim3 grid((unsigned)((long long)total_nodes * p.cpr));
+    const bool aligned = (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
+    if (bf16) {
+      if (aligned && V % 8 == 0)
+        hipLaunchKernelGGL((argmax_partial_kernel<true, 8>), grid, dim3(kThreads), 0, stream,
+                           logits, V, p.cpr, p.chunk, ws);
+      else
+        hipLaunchKernelGGL((argmax_partial_kernel<true, 1>), grid, dim3(kThreads), 0, stream,
+                           logits, V, p.cpr, p.chunk, ws);
+    } else {
+      if (aligned && V % 4 == 0)
+        hipLaunchKernelGGL((argmax_partial_kernel<false, 4>), grid, dim3(kThreads), 0, stream,
+                           logits, V, p.cpr, p.chunk, ws);
+      else
+        hipLaunchKernelGGL((argmax_partial_kernel<false, 1>), grid, dim3(kThreads), 0, stream,
+                           logits, V, p.cpr, p.chunk, ws);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(path_select_kernel, dim3(B), dim3(kThreads), 0, stream, ws, p.cpr, draft,
+                     mask, node_offsets, total_nodes, max_nodes, W, target_argmax, accept_len,
+                     accept_nodes, accept_tokens);
+  return hipGetLastError();
+}
+
+}  // namespace ta
