@@ -42,7 +42,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="llama3_8b")
-    p.add_argument("--sets", type=int, default=16)
+    p.add_argument("--sets", type=int, default=32)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     return p.parse_args()
@@ -102,7 +102,10 @@ def main():
         "kp": case.k_prefix.to(dev), "vp": case.v_prefix.to(dev),
         "logits": case.logits.to(dev), "draft": torch.from_numpy(case.draft).to(dev),
     }
-    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(args.sets - 1)]
+    # Enough distinct copies to cycle through 2x the 256 MB Infinity Cache.
+    set_bytes = sum(v.numel() * v.element_size() for v in base.values())
+    n_sets = max(1, min(args.sets, -(-2 * 256 * 2**20 // set_bytes)))
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_sets - 1)]
     mask = torch.empty((sum_n, W), dtype=torch.uint64, device=dev)
     depth = torch.empty(sum_n, dtype=torch.int32, device=dev)
     status = torch.empty(B, dtype=torch.int32, device=dev)
@@ -228,7 +231,7 @@ def main():
             "workload": f"{args.config}: B={B} Hq={Hq} Hkv={Hkv} D={D} L={max_prefix} N={max_nodes} "
                         f"(sum_L={sum_l}, sum_N={sum_n}); greedy verify over V={V} bf16 logits",
             "step": "build_mask + forward + verify_greedy, inputs rotated over "
-                    f"{args.sets} resident copies",
+                    f"{len(sets)} resident copies of {set_bytes / 2**20:.1f} MiB",
             "global_batch": B, "seq_len": max_prefix, "tree_nodes": sum_n,
         },
         "roofline": roof(dominant),

@@ -125,6 +125,18 @@ def test_forward_bf16_small_full_check(ta, shape):
     check_attention(out, lse, *_oracle_attn(c), fp32=False, what=f"bf16 {lens}/{ns}")
 
 
+def test_forward_many_sequences_full_check(ta):
+    """16 ragged sequences x 8 KV heads: the 256-row, single-key-group
+    workgroup shape with several key splits, checked on every node."""
+    rng = np.random.default_rng(21)
+    lens = [int(x) for x in rng.integers(0, 300, 16)]
+    trees = [synthetic.random_tree(rng, 64, 1, 6, 4).tolist() for _ in range(16)]
+    c = synthetic.make_case("many", prefix_lens=lens, trees=trees, Hq=32, Hkv=8, D=128, seed=21)
+    dc, mask = _check_mask(ta, c)
+    out, lse = gpu_forward(ta, dc, mask)
+    check_attention(out, lse, *_oracle_attn(c), fp32=False, what="16 ragged sequences")
+
+
 def test_forward_llama3_8b_full_check(ta):
     """The benchmarked workload (one 8B-shaped layer, N=64, L=4096), every
     node and head, in the same launch configuration the benchmark times."""
@@ -202,7 +214,8 @@ def test_verify_tiny_example(ta):
 
 
 @pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 50000), (torch.float32, 1001),
-                                     (torch.bfloat16, 77), (torch.float32, 4096)])
+                                     (torch.bfloat16, 77), (torch.float32, 4096),
+                                     (torch.bfloat16, 600001), (torch.float32, 700000)])
 def test_verify_random_trees(ta, dtype, V):
     rng = np.random.default_rng(V)
     trees = [synthetic.random_tree(rng, n, r, 8, 3).tolist() for n, r in

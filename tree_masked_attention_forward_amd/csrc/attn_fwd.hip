@@ -1,4 +1,4 @@
-// Tree attention forward on gfx950.
+// Tree attention forward on gfx950, bf16 inputs, head size 128.
 //
 // What is computed ("Tree Attention", inferensys.com glossary, Modified Causal
 // Attention Mask and Speculative KV Cache Reuse; "Tree Attention",
@@ -6,60 +6,70 @@
 // head h, attends to all L_b prefix keys of KV head g = h / G, to itself and
 // to its ancestors; softmax(scale * q.k) weights the matching values.
 //
-// bf16 path (D = 128).  For one (sequence, KV head) the N_b nodes times the G
+// Layout of the work.  For one (sequence, KV head) the N_b nodes times the G
 // query heads that share the KV head form a dense block of N_b*G query rows
 // (row = node*G + j), so every key/value row fetched from HBM is used by all
-// of them: the key scan is a dense contraction on MFMA.  The work is cut into
-// items (sequence, KV head, key split, row tile):
+// of them and the key scan is a dense contraction on MFMA.  A sequence's key
+// axis is [prefix, padded to 32 | tree nodes] in 32-key tiles; prefix tiles
+// need no mask; a tree tile tests the row node's ancestor bits (one uint64
+// word per 64 nodes); tiles past a row tile's last node are never visited
+// because nodes are topologically ordered.
 //
-//   * each wave owns 32 query rows; the workgroup (up to 8 waves) shares one
-//     32-key K tile and the matching V tile, staged through LDS from 16-byte
-//     coalesced global loads (double buffered, one barrier per tile);
-//   * scores are computed transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T held in registers), so
-//     each lane holds 16 keys of ONE query row and the other 16 keys of that
-//     row sit in lane ^ 32: the row max needs one cross-lane step and the
-//     rescale of the output accumulator is one factor per lane;
-//   * online softmax in fp32 in the log2 domain (scale * log2(e) folded into
-//     one FMA before v_exp_f32), probabilities rounded to bf16;
-//   * O^T += V^T P^T on the same MFMA (A = V^T from LDS, stored transposed
-//     when the tile is staged; B = P^T straight from the score registers);
-//   * the key axis of a sequence is [prefix (padded to 32) | tree nodes]; a
-//     prefix tile needs no mask; a tree tile tests bit (key) of the row's
-//     node mask word (one uint64 word per 64 nodes, built by
-//     tree_attn_build_mask); tiles past the row tile's last node are never
-//     visited because nodes are topologically ordered;
-//   * each item leaves a partial (unnormalised O, running max m, sum l); a
-//     second kernel merges the partials of a row by log-sum-exp.  With a
-//     single split the item writes the final output directly.
+// Workgroup = RG row groups x KG key groups of one wave each.  A wave owns 32
+// query rows; the KG waves that share those rows take alternate tiles of the
+// workgroup's key range, and are merged through LDS at the end.  Grid items
+// are (sequence, KV head, key split, row tile); splits cut the tile range in
+// balanced pieces (the tree tiles ride with the last prefix tiles).  Items
+// that share a KV chunk have consecutive ids and land on one XCD, so the
+// second row tile reads the chunk from that XCD's L2.
 //
-// fp32 path: one wave per (node, head), exact-fp32 dot products reduced
-// across lanes, online softmax with expf.  A plain correctness path.
+// Per 32-key tile and wave:
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T
+//     held in registers for the whole kernel): each lane holds 16 keys of ONE
+//     query row and lane^32 holds the other 16, so the row max is one
+//     cross-lane step and the output rescale is one factor per lane;
+//   * online softmax in fp32 in the log2 domain (scale*log2(e) folded into one
+//     FMA before v_exp_f32); the running max is lazy (it moves only when a
+//     tile exceeds it by 2^8), so the 64-register rescale of O is rare;
+//   * O^T += V^T P^T on the same MFMA: B = P^T comes straight from the score
+//     registers (rounded to bf16), A = V^T is read from the row-major V tile
+//     with ds_read_b64_tr_b16, whose 16-lane 4x16 transpose hands each lane
+//     four consecutive keys of one head dimension.
+// K and V tiles are staged through LDS with 16-byte coalesced loads, double
+// buffered, one barrier per stage.  Items with one split write bf16 output
+// (and lse) directly; otherwise each leaves (unnormalised O, max, sum) in the
+// workspace (normalised O in bf16, max and sum in fp32), in the MFMA register
+// layout so every store is coalesced, and a merge kernel combines the splits
+// by log-sum-exp.
 #include "internal.h"
 
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace ta {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kD = 128;                        // head size of the MFMA path
-constexpr int kKT = 32;                        // keys per tile
-constexpr int kKStride = kD * 2 + 16;          // LDS bytes per K row (padded: no bank conflicts)
-constexpr int kVStride = kKT * 2 + 16;         // LDS bytes per V^T row
-constexpr int kKTileBytes = kKT * kKStride;    // 8704
-constexpr int kVTileBytes = kD * kVStride;     // 10240
-constexpr int kStageBytes = kKTileBytes + kVTileBytes;
+constexpr int kD = 128;                       // head size of the MFMA path
+constexpr int kKT = 32;                       // keys per tile
+constexpr int kKStride = kD * 2 + 16;         // LDS bytes per K row: 68 dwords, conflict-free b128 reads
+constexpr int kVStride = kD * 2 + 64;         // LDS bytes per V row: 80 dwords, for the 4-row transpose reads
+constexpr int kKBytes = kKT * kKStride;       // 8704
+constexpr int kTileBytes = kKBytes + kKT * kVStride;   // 18944: one K tile + one V tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kLazyLog2 = 8.f;              // running-max slack: probabilities stay <= 256
 
 struct KParams {
   const uint16_t* q;
@@ -72,17 +82,17 @@ struct KParams {
   const uint64_t* mask;
   uint16_t* out;
   float* lse;
-  float* ws_o;   // [n_items][rows_wg][128] unnormalised partial outputs
-  float* ws_ml;  // [n_items][rows_wg][2]   (running max in score units, sum)
+  u32x2_t* ws_o;   // [n_items][RG][16][64] 4 x bf16: O / l in register layout
+  float2* ws_ml;   // [n_items][rows_wg]   (running max in score units, sum)
   long long total_prefix, max_prefix, n_items;
   int total_nodes, max_nodes;
   int Hq, Hkv, G, W;
-  int rows_wg, R, S, chunk;
+  int rows_wg, R, S, tmax;
   float scale, scale_log2;
 };
 
-// One sequence's extents, with every offset checked against the host sizes
-// so that a malformed offset array can never send a load out of bounds.
+// One sequence's extents, every offset checked against the host sizes so a
+// malformed offset array can never send a load out of bounds.
 struct Seq {
   int n0, nn, L;
   long long p0;
@@ -102,40 +112,51 @@ __device__ inline bool decode_seq(const KParams& P, int b, Seq& s) {
   return true;
 }
 
-// Position of key k (0..31 in a tile) inside a transposed V row: within each
-// 16-key group the middle two quads swap, so that the 8 keys one MFMA lane
-// needs for P^T (keys 4h..4h+3 and 8+4h..8+4h+3 of the group) are contiguous.
-__device__ inline int vt_pos(int k) {
-  const int quad = (k >> 2) & 3;
-  const int nq = (quad == 1) ? 2 : (quad == 2) ? 1 : quad;
-  return (k & 16) | (nq << 2) | (k & 3);
+// Tile range of one (sequence, row tile): prefix tiles then tree tiles up to
+// the row tile's last node, and how many splits it gets (in proportion to the
+// longest possible range, so equal-length sequences split identically).
+struct Range {
+  int rows_here, n_hi, Lt, T, Sb;
+};
+
+__device__ inline bool row_tile_range(const KParams& P, const Seq& sq, int r, Range& g) {
+  const int rows_b = sq.nn * P.G;
+  const int row0 = r * P.rows_wg;
+  if (row0 >= rows_b) return false;
+  g.rows_here = min(P.rows_wg, rows_b - row0);
+  g.n_hi = (row0 + g.rows_here - 1) / P.G;
+  g.Lt = (sq.L + kKT - 1) / kKT;
+  g.T = g.Lt + (g.n_hi + kKT) / kKT;
+  int sb = (int)(((long long)P.S * g.T + P.tmax - 1) / P.tmax);
+  g.Sb = max(1, min(sb, min(P.S, g.T)));
+  return true;
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int NW>
-struct TileRegs {
-  static constexpr int NT = NW * 64;
-  static constexpr int KC = (kKT * 16 + NT - 1) / NT;  // 16-byte K chunks per thread
-  static constexpr int VU = (kKT * 8 + NT - 1) / NT;   // (key pair, 8-d chunk) units per thread
-  u32x4_t k[KC];
-  u32x4_t v[2 * VU];
-};
+__device__ inline i16x4_t lds_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(p));
+}
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(KParams P) {
+template <int RG, int KG, int DEPTH>
+__global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
+  static_assert(DEPTH == 1 || DEPTH == 2, "one or two stages of register prefetch");
+  constexpr int NT = RG * KG * 64;
+  constexpr int kStage = KG * kTileBytes;
   extern __shared__ __align__(16) unsigned char lds[];
-  constexpr int NT = NW * 64;
-  using Regs = TileRegs<NW>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int kg = wave / RG;
+  const int rg = wave % RG;
   const int hh = lane >> 5;   // lane half: which 8 of each 16 contraction elements
   const int l32 = lane & 31;
 
-  // Consecutive items (same sequence and KV head) go to the same XCD: the
-  // hardware deals workgroup ids round-robin over the 8 XCDs.
+  // Workgroup ids are dealt round-robin over the 8 XCDs; remap so that
+  // consecutive items (same sequence and KV head, same key split, different
+  // row tiles) run on one XCD.
   const long long nb = gridDim.x;
   const long long item = (long long)(blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
   if (item >= P.n_items) return;
@@ -148,26 +169,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(KParams P) {
 
   Seq sq;
   if (!decode_seq(P, b, sq)) return;
-  const int G = P.G;
-  const int rows_b = sq.nn * G;
-  const int row0 = r * P.rows_wg;
-  if (row0 >= rows_b) return;
-  const int rows_here = min(P.rows_wg, rows_b - row0);
-  const int n_hi = (row0 + rows_here - 1) / G;          // last node of this row tile
+  Range rgn;
+  if (!row_tile_range(P, sq, r, rgn)) return;
+  if (s >= rgn.Sb) return;
+  const int t_lo = (int)((long long)s * rgn.T / rgn.Sb);
+  const int t_hi = (int)((long long)(s + 1) * rgn.T / rgn.Sb);
   const int L = sq.L;
-  const int Lpad = (L + kKT - 1) & ~(kKT - 1);
-  const int keys_total = Lpad + n_hi + 1;
-  const int n_splits = (keys_total + P.chunk - 1) / P.chunk;
-  if (s >= n_splits) return;
-  const int k_begin = s * P.chunk;
-  const int k_end = min(k_begin + P.chunk, keys_total);
+  const int Lt = rgn.Lt;
+  const int row0 = r * P.rows_wg;
 
   // This lane's query row.
-  const int my_row = row0 + wave * 32 + l32;
-  const bool row_ok = my_row < row0 + rows_here;
-  const bool wave_active = wave * 32 < rows_here;
-  const int node = row_ok ? my_row / G : 0;
-  const int head = g * G + (row_ok ? my_row % G : 0);
+  const int my_row = row0 + rg * 32 + l32;
+  const bool row_ok = my_row < row0 + rgn.rows_here;
+  const bool group_active = rg * 32 < rgn.rows_here;
+  const int node = row_ok ? my_row / P.G : 0;
+  const int head = g * P.G + (row_ok ? my_row % P.G : 0);
 
   bf16x8_t qf[8];
   {
@@ -187,68 +203,72 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(KParams P) {
   const uint16_t* kt = P.k_tree + ((size_t)sq.n0 * P.Hkv + g) * kD;
   const uint16_t* vt = P.v_tree + ((size_t)sq.n0 * P.Hkv + g) * kD;
 
-  // Global source row of virtual key kk, or null for padding / past the end.
-  auto src_row = [&](const uint16_t* pre, const uint16_t* tre, int kk) -> const uint16_t* {
-    if (kk < L) return pre + (size_t)kk * kv_row;
-    if (kk >= Lpad && kk < k_end) return tre + (size_t)(kk - Lpad) * kv_row;
-    return nullptr;
-  };
-
-  auto load_tile = [&](int kt0, Regs& rg) {
+  // Stage loader.  For each tile of the stage and each of K, V: thread tid
+  // moves rows key = tid/16 + (NT/16)*u, 16-byte column tid%16, so sixteen
+  // consecutive threads read one 256-byte key row.  Every load reads an
+  // in-bounds row (padding and past-the-end keys read tree row 0); validity
+  // is kept as bits and applied when the stage is written to LDS, so nothing
+  // consumes a load result before the compute of the current stage is done.
+  // The same batch fetches this lane's ancestor-mask word for the tile its
+  // wave handles next.
+  constexpr int kRowsPerPass = NT / 16;
+  constexpr int kPasses = kKT / kRowsPerPass;   // per tile and per K/V
+  static_assert(kPasses * kRowsPerPass == kKT, "tile rows must split evenly");
+  static_assert(KG * kPasses <= 32, "validity bits must fit one word");
+  const int ld_key = tid >> 4;
+  const int ld_col = (tid & 15) * 8;
+  // DEPTH register slots: with two, the loads of stage it+2 are in flight
+  // while stage it is computed and stage it+1 waits in registers.
+  u32x4_t pre[DEPTH][KG][2][kPasses];
+  uint32_t pre_valid[DEPTH];
+  uint64_t mword_pre[DEPTH];
+  auto load_stage = [&](auto slot_c, int tile0) {
+    constexpr int slot = decltype(slot_c)::value;
+    uint32_t bits = 0;
 #pragma unroll
-    for (int j = 0; j < Regs::KC; ++j) {
-      const int c = tid + j * NT;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (c < kKT * 16) {
-        const uint16_t* p = src_row(kp, kt, kt0 + (c >> 4));
-        if (p) v = *reinterpret_cast<const u32x4_t*>(p + (c & 15) * 8);
-      }
-      rg.k[j] = v;
-    }
+    for (int tk = 0; tk < KG; ++tk) {
+      const int tile = tile0 + tk;
 #pragma unroll
-    for (int j = 0; j < Regs::VU; ++j) {
-      const int u = tid + j * NT;
-      u32x4_t a = {0u, 0u, 0u, 0u}, c2 = {0u, 0u, 0u, 0u};
-      if (u < kKT * 8) {
-        const int key = 2 * (u >> 4);
-        const int dc = (u & 15) * 8;
-        const uint16_t* p0 = src_row(vp, vt, kt0 + key);
-        const uint16_t* p1 = src_row(vp, vt, kt0 + key + 1);
-        if (p0) a = *reinterpret_cast<const u32x4_t*>(p0 + dc);
-        if (p1) c2 = *reinterpret_cast<const u32x4_t*>(p1 + dc);
-      }
-      rg.v[2 * j] = a;
-      rg.v[2 * j + 1] = c2;
-    }
-  };
-
-  auto store_tile = [&](unsigned char* stage, const Regs& rg) {
+      for (int u = 0; u < kPasses; ++u) {
+        const int key = ld_key + kRowsPerPass * u;
+        const int kk = tile * kKT + key;
+        const int tn = kk - Lt * kKT;
+        const bool in_prefix = kk < L;
+        const bool in_tree = tile >= Lt && tn < sq.nn;
+        const bool valid = tile < t_hi && (in_prefix || in_tree);
+        bits |= (valid ? 1u : 0u) << (tk * kPasses + u);
+        const size_t off = (size_t)(in_prefix ? kk : (in_tree ? tn : 0)) * kv_row + ld_col;
 #pragma unroll
-    for (int j = 0; j < Regs::KC; ++j) {
-      const int c = tid + j * NT;
-      if (c < kKT * 16)
-        *reinterpret_cast<u32x4_t*>(stage + (c >> 4) * kKStride + (c & 15) * 16) = rg.k[j];
-    }
-    unsigned char* vs = stage + kKTileBytes;
-#pragma unroll
-    for (int j = 0; j < Regs::VU; ++j) {
-      const int u = tid + j * NT;
-      if (u < kKT * 8) {
-        const int key = 2 * (u >> 4);
-        const int dc = (u & 15) * 8;
-        const int pos = vt_pos(key);   // key and key+1 stay adjacent
-        const u32x4_t a = rg.v[2 * j];
-        const u32x4_t c2 = rg.v[2 * j + 1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = (a[e] & 0xffffu) | (c2[e] << 16);
-          const uint32_t hi = (a[e] >> 16) | (c2[e] & 0xffff0000u);
-          *reinterpret_cast<uint32_t*>(vs + (dc + 2 * e) * kVStride + pos * 2) = lo;
-          *reinterpret_cast<uint32_t*>(vs + (dc + 2 * e + 1) * kVStride + pos * 2) = hi;
+        for (int kv = 0; kv < 2; ++kv) {
+          const uint16_t* src = in_prefix ? (kv ? vp : kp) + off : (kv ? vt : kt) + off;
+          pre[slot][tk][kv][u] = *reinterpret_cast<const u32x4_t*>(src);
         }
       }
     }
+    pre_valid[slot] = bits;
+    const int my_tile = tile0 + kg;
+    const int t0 = (my_tile - Lt) * kKT;
+    uint64_t w = 0;
+    if (row_ok && my_tile >= Lt && my_tile < t_hi) w = mrow[t0 >> 6];
+    mword_pre[slot] = w;
   };
+  auto store_stage = [&](auto slot_c, unsigned char* stage) {
+    constexpr int slot = decltype(slot_c)::value;
+#pragma unroll
+    for (int tk = 0; tk < KG; ++tk)
+#pragma unroll
+      for (int u = 0; u < kPasses; ++u) {
+        const int key = ld_key + kRowsPerPass * u;
+        const bool valid = (pre_valid[slot] >> (tk * kPasses + u)) & 1u;
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        unsigned char* kdst = stage + tk * kTileBytes + key * kKStride + ld_col * 2;
+        unsigned char* vdst = stage + tk * kTileBytes + kKBytes + key * kVStride + ld_col * 2;
+        *reinterpret_cast<u32x4_t*>(kdst) = valid ? pre[slot][tk][0][u] : z;
+        *reinterpret_cast<u32x4_t*>(vdst) = valid ? pre[slot][tk][1][u] : z;
+      }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, DEPTH - 1>;
 
   f32x16_t oacc[4];
 #pragma unroll
@@ -259,25 +279,25 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(KParams P) {
   float l_run = 0.f;
   const float c2 = P.scale_log2;
 
-  const int n_tiles = (k_end - k_begin + kKT - 1) / kKT;
-  Regs rg;
-  load_tile(k_begin, rg);
-  store_tile(lds, rg);
-  __syncthreads();
+  // Per-lane offsets of the transposed V reads: a 16-lane group reads a
+  // 4-key x 16-dim block; lane i of the group gets dim (base + i).
+  const int tr_key = (lane & 15) >> 2;
+  const int tr_col = 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
-  for (int it = 0; it < n_tiles; ++it) {
-    const int kt0 = k_begin + it * kKT;
-    unsigned char* cur = lds + (it & 1) * kStageBytes;
-    unsigned char* nxt = lds + ((it + 1) & 1) * kStageBytes;
-    const bool more = it + 1 < n_tiles;
-    if (more) load_tile(kt0 + kKT, rg);
+  const int n_iter = (t_hi - t_lo + KG - 1) / KG;
 
-    if (wave_active) {
-      // S^T = K Q^T for 32 keys x this wave's 32 rows.
+  // One stage of work for this wave: tile (t_lo + it*KG + kg) from LDS.
+  auto compute = [&](const unsigned char* cur, int it, uint64_t mw) {
+    const int tile = t_lo + it * KG + kg;
+    const uint64_t mword = mw;
+    if (group_active && tile < t_hi) {
+      const unsigned char* kb = cur + kg * kTileBytes;
+      const unsigned char* vb = kb + kKBytes;
+      // S^T = K Q^T for this tile's 32 keys x this wave's 32 rows.
       f32x16_t sacc;
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
-      const unsigned char* krow = cur + l32 * kKStride + 16 * hh;
+      const unsigned char* krow = kb + l32 * kKStride + 16 * hh;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(krow + 32 * i);
@@ -285,29 +305,36 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(KParams P) {
                                                        sacc, 0, 0, 0);
       }
       // Accumulator v of this lane holds key 8*(v/4) + 4*hh + v%4 of the tile.
-      if (kt0 >= Lpad) {
-        const int t0 = kt0 - Lpad;   // multiple of 32
-        const uint64_t word = row_ok ? mrow[t0 >> 6] : 0ull;
-        const uint32_t bits = (uint32_t)(word >> (t0 & 63));
+      if (tile >= Lt) {
+        const int t0 = (tile - Lt) * kKT;
+        const uint32_t bits = (uint32_t)(mword >> (t0 & 63));
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = 8 * (v >> 2) + 4 * hh + (v & 3);
           if (!((bits >> key) & 1u)) sacc[v] = kNegInf;
         }
-      } else if (kt0 + kKT > L) {
+      } else if ((tile + 1) * kKT > L) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (kt0 + key >= L) sacc[v] = kNegInf;
+          if (tile * kKT + key >= L) sacc[v] = kNegInf;
         }
       }
       float mt = sacc[0];
 #pragma unroll
       for (int v = 1; v < 16; ++v) mt = fmaxf(mt, sacc[v]);
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run - m_use) * c2);
+      // Lazy running max: the reference moves only when the tile's max
+      // exceeds it by more than kLazyLog2 (log2 units), so after the first
+      // tiles the output is almost never rescaled; probabilities stay below
+      // 2^kLazyLog2 and numerator and denominator share the reference, so
+      // the result is unchanged.  Lanes l and l^32 hold the same row and take
+      // the same decision.
+      const bool move = (mt - m_run) * c2 > kLazyLog2;   // also true when m_run = -inf
+      const float m_old = m_run;
+      if (move) m_run = mt;
+      const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+      const float alpha = move ? fast_exp2((m_old - m_use) * c2) : 1.f;
       const float mc = m_use * c2;
       float ps = 0.f;
       f32x16_t p;
@@ -317,36 +344,118 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(KParams P) {
         ps += p[v];
       }
       l_run = fmaf(l_run, alpha, ps);
-      m_run = m_new;
+      if (__ballot(move)) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[e][v] *= alpha;
+          for (int v = 0; v < 16; ++v) oacc[e][v] *= alpha;
+      }
 
-      // O^T += V^T P^T, two 16-key steps.
+      // O^T += V^T P^T: two 16-key steps x four 32-dim blocks.
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         f32x8_t pf;
 #pragma unroll
         for (int j = 0; j < 8; ++j) pf[j] = p[8 * cc + j];
         const bf16x8_t pb = __builtin_convertvector(pf, bf16x8_t);
-        const unsigned char* vrow = cur + kKTileBytes + l32 * kVStride + (16 * cc + 8 * hh) * 2;
+        // slots 0-3: keys 16cc+4hh+0..3, slots 4-7: keys 16cc+8+4hh+0..3
+        const unsigned char* v0 = vb + (16 * cc + 4 * hh + tr_key) * kVStride + tr_col;
+        const unsigned char* v1 = v0 + 8 * kVStride;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(vrow + 32 * e * kVStride);
-          oacc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pb,
+          const i16x4_t lo = lds_read_tr16(v0 + 64 * e);
+          const i16x4_t hi = lds_read_tr16(v1 + 64 * e);
+          const i16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb,
                                                             oacc[e], 0, 0, 0);
         }
       }
     }
-    if (more) store_tile(nxt, rg);
+  };
+
+  unsigned char* buf0 = lds;
+  unsigned char* buf1 = lds + kStage;
+  if (DEPTH == 1) {
+    load_stage(S0{}, t_lo);
+    store_stage(S0{}, buf0);
+    uint64_t mw = mword_pre[0];
     __syncthreads();
+    for (int it = 0; it < n_iter; ++it) {
+      unsigned char* cur = (it & 1) ? buf1 : buf0;
+      unsigned char* nxt = (it & 1) ? buf0 : buf1;
+      const bool more = it + 1 < n_iter;
+      if (more) load_stage(S0{}, t_lo + (it + 1) * KG);
+      compute(cur, it, mw);
+      if (more) {
+        store_stage(S0{}, nxt);
+        mw = mword_pre[0];
+      }
+      __syncthreads();
+    }
+  } else {
+    // Two slots, loop unrolled by two so each slot is named statically:
+    // even iterations compute buf0 while slot 1 waits and slot 0 refills.
+    load_stage(S0{}, t_lo);
+    if (n_iter > 1) load_stage(S1{}, t_lo + KG);
+    store_stage(S0{}, buf0);
+    uint64_t mw = mword_pre[0];
+    __syncthreads();
+    for (int it = 0; it < n_iter; it += 2) {
+      if (it + 2 < n_iter) load_stage(S0{}, t_lo + (it + 2) * KG);
+      compute(buf0, it, mw);
+      if (it + 1 < n_iter) {
+        store_stage(S1{}, buf1);
+        mw = mword_pre[DEPTH - 1];
+      }
+      __syncthreads();
+      if (it + 1 >= n_iter) break;
+      if (it + 3 < n_iter) load_stage(S1{}, t_lo + (it + 3) * KG);
+      compute(buf1, it + 1, mw);
+      if (it + 2 < n_iter) {
+        store_stage(S0{}, buf0);
+        mw = mword_pre[0];
+      }
+      __syncthreads();
+    }
   }
 
-  if (!row_ok) return;
+  if (KG > 1) {
+    // Merge the key groups through LDS (the stage buffers are free now):
+    // O in register order [rg][v][lane], then max and per-lane sum.
+    float* xo = reinterpret_cast<float*>(lds);
+    float* xm = xo + RG * 64 * 64;
+    float* xl = xm + RG * 64;
+    if (kg == 1 && group_active) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) xo[(rg * 64 + 16 * e + v) * 64 + lane] = oacc[e][v];
+      xm[rg * 64 + lane] = m_run;
+      xl[rg * 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (kg != 0 || !group_active) return;
+    const float m1 = xm[rg * 64 + lane];
+    const float l1 = xl[rg * 64 + lane];
+    const float mm = fmaxf(m_run, m1);
+    const float mu = (mm == kNegInf) ? 0.f : mm;
+    const float a0 = fast_exp2((m_run - mu) * c2);
+    const float a1 = fast_exp2((m1 - mu) * c2);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        oacc[e][v] = oacc[e][v] * a0 + xo[(rg * 64 + 16 * e + v) * 64 + lane] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_run = mm;
+  } else if (!group_active) {
+    return;
+  }
+
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  // Accumulator v of oacc[e] holds d = 32e + 8*(v/4) + 4*hh + v%4 of this row.
-  if (n_splits == 1) {
+  if (!row_ok) return;
+  // Accumulator v of oacc[e] holds dim 32e + 8*(v/4) + 4*hh + v%4 of this row.
+  if (rgn.Sb == 1) {
     const float inv = 1.f / l_tot;
     uint16_t* orow = P.out + ((size_t)(sq.n0 + node) * P.Hq + head) * kD;
 #pragma unroll
@@ -356,216 +465,158 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(KParams P) {
         f32x4_t f;
 #pragma unroll
         for (int x = 0; x < 4; ++x) f[x] = oacc[e][4 * j + x] * inv;
-        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
         const bf16x4_t h4 = __builtin_convertvector(f, bf16x4_t);
         *reinterpret_cast<u32x2_t*>(orow + 32 * e + 8 * j + 4 * hh) = __builtin_bit_cast(u32x2_t, h4);
       }
     if (P.lse && hh == 0) P.lse[(size_t)(sq.n0 + node) * P.Hq + head] = m_run * P.scale + logf(l_tot);
   } else {
-    const size_t prow = (size_t)item * P.rows_wg + (my_row - row0);
-    float* wo = P.ws_o + prow * kD;
+    // Normalised partial O in bf16 (the merge reweights by l), lane-major so
+    // each store instruction writes 512 contiguous bytes.
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    u32x2_t* wo = P.ws_o + ((size_t)item * RG + rg) * 16 * 64 + lane;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         f32x4_t f;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) f[x] = oacc[e][4 * j + x];
-        *reinterpret_cast<f32x4_t*>(wo + 32 * e + 8 * j + 4 * hh) = f;
+        for (int x = 0; x < 4; ++x) f[x] = oacc[e][4 * j + x] * inv;
+        wo[(4 * e + j) * 64] = __builtin_bit_cast(u32x2_t, __builtin_convertvector(f, bf16x4_t));
       }
-    if (hh == 0) {
-      P.ws_ml[2 * prow] = m_run;
-      P.ws_ml[2 * prow + 1] = l_tot;
-    }
+    if (hh == 0) P.ws_ml[(size_t)item * P.rows_wg + rg * 32 + l32] = make_float2(m_run, l_tot);
   }
 }
 
-// Log-sum-exp merge of the split partials of one (sequence, KV head, row
-// tile): with M = max_s m_s and w_s = exp(scale * (m_s - M)),
-//   out = sum_s w_s O_s / sum_s w_s l_s,  lse = scale * M + log(sum_s w_s l_s).
-// Splits that saw no visible key carry m = -inf and weigh nothing.
+// Log-sum-exp merge of the splits of one (sequence, KV head, row tile, row
+// group, 32-dim block): split s left its normalised output O_s (bf16), its
+// running max m_s and sum l_s; with M = max_s m_s and
+// w_s = l_s * exp(scale*(m_s - M)),
+//   out = sum_s w_s O_s / sum_s w_s,  lse = scale*M + log(sum_s w_s).
+// Splits that saw no visible key carry m = -inf and weigh nothing.  Thread
+// (wave j, lane) owns dims 32e + 8j + 4*(lane/32) .. +3 of row lane%32.
+template <int RG>
 __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
-  const int grp = blockIdx.x;
-  const int r = grp % P.R;
-  const int g = (grp / P.R) % P.Hkv;
-  const int b = grp / (P.R * P.Hkv);
+  long long t = blockIdx.x;
+  const int e = (int)(t % 4);
+  t /= 4;
+  const int rg = (int)(t % RG);
+  t /= RG;
+  const int r = (int)(t % P.R);
+  t /= P.R;
+  const int g = (int)(t % P.Hkv);
+  const int b = (int)(t / P.Hkv);
   Seq sq;
   if (!decode_seq(P, b, sq)) return;
-  const int G = P.G;
-  const int rows_b = sq.nn * G;
-  const int row0 = r * P.rows_wg;
-  if (row0 >= rows_b) return;
-  const int rows_here = min(P.rows_wg, rows_b - row0);
-  const int n_hi = (row0 + rows_here - 1) / G;
-  const int Lpad = (sq.L + kKT - 1) & ~(kKT - 1);
-  const int n_splits = (Lpad + n_hi + 1 + P.chunk - 1) / P.chunk;
-  if (n_splits <= 1) return;
+  Range rgn;
+  if (!row_tile_range(P, sq, r, rgn)) return;
+  if (rgn.Sb <= 1 || rg * 32 >= rgn.rows_here) return;
+  const int lane = threadIdx.x & 63;
+  const int j = threadIdx.x >> 6;
+  const int hh = lane >> 5;
+  const int rl = rg * 32 + (lane & 31);
+  if (rl >= rgn.rows_here) return;
   const float c2 = P.scale_log2;
   const long long item0 = ((long long)(b * P.Hkv + g) * P.S) * P.R + r;   // split s adds s*R
+  const int Sb = rgn.Sb;
 
-  for (int idx = threadIdx.x; idx < rows_here * 32; idx += blockDim.x) {
-    const int rl = idx >> 5;
-    const int d0 = (idx & 31) * 4;
-    float M = kNegInf;
-    for (int s = 0; s < n_splits; ++s) {
-      const size_t prow = (size_t)(item0 + (long long)s * P.R) * P.rows_wg + rl;
-      M = fmaxf(M, P.ws_ml[2 * prow]);
-    }
-    float lsum = 0.f;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    if (M != kNegInf) {
-      for (int s = 0; s < n_splits; ++s) {
-        const size_t prow = (size_t)(item0 + (long long)s * P.R) * P.rows_wg + rl;
-        const float w = fast_exp2((P.ws_ml[2 * prow] - M) * c2);
-        lsum = fmaf(w, P.ws_ml[2 * prow + 1], lsum);
-        const f32x4_t o = *reinterpret_cast<const f32x4_t*>(P.ws_o + prow * kD + d0);
-        acc += w * o;
+  // Online merge, eight splits' loads in flight per batch.
+  constexpr int kBatch = 8;
+  float M = kNegInf;
+  float lsum = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < Sb; s0 += kBatch) {
+    float2 ml[kBatch];
+    f32x4_t o[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      ml[k] = make_float2(kNegInf, 0.f);
+      o[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (s0 + k < Sb) {
+        const long long it = item0 + (long long)(s0 + k) * P.R;
+        ml[k] = P.ws_ml[(size_t)it * P.rows_wg + rl];
+        const u32x2_t h = P.ws_o[(((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane];
+        o[k] = f32x4_t{__uint_as_float(h[0] << 16), __uint_as_float(h[0] & 0xffff0000u),
+                       __uint_as_float(h[1] << 16), __uint_as_float(h[1] & 0xffff0000u)};
       }
     }
-    const int my_row = row0 + rl;
-    const int node = my_row / G;
-    const int head = g * G + my_row % G;
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-    const bf16x4_t h4 = __builtin_convertvector(acc * inv, bf16x4_t);
-    *reinterpret_cast<u32x2_t*>(P.out + ((size_t)(sq.n0 + node) * P.Hq + head) * kD + d0) =
-        __builtin_bit_cast(u32x2_t, h4);
-    if (P.lse && d0 == 0)
-      P.lse[(size_t)(sq.n0 + node) * P.Hq + head] =
-          lsum > 0.f ? M * P.scale + logf(lsum) : kNegInf;
-  }
-}
-
-// ------------------------------------------------------------------ fp32 path
-
-struct F32Params {
-  const float* q;
-  const float* k_tree;
-  const float* v_tree;
-  const float* k_prefix;
-  const float* v_prefix;
-  const int64_t* prefix_offsets;
-  const int32_t* node_offsets;
-  const uint64_t* mask;
-  float* out;
-  float* lse;
-  long long total_prefix, max_prefix;
-  int B, total_nodes, max_nodes, Hq, Hkv, G, D, W;
-  float scale;
-};
-
-__device__ inline float wave_sum(float x) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-__global__ __launch_bounds__(256) void fwd_f32_kernel(F32Params P) {
-  const int lane = threadIdx.x & 63;
-  const long long wid = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wid >= (long long)P.total_nodes * P.Hq) return;
-  const int gnode = (int)(wid / P.Hq);
-  const int head = (int)(wid % P.Hq);
-  const int g = head / P.G;
-  // Sequence of this node: last b with node_offsets[b] <= gnode.
-  int lo = 0, hi = P.B;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (P.node_offsets[mid] <= gnode) lo = mid; else hi = mid;
-  }
-  const int b = lo;
-  const int n0 = P.node_offsets[b], n1 = P.node_offsets[b + 1];
-  const long long p0 = P.prefix_offsets[b], p1 = P.prefix_offsets[b + 1];
-  if (n0 < 0 || n1 <= n0 || n1 - n0 > P.max_nodes || n1 > P.total_nodes) return;
-  if (gnode < n0 || gnode >= n1) return;
-  if (p0 < 0 || p1 < p0 || p1 - p0 > P.max_prefix || p1 > P.total_prefix) return;
-  const int nn = n1 - n0;
-  const int D = P.D;
-  float qv[4], acc[4];
-  const float* qrow = P.q + ((size_t)gnode * P.Hq + head) * D;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int d = lane + 64 * j;
-    qv[j] = d < D ? qrow[d] : 0.f;
-    acc[j] = 0.f;
-  }
-  float m = kNegInf, l = 0.f;
-  auto step = [&](const float* krow, const float* vrow) {
-    float part = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = lane + 64 * j;
-      if (d < D) part = fmaf(qv[j], krow[d], part);
-    }
-    const float sc = wave_sum(part) * P.scale;
-    const float m_new = fmaxf(m, sc);
-    const float alpha = expf(m - m_new);
-    const float p = expf(sc - m_new);
-    l = l * alpha + p;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = lane + 64 * j;
-      acc[j] = acc[j] * alpha + (d < D ? p * vrow[d] : 0.f);
-    }
-    m = m_new;
-  };
-  const size_t kv_row = (size_t)P.Hkv * D;
-  for (long long k = 0; k < p1 - p0; ++k)
-    step(P.k_prefix + (size_t)(p0 + k) * kv_row + (size_t)g * D,
-         P.v_prefix + (size_t)(p0 + k) * kv_row + (size_t)g * D);
-  const uint64_t* mrow = P.mask + (size_t)gnode * P.W;
-  for (int w = 0; w < P.W; ++w) {
-    uint64_t bits = mrow[w];
-    while (bits) {
-      const int tn = 64 * w + __builtin_ctzll(bits);
-      bits &= bits - 1;
-      if (tn >= nn) break;
-      step(P.k_tree + (size_t)(n0 + tn) * kv_row + (size_t)g * D,
-           P.v_tree + (size_t)(n0 + tn) * kv_row + (size_t)g * D);
+    for (int k = 0; k < kBatch; ++k) {
+      const float m_new = fmaxf(M, ml[k].x);
+      const float mu = (m_new == kNegInf) ? 0.f : m_new;
+      const float a = fast_exp2((M - mu) * c2);
+      const float w = fast_exp2((ml[k].x - mu) * c2) * ml[k].y;
+      acc = acc * a + w * o[k];
+      lsum = lsum * a + w;
+      M = m_new;
     }
   }
-  float* orow = P.out + ((size_t)gnode * P.Hq + head) * D;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int d = lane + 64 * j;
-    if (d < D) orow[d] = acc[j] * inv;
-  }
-  if (P.lse && lane == 0) P.lse[(size_t)gnode * P.Hq + head] = l > 0.f ? m + logf(l) : kNegInf;
+  const int my_row = r * P.rows_wg + rl;
+  const int node = my_row / P.G;
+  const int head = g * P.G + my_row % P.G;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const bf16x4_t h4 = __builtin_convertvector(acc * inv, bf16x4_t);
+  *reinterpret_cast<u32x2_t*>(P.out + ((size_t)(sq.n0 + node) * P.Hq + head) * kD + 32 * e + 8 * j +
+                              4 * hh) = __builtin_bit_cast(u32x2_t, h4);
+  if (P.lse && e == 0 && j == 0 && hh == 0)
+    P.lse[(size_t)(sq.n0 + node) * P.Hq + head] = lsum > 0.f ? M * P.scale + logf(lsum) : kNegInf;
 }
 
-template <int NW>
-hipError_t launch_nw(const KParams& kp, long long grid, hipStream_t stream) {
-  hipLaunchKernelGGL(fwd_bf16_kernel<NW>, dim3((unsigned)grid), dim3(NW * 64), 2 * kStageBytes,
-                     stream, kp);
+template <int RG, int KG, int DEPTH>
+hipError_t launch_shape(const KParams& kp, long long grid, long long merge_grid, hipStream_t stream) {
+  const size_t lds = 2 * (size_t)KG * kTileBytes;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&fwd_bf16_kernel<RG, KG, DEPTH>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((fwd_bf16_kernel<RG, KG, DEPTH>), dim3((unsigned)grid), dim3(RG * KG * 64),
+                     lds, stream, kp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || merge_grid == 0) return e;
+  hipLaunchKernelGGL((merge_bf16_kernel<RG>), dim3((unsigned)merge_grid), dim3(256), 0, stream, kp);
   return hipGetLastError();
+}
+
+int pow2_ceil(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
 }
 
 }  // namespace
 
 FwdPlan plan_forward_bf16(int B, int total_nodes, int max_nodes, int Hq, int Hkv,
                           long long total_prefix, long long max_prefix) {
+  (void)total_nodes;
   FwdPlan p{};
   const int G = Hq / Hkv;
   const long long rows_max = (long long)max_nodes * G;
-  p.nwaves = (int)std::min<long long>(8, (rows_max + 31) / 32);
-  if (p.nwaves == 3) p.nwaves = 4;
-  if (p.nwaves >= 5) p.nwaves = 8;
-  p.rows_wg = 32 * p.nwaves;
+  if (rows_max <= 128) {
+    p.rg = pow2_ceil((int)((rows_max + 31) / 32));
+    p.kg = 2;
+  } else {
+    // Many row tiles already fill the chip: one key group, 256-row tiles.
+    // Few: 128-row tiles with two key groups halve the split partials.
+    const long long units8 = (long long)B * Hkv * ((rows_max + 255) / 256);
+    p.rg = units8 >= 128 ? 8 : 4;
+    p.kg = units8 >= 128 ? 1 : 2;
+  }
+  p.nwaves = p.rg * p.kg;
+  p.rows_wg = 32 * p.rg;
   p.R = (int)((rows_max + p.rows_wg - 1) / p.rows_wg);
-  const long long keys_max = ((max_prefix + kKT - 1) / kKT) * kKT + max_nodes;
-  // Aim for about two workgroups per compute unit over the whole call; never
-  // split below 4 tiles, never above the longest sequence.
-  const long long total_keys = total_prefix + (long long)kKT * B + total_nodes;
-  const long long target_items = 512;
-  long long chunk = (total_keys * Hkv * p.R + target_items - 1) / target_items;
-  chunk = ((chunk + kKT - 1) / kKT) * kKT;
-  chunk = std::max<long long>(chunk, 4 * kKT);
-  chunk = std::min<long long>(chunk, ((keys_max + kKT - 1) / kKT) * kKT);
-  p.chunk = (int)chunk;
-  p.S = (int)((keys_max + chunk - 1) / chunk);
-  p.n_items = (long long)B * Hkv * p.S * p.R;
-  p.ws_bytes = p.S > 1 ? (size_t)p.n_items * p.rows_wg * (kD + 2) * sizeof(float) : 0;
+  p.tmax = (int)((max_prefix + kKT - 1) / kKT + (max_nodes + kKT - 1) / kKT);
+  // Splits: aim for one full round of workgroups (256 CUs); twice that when
+  // prefix lengths are ragged so short and long sequences balance out.  Keep
+  // at least two iterations per split.
+  const long long units = (long long)B * Hkv * p.R;
+  const bool ragged = max_prefix * B > total_prefix + total_prefix / 4;
+  const long long target = ragged ? 512 : 256;
+  long long S = (target + units - 1) / units;
+  S = std::min<long long>(S, std::max(1, p.tmax / (2 * p.kg)));
+  p.S = (int)std::max<long long>(1, S);
+  p.n_items = units * p.S;
+  p.ws_bytes = p.S > 1 ? (size_t)p.n_items * p.rows_wg * (kD * 2 + 8) : 0;
   return p;
 }
 
@@ -582,8 +633,9 @@ hipError_t launch_forward_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t s
   kp.out = static_cast<uint16_t*>(a.out);
   kp.lse = a.lse;
   if (p.S > 1) {
-    kp.ws_o = static_cast<float*>(a.workspace);
-    kp.ws_ml = kp.ws_o + (size_t)p.n_items * p.rows_wg * kD;
+    kp.ws_o = static_cast<u32x2_t*>(a.workspace);
+    kp.ws_ml = reinterpret_cast<float2*>(static_cast<unsigned char*>(a.workspace) +
+                                         (size_t)p.n_items * p.rows_wg * kD * 2);
   }
   kp.total_prefix = a.total_prefix;
   kp.max_prefix = a.max_prefix;
@@ -597,49 +649,18 @@ hipError_t launch_forward_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t s
   kp.rows_wg = p.rows_wg;
   kp.R = p.R;
   kp.S = p.S;
-  kp.chunk = p.chunk;
+  kp.tmax = p.tmax;
   kp.scale = a.scale;
   kp.scale_log2 = a.scale * kLog2e;
   const long long grid = (p.n_items + 7) / 8 * 8;
-  hipError_t e;
-  switch (p.nwaves) {
-    case 1: e = launch_nw<1>(kp, grid, stream); break;
-    case 2: e = launch_nw<2>(kp, grid, stream); break;
-    case 4: e = launch_nw<4>(kp, grid, stream); break;
-    default: e = launch_nw<8>(kp, grid, stream); break;
+  const long long merge_grid = p.S > 1 ? (long long)a.B * a.Hkv * p.R * p.rg * 4 : 0;
+  switch (p.rg * 16 + p.kg) {
+    case 1 * 16 + 2: return launch_shape<1, 2, 1>(kp, grid, merge_grid, stream);
+    case 2 * 16 + 2: return launch_shape<2, 2, 1>(kp, grid, merge_grid, stream);
+    case 4 * 16 + 2: return launch_shape<4, 2, 2>(kp, grid, merge_grid, stream);
+    case 8 * 16 + 1: return launch_shape<8, 1, 2>(kp, grid, merge_grid, stream);
+    default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess || p.S <= 1) return e;
-  const long long groups = (long long)a.B * a.Hkv * p.R;
-  hipLaunchKernelGGL(merge_bf16_kernel, dim3((unsigned)groups), dim3(256), 0, stream, kp);
-  return hipGetLastError();
-}
-
-hipError_t launch_forward_f32(const FwdArgs& a, hipStream_t stream) {
-  F32Params fp{};
-  fp.q = static_cast<const float*>(a.q);
-  fp.k_tree = static_cast<const float*>(a.k_tree);
-  fp.v_tree = static_cast<const float*>(a.v_tree);
-  fp.k_prefix = static_cast<const float*>(a.k_prefix);
-  fp.v_prefix = static_cast<const float*>(a.v_prefix);
-  fp.prefix_offsets = a.prefix_offsets;
-  fp.node_offsets = a.node_offsets;
-  fp.mask = a.mask;
-  fp.out = static_cast<float*>(a.out);
-  fp.lse = a.lse;
-  fp.total_prefix = a.total_prefix;
-  fp.max_prefix = a.max_prefix;
-  fp.B = a.B;
-  fp.total_nodes = a.total_nodes;
-  fp.max_nodes = a.max_nodes;
-  fp.Hq = a.Hq;
-  fp.Hkv = a.Hkv;
-  fp.G = a.Hq / a.Hkv;
-  fp.D = a.D;
-  fp.W = a.W;
-  fp.scale = a.scale;
-  const long long waves = (long long)a.total_nodes * a.Hq;
-  hipLaunchKernelGGL(fwd_f32_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, fp);
-  return hipGetLastError();
 }
 
 }  // namespace ta

@@ -13,11 +13,13 @@ namespace ta {
 // Work decomposition of one tree_attn_forward call on the bf16 MFMA path.
 // Derived from host scalars only, so the workspace query and the call agree.
 struct FwdPlan {
-  int nwaves;      // waves per workgroup; each wave owns 32 query rows
-  int rows_wg;     // query rows per workgroup = 32 * nwaves
+  int rg;          // row groups per workgroup (one wave = 32 query rows each)
+  int kg;          // key groups per workgroup (waves sharing rows, alternate tiles)
+  int nwaves;      // rg * kg
+  int rows_wg;     // query rows per workgroup = 32 * rg
   int R;           // row tiles per (sequence, KV head) = ceil(max_nodes*G / rows_wg)
-  int S;           // key splits per row tile (upper bound over sequences)
-  int chunk;       // keys per split, a multiple of the 32-key tile
+  int S;           // key splits for the longest possible tile range
+  int tmax;        // that longest range, in 32-key tiles
   long long n_items;   // B * Hkv * S * R
   size_t ws_bytes;     // partial (O, m, l) storage; 0 when S == 1
 };

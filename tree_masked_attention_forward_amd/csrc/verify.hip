@@ -27,6 +27,8 @@
 namespace ta {
 namespace {
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
 constexpr float kNegInf = -__builtin_inff();
 
@@ -47,7 +49,11 @@ __device__ inline void wave_best(float& bv, int& bi) {
 }
 
 // VEC: elements per 16-byte load (8 for bf16, 4 for fp32), or 1 for scalar
-// loads when the row start is not 16-byte aligned.
+// loads when rows are not 16-byte aligned.  Each thread keeps kUnroll loads
+// in flight before comparing, so one workgroup streams a whole chunk
+// (kUnroll * 256 * VEC elements per pass) at full memory-level parallelism.
+constexpr int kUnroll = 8;
+
 template <bool BF16, int VEC>
 __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const void* __restrict__ logits,
                                                                   int V, int cpr, int chunk,
@@ -59,23 +65,38 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const void* __
   float bv = kNegInf;
   int bi = 0x7fffffff;
   if (VEC > 1) {
-    for (int e = lo + threadIdx.x * VEC; e < hi; e += kThreads * VEC) {
-      uint4 u;
-      if (BF16)
-        u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(logits) + row * V + e);
-      else
-        u = *reinterpret_cast<const uint4*>(static_cast<const float*>(logits) + row * V + e);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    for (int base = lo; base < hi; base += kThreads * VEC * kUnroll) {
+      u32x4_t u[kUnroll];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (BF16) {
-          const float a = __uint_as_float(w[j] << 16);
-          const float b = __uint_as_float(w[j] & 0xffff0000u);
-          if (better(a, e + 2 * j, bv, bi)) { bv = a; bi = e + 2 * j; }
-          if (better(b, e + 2 * j + 1, bv, bi)) { bv = b; bi = e + 2 * j + 1; }
+      for (int k = 0; k < kUnroll; ++k) {
+        const int e = base + (k * kThreads + threadIdx.x) * VEC;
+        if (e < hi) {
+          if (BF16)
+            u[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+                static_cast<const uint16_t*>(logits) + row * V + e));
+          else
+            u[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+                static_cast<const float*>(logits) + row * V + e));
         } else {
-          const float a = __uint_as_float(w[j]);
-          if (better(a, e + j, bv, bi)) { bv = a; bi = e + j; }
+          u[k] = u32x4_t{0u, 0u, 0u, 0u};   // never compared: e >= hi
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kUnroll; ++k) {
+        const int e = base + (k * kThreads + threadIdx.x) * VEC;
+        if (e >= hi) continue;
+        const uint32_t w[4] = {u[k][0], u[k][1], u[k][2], u[k][3]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (BF16) {
+            const float a = __uint_as_float(w[j] << 16);
+            const float b = __uint_as_float(w[j] & 0xffff0000u);
+            if (better(a, e + 2 * j, bv, bi)) { bv = a; bi = e + 2 * j; }
+            if (better(b, e + 2 * j + 1, bv, bi)) { bv = b; bi = e + 2 * j + 1; }
+          } else {
+            const float a = __uint_as_float(w[j]);
+            if (better(a, e + j, bv, bi)) { bv = a; bi = e + j; }
+          }
         }
       }
     }
@@ -130,28 +151,32 @@ __global__ __launch_bounds__(kThreads) void path_select_kernel(
   for (int w = tid; w < W; w += kThreads) match_w[w] = 0ull;
   __syncthreads();
 
-  const int rounds = nn > 0 ? (nn + kThreads - 1) / kThreads : 0;
-  for (int it = 0; it < rounds; ++it) {
-    const int i = it * kThreads + tid;
-    bool m = false;
-    if (i < nn) {
-      float bv = kNegInf;
-      int bi = 0x7fffffff;
-      const float2* pr = ws + (size_t)(n0 + i) * cpr;
-      for (int c = 0; c < cpr; ++c) {
-        const float2 x = pr[c];
-        const int xi = __float_as_int(x.y);
-        if (better(x.x, xi, bv, bi)) {
-          bv = x.x;
-          bi = xi;
-        }
-      }
-      if (target_argmax) target_argmax[n0 + i] = bi;
-      m = draft[n0 + i] == bi;
+  // Target argmax per node: the cpr chunk results of one node sit in cpr
+  // consecutive lanes of one wave (cpr is a power of two <= 64); a segmented
+  // butterfly leaves the winner in the node's first lane.
+  const int pairs = nn > 0 ? nn * cpr : 0;
+  for (int p0 = 0; p0 < pairs; p0 += kThreads) {
+    const int pidx = p0 + tid;
+    float bv = kNegInf;
+    int bi = 0x7fffffff;
+    if (pidx < pairs) {
+      const float2 x = ws[(size_t)n0 * cpr + pidx];
+      bv = x.x;
+      bi = __float_as_int(x.y);
     }
-    const unsigned long long bal = __ballot(m);
-    const int word = (it * kThreads + wave * 64) >> 6;
-    if (lane == 0 && word < W) match_w[word] = bal;
+    for (int o = cpr >> 1; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (pidx < pairs && (pidx & (cpr - 1)) == 0) {
+      const int i = pidx / cpr;
+      if (target_argmax) target_argmax[n0 + i] = bi;
+      if (draft[n0 + i] == bi) atomicOr(&match_w[i >> 6], 1ull << (i & 63));
+    }
   }
   __syncthreads();
 
@@ -209,15 +234,18 @@ __global__ __launch_bounds__(kThreads) void path_select_kernel(
 }  // namespace
 
 VerifyPlan plan_verify(int total_nodes, int V) {
+  (void)total_nodes;
   VerifyPlan p{};
-  // Enough workgroups to cover the chip (the logits scan is bound by HBM):
-  // split short batches' rows into vocabulary chunks of at least 4096 entries.
-  const int rows = std::max(total_nodes, 1);
-  int cpr = (2048 + rows - 1) / rows;
-  cpr = std::max(1, std::min(cpr, (V + 4095) / 4096));
+  // One chunk is one pass of the unrolled scan (16384 bf16 / 8192 fp32 would
+  // both fit; 16384 entries is used for either) so each workgroup streams 32
+  // or 64 KB; chunks per row are a power of two (at most 64) for the
+  // in-wave reduction in path_select_kernel.
+  const int target = kThreads * 8 * kUnroll;
+  int cpr = 1;
+  while (cpr < 64 && (long long)cpr * target < V) cpr <<= 1;
   int chunk = (V + cpr - 1) / cpr;
   chunk = (chunk + 7) / 8 * 8;
-  p.cpr = (V + chunk - 1) / chunk;
+  p.cpr = cpr;
   p.chunk = chunk;
   p.ws_bytes = (size_t)total_nodes * p.cpr * sizeof(float2);
   return p;
