@@ -63,10 +63,10 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kD = 128;                       // head size of the MFMA path
 constexpr int kKT = 32;                       // keys per tile
-constexpr int kKStride = kD * 2 + 16;         // LDS bytes per K row: 68 dwords, conflict-free b128 reads
-constexpr int kVStride = kD * 2 + 64;         // LDS bytes per V row: 80 dwords, for the 4-row transpose reads
-constexpr int kKBytes = kKT * kKStride;       // 8704
-constexpr int kTileBytes = kKBytes + kKT * kVStride;   // 18944: one K tile + one V tile
+constexpr int kRow = kD * 2;                  // LDS bytes per K or V row (unpadded, chunks swizzled)
+constexpr int kTileKV = kKT * kRow;           // 8192: one K or one V tile
+constexpr int kTileBytes = 2 * kTileKV;       // K tile then V tile
+constexpr int kNumStages = 3;                 // LDS ring: stage it in use, it+1 and it+2 in flight
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazyLog2 = 8.f;              // running-max slack: probabilities stay <= 256
@@ -134,21 +134,48 @@ __device__ inline bool row_tile_range(const KParams& P, const Seq& sq, int r, Ra
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Direct global -> LDS loads, issued through inline asm so that the only
+// waits on them are the explicit vmcnt waits of the pipeline (the compiler
+// would otherwise wait for every pending load before each LDS read).  The
+// LDS base goes to M0 and must be wave-uniform; lane i's data lands at
+// base + i * size.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
+}
+__device__ inline void dma_b128(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_base), "v"(g)
+               : "memory", "m0");
+}
+__device__ inline void dma_b32(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(lds_base), "v"(g)
+               : "memory", "m0");
+}
+
 __device__ inline i16x4_t lds_read_tr16(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4_t*)(p));
 }
 
-template <int RG, int KG, int DEPTH>
+template <int RG, int KG, int TPW>
 __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
-  static_assert(DEPTH == 1 || DEPTH == 2, "one or two stages of register prefetch");
-  constexpr int NT = RG * KG * 64;
-  constexpr int kStage = KG * kTileBytes;
+  constexpr int NW = RG * KG;
+  constexpr int NT = NW * 64;
+  constexpr int kTilesPerStage = KG * TPW;
+  // Stage layout: KG*TPW x (K tile, V tile), then TPW mask dwords per lane
+  // per wave.
+  constexpr int kMaskOff = kTilesPerStage * kTileBytes;
+  constexpr int kStage = kMaskOff + NW * TPW * 256;
   extern __shared__ __align__(16) unsigned char lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // Wave-uniform values live in scalar registers, so tile-type tests below
+  // are uniform branches (the masking code is skipped on prefix tiles).
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = wave / RG;
   const int rg = wave % RG;
   const int hh = lane >> 5;   // lane half: which 8 of each 16 contraction elements
@@ -187,12 +214,19 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
 
   bf16x8_t qf[8];
   {
+    // Rows past the tile's end read row 0 of the tile (in bounds) and are
+    // zeroed; their outputs are never written.
     const uint16_t* qrow = P.q + ((size_t)(sq.n0 + node) * P.Hq + head) * kD + 8 * hh;
+    u32x4_t qv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] = *reinterpret_cast<const u32x4_t*>(qrow + 16 * i);
+    // Retire the query loads here, before any pipeline load is issued, so
+    // the compiler never needs a later catch-all wait for them.
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = *reinterpret_cast<const u32x4_t*>(qrow + 16 * i);
-      qf[i] = __builtin_bit_cast(bf16x8_t, v);
+      if (!row_ok) qv[i] = u32x4_t{0u, 0u, 0u, 0u};
+      qf[i] = __builtin_bit_cast(bf16x8_t, qv[i]);
     }
   }
   const uint64_t* mrow = P.mask + (size_t)(sq.n0 + node) * P.W;
@@ -203,72 +237,89 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
   const uint16_t* kt = P.k_tree + ((size_t)sq.n0 * P.Hkv + g) * kD;
   const uint16_t* vt = P.v_tree + ((size_t)sq.n0 * P.Hkv + g) * kD;
 
-  // Stage loader.  For each tile of the stage and each of K, V: thread tid
-  // moves rows key = tid/16 + (NT/16)*u, 16-byte column tid%16, so sixteen
-  // consecutive threads read one 256-byte key row.  Every load reads an
-  // in-bounds row (padding and past-the-end keys read tree row 0); validity
-  // is kept as bits and applied when the stage is written to LDS, so nothing
-  // consumes a load result before the compute of the current stage is done.
-  // The same batch fetches this lane's ancestor-mask word for the tile its
-  // wave handles next.
+  // Stage loader: direct global -> LDS loads (no staging registers).  For each
+  // tile of the stage and each of K, V, wave w writes rows 4w + 4*NW*u ..
+  // +3 (1 KB) per instruction; lane i lands at byte 16*i of that block, i.e.
+  // row 4w + 4*NW*u + i/16, 16-byte slot i%16.  The slot holds logical chunk
+  // (i%16) ^ swz(row): K uses swz = row%16 and V uses swz = 4*(row%4), which
+  // keeps the K b128 reads and the V transpose reads free of bank conflicts.
+  // Padding keys, past-the-end tree nodes and tiles beyond the split read tree
+  // row 0 (in bounds, finite); the mask turns their scores into -inf, so they
+  // contribute exactly zero.  Each thread issues the same number of loads per
+  // stage (kLoads), so stage it is complete when vmcnt <= kLoads * (stages
+  // issued after it).
   constexpr int kRowsPerPass = NT / 16;
   constexpr int kPasses = kKT / kRowsPerPass;   // per tile and per K/V
   static_assert(kPasses * kRowsPerPass == kKT, "tile rows must split evenly");
-  static_assert(KG * kPasses <= 32, "validity bits must fit one word");
+  constexpr int kLoads = kTilesPerStage * 2 * kPasses + TPW;
+  static_assert(kLoads <= 63, "vmcnt range");
   const int ld_key = tid >> 4;
-  const int ld_col = (tid & 15) * 8;
-  // DEPTH register slots: with two, the loads of stage it+2 are in flight
-  // while stage it is computed and stage it+1 waits in registers.
-  u32x4_t pre[DEPTH][KG][2][kPasses];
-  uint32_t pre_valid[DEPTH];
-  uint64_t mword_pre[DEPTH];
-  auto load_stage = [&](auto slot_c, int tile0) {
-    constexpr int slot = decltype(slot_c)::value;
-    uint32_t bits = 0;
+  const int ld_slot = tid & 15;
+  // Loop-invariant per-lane source pointers: this lane's row of K and V
+  // (chunk already swizzled) at tile 0 of the prefix and of the tree, and
+  // its mask row.  A plain prefix tile then costs one uniform 64-bit add per
+  // load; only the boundary tile and the tree tiles take the general path.
+  const size_t tile_stride = (size_t)kKT * kv_row;    // elements per 32 key rows
+  const uint16_t* pk[kPasses];
+  const uint16_t* pv[kPasses];
 #pragma unroll
-    for (int tk = 0; tk < KG; ++tk) {
-      const int tile = tile0 + tk;
+  for (int u = 0; u < kPasses; ++u) {
+    const int row = ld_key + kRowsPerPass * u;
+    pk[u] = kp + (size_t)row * kv_row + ((ld_slot ^ (row & 15)) << 3);
+    pv[u] = vp + (size_t)row * kv_row + ((ld_slot ^ ((row & 3) << 2)) << 3);
+  }
+  const int L_full = L / kKT;                         // tiles entirely inside the prefix
+  const uint32_t* mrow_dw = reinterpret_cast<const uint32_t*>(
+      P.mask + (size_t)(sq.n0 + (row_ok ? node : 0)) * P.W);
+  auto issue_stage = [&](int it) {
+    unsigned char* st = lds + (it % kNumStages) * kStage;
+#pragma unroll
+    for (int tk = 0; tk < kTilesPerStage; ++tk) {
+      const int tile = t_lo + it * kTilesPerStage + tk;
 #pragma unroll
       for (int u = 0; u < kPasses; ++u) {
-        const int key = ld_key + kRowsPerPass * u;
-        const int kk = tile * kKT + key;
-        const int tn = kk - Lt * kKT;
-        const bool in_prefix = kk < L;
-        const bool in_tree = tile >= Lt && tn < sq.nn;
-        const bool valid = tile < t_hi && (in_prefix || in_tree);
-        bits |= (valid ? 1u : 0u) << (tk * kPasses + u);
-        const size_t off = (size_t)(in_prefix ? kk : (in_tree ? tn : 0)) * kv_row + ld_col;
-#pragma unroll
-        for (int kv = 0; kv < 2; ++kv) {
-          const uint16_t* src = in_prefix ? (kv ? vp : kp) + off : (kv ? vt : kt) + off;
-          pre[slot][tk][kv][u] = *reinterpret_cast<const u32x4_t*>(src);
+        const uint16_t* gk;
+        const uint16_t* gv;
+        if (tile < L_full) {
+          gk = pk[u] + (size_t)tile * tile_stride;
+          gv = pv[u] + (size_t)tile * tile_stride;
+        } else {
+          const int row = ld_key + kRowsPerPass * u;
+          const int kk = tile * kKT + row;
+          const int tn = kk - Lt * kKT;
+          const bool in_prefix = kk < L;
+          const bool in_tree = tile >= Lt && tn < sq.nn;
+          const size_t off = (size_t)(in_prefix ? kk : (in_tree ? tn : 0)) * kv_row;
+          gk = (in_prefix ? kp : kt) + off + ((ld_slot ^ (row & 15)) << 3);
+          gv = (in_prefix ? vp : vt) + off + ((ld_slot ^ ((row & 3) << 2)) << 3);
         }
+        const uint32_t dk = lds_addr(st + tk * kTileBytes + (4 * wave + kRowsPerPass * u) * kRow);
+        dma_b128(gk, dk);
+        dma_b128(gv, dk + kTileKV);
       }
     }
-    pre_valid[slot] = bits;
-    const int my_tile = tile0 + kg;
-    const int t0 = (my_tile - Lt) * kKT;
-    uint64_t w = 0;
-    if (row_ok && my_tile >= Lt && my_tile < t_hi) w = mrow[t0 >> 6];
-    mword_pre[slot] = w;
-  };
-  auto store_stage = [&](auto slot_c, unsigned char* stage) {
-    constexpr int slot = decltype(slot_c)::value;
+    // The 32-bit half of this lane's mask word that covers each of its
+    // wave's tiles (any in-bounds word for prefix tiles and idle rows).
 #pragma unroll
-    for (int tk = 0; tk < KG; ++tk)
-#pragma unroll
-      for (int u = 0; u < kPasses; ++u) {
-        const int key = ld_key + kRowsPerPass * u;
-        const bool valid = (pre_valid[slot] >> (tk * kPasses + u)) & 1u;
-        const u32x4_t z = {0u, 0u, 0u, 0u};
-        unsigned char* kdst = stage + tk * kTileBytes + key * kKStride + ld_col * 2;
-        unsigned char* vdst = stage + tk * kTileBytes + kKBytes + key * kVStride + ld_col * 2;
-        *reinterpret_cast<u32x4_t*>(kdst) = valid ? pre[slot][tk][0][u] : z;
-        *reinterpret_cast<u32x4_t*>(vdst) = valid ? pre[slot][tk][1][u] : z;
-      }
+    for (int j = 0; j < TPW; ++j) {
+      const int my_tile = t_lo + (it * KG + kg) * TPW + j;
+      const int dw = (my_tile >= Lt && my_tile < t_hi) ? my_tile - Lt : 0;
+      dma_b32(mrow_dw + dw, lds_addr(st + kMaskOff + (wave * TPW + j) * 256));
+    }
   };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, DEPTH - 1>;
+  // Stage it is in LDS for every wave once each has retired its own loads up
+  // to stage it and all have passed the barrier.  The barrier carries no
+  // memory fence (a fence would wait for the stages still in flight); the
+  // empty asm statements keep the compiler from moving LDS accesses across.
+  auto wait_stage = [&](int it, int n_iter) {
+    if (it + 1 < n_iter)
+      __builtin_amdgcn_s_waitcnt((kLoads & 15) | ((kLoads >> 4) << 14) | (7 << 4) | (15 << 8));
+    else
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
 
   f32x16_t oacc[4];
 #pragma unroll
@@ -279,145 +330,145 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
   float l_run = 0.f;
   const float c2 = P.scale_log2;
 
-  // Per-lane offsets of the transposed V reads: a 16-lane group reads a
-  // 4-key x 16-dim block; lane i of the group gets dim (base + i).
-  const int tr_key = (lane & 15) >> 2;
-  const int tr_col = 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  // Per-lane LDS offsets (swizzled rows, see the loader).  K: chunk 2i+hh of
+  // key row l32.  V transpose reads: a 16-lane group reads a 4-key x 16-dim
+  // block, lane i of the group gets dim (base + i) of keys key0 .. key0+3;
+  // with r = (lane%16)/4 the physical chunk of dim block e is 4*(e^r) + clo.
+  uint32_t koff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) koff[i] = l32 * kRow + (((2 * i + hh) ^ (l32 & 15)) << 4);
+  uint32_t voff[4];
+  {
+    const int r = (lane & 15) >> 2;
+    const int clo = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      voff[e] = (4 * hh + r) * kRow + (((4 * (e ^ r)) + clo) << 4) + 8 * (lane & 1);
+  }
 
-  const int n_iter = (t_hi - t_lo + KG - 1) / KG;
+  const int n_iter = (t_hi - t_lo + kTilesPerStage - 1) / kTilesPerStage;
 
-  // One stage of work for this wave: tile (t_lo + it*KG + kg) from LDS.
-  auto compute = [&](const unsigned char* cur, int it, uint64_t mw) {
-    const int tile = t_lo + it * KG + kg;
-    const uint64_t mword = mw;
-    if (group_active && tile < t_hi) {
-      const unsigned char* kb = cur + kg * kTileBytes;
-      const unsigned char* vb = kb + kKBytes;
-      // S^T = K Q^T for this tile's 32 keys x this wave's 32 rows.
-      f32x16_t sacc;
+  // S^T = K Q^T for one tile's 32 keys x this wave's 32 rows.  Accumulator v
+  // of this lane holds key 8*(v/4) + 4*hh + v%4 of the tile.
+  auto qk = [&](const unsigned char* kb) {
+    f32x16_t sacc;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
-      const unsigned char* krow = kb + l32 * kKStride + 16 * hh;
+    for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(krow + 32 * i);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv), qf[i],
-                                                       sacc, 0, 0, 0);
-      }
-      // Accumulator v of this lane holds key 8*(v/4) + 4*hh + v%4 of the tile.
-      if (tile >= Lt) {
-        const int t0 = (tile - Lt) * kKT;
-        const uint32_t bits = (uint32_t)(mword >> (t0 & 63));
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (!((bits >> key) & 1u)) sacc[v] = kNegInf;
-        }
-      } else if ((tile + 1) * kKT > L) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (tile * kKT + key >= L) sacc[v] = kNegInf;
-        }
-      }
-      float mt = sacc[0];
-#pragma unroll
-      for (int v = 1; v < 16; ++v) mt = fmaxf(mt, sacc[v]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      // Lazy running max: the reference moves only when the tile's max
-      // exceeds it by more than kLazyLog2 (log2 units), so after the first
-      // tiles the output is almost never rescaled; probabilities stay below
-      // 2^kLazyLog2 and numerator and denominator share the reference, so
-      // the result is unchanged.  Lanes l and l^32 hold the same row and take
-      // the same decision.
-      const bool move = (mt - m_run) * c2 > kLazyLog2;   // also true when m_run = -inf
-      const float m_old = m_run;
-      if (move) m_run = mt;
-      const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-      const float alpha = move ? fast_exp2((m_old - m_use) * c2) : 1.f;
-      const float mc = m_use * c2;
-      float ps = 0.f;
-      f32x16_t p;
+    for (int i = 0; i < 8; ++i) {
+      const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(kb + koff[i]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv), qf[i],
+                                                     sacc, 0, 0, 0);
+    }
+    return sacc;
+  };
+
+  // Mask, online softmax and O^T += V^T P^T for one tile whose scores are in
+  // sacc and whose V rows start at vb.
+  auto softmax_pv = [&](f32x16_t sacc, const unsigned char* vb, int tile, uint32_t mbits) {
+    if (tile >= Lt) {
+      const uint32_t bits = row_ok ? mbits : 0u;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        p[v] = fast_exp2(fmaf(sacc[v], c2, -mc));
-        ps += p[v];
+        const int key = 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (!((bits >> key) & 1u)) sacc[v] = kNegInf;
       }
-      l_run = fmaf(l_run, alpha, ps);
-      if (__ballot(move)) {
+    } else if ((tile + 1) * kKT > L) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) oacc[e][v] *= alpha;
+      for (int v = 0; v < 16; ++v) {
+        const int key = 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (tile * kKT + key >= L) sacc[v] = kNegInf;
       }
-
-      // O^T += V^T P^T: two 16-key steps x four 32-dim blocks.
+    }
+    float mt = sacc[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mt = fmaxf(mt, sacc[v]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    // Lazy running max: the reference moves only when the tile's max exceeds
+    // it by more than kLazyLog2 (log2 units), so after the first tiles the
+    // output is almost never rescaled; probabilities stay below 2^kLazyLog2
+    // and numerator and denominator share the reference, so the result is
+    // unchanged.  Lanes l and l^32 hold the same row and take the same
+    // decision.
+    const bool move = (mt - m_run) * c2 > kLazyLog2;   // also true when m_run = -inf
+    const float m_old = m_run;
+    if (move) m_run = mt;
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    const float alpha = move ? fast_exp2((m_old - m_use) * c2) : 1.f;
+    const float mc = m_use * c2;
+    float ps = 0.f;
+    f32x16_t p;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      p[v] = fast_exp2(fmaf(sacc[v], c2, -mc));
+      ps += p[v];
+    }
+    l_run = fmaf(l_run, alpha, ps);
+    if (__ballot(move)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[e][v] *= alpha;
+    }
+    // Two 16-key steps x four 32-dim blocks; one address add per dim block,
+    // the key offsets are immediates.
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      f32x8_t pf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pf[j] = p[8 * cc + j];
+      pb[cc] = __builtin_convertvector(pf, bf16x8_t);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned char* ve = vb + voff[e];
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        f32x8_t pf;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pf[j] = p[8 * cc + j];
-        const bf16x8_t pb = __builtin_convertvector(pf, bf16x8_t);
         // slots 0-3: keys 16cc+4hh+0..3, slots 4-7: keys 16cc+8+4hh+0..3
-        const unsigned char* v0 = vb + (16 * cc + 4 * hh + tr_key) * kVStride + tr_col;
-        const unsigned char* v1 = v0 + 8 * kVStride;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const i16x4_t lo = lds_read_tr16(v0 + 64 * e);
-          const i16x4_t hi = lds_read_tr16(v1 + 64 * e);
-          const i16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb,
-                                                            oacc[e], 0, 0, 0);
-        }
+        const i16x4_t lo = lds_read_tr16(ve + 16 * cc * kRow);
+        const i16x4_t hi = lds_read_tr16(ve + (16 * cc + 8) * kRow);
+        const i16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb[cc],
+                                                          oacc[e], 0, 0, 0);
       }
     }
   };
 
-  unsigned char* buf0 = lds;
-  unsigned char* buf1 = lds + kStage;
-  if (DEPTH == 1) {
-    load_stage(S0{}, t_lo);
-    store_stage(S0{}, buf0);
-    uint64_t mw = mword_pre[0];
-    __syncthreads();
-    for (int it = 0; it < n_iter; ++it) {
-      unsigned char* cur = (it & 1) ? buf1 : buf0;
-      unsigned char* nxt = (it & 1) ? buf0 : buf1;
-      const bool more = it + 1 < n_iter;
-      if (more) load_stage(S0{}, t_lo + (it + 1) * KG);
-      compute(cur, it, mw);
-      if (more) {
-        store_stage(S0{}, nxt);
-        mw = mword_pre[0];
-      }
-      __syncthreads();
+  // Pipeline: stage it is computed while stages it+1 and it+2 are in flight;
+  // the LDS ring reuses slot (it+2) % kNumStages, which every wave finished
+  // reading before the barrier of stage it.  Each wave takes TPW consecutive
+  // tiles per stage: all their scores first, then softmax + PV of each, in
+  // one basic block, so the scheduler can fill the MFMA chains of one tile
+  // with the VALU work of the other.
+  issue_stage(0);
+  if (n_iter > 1) issue_stage(1);
+  int slot = 0;   // it % kNumStages, kept in a scalar register
+  for (int it = 0; it < n_iter; ++it) {
+    wait_stage(it, n_iter);
+    if (it + 2 < n_iter) issue_stage(it + 2);
+    // Stage base as one uniform value, so each LDS read needs one add.
+    const unsigned char* st = lds + __builtin_amdgcn_readfirstlane(slot * kStage);
+    slot = (slot + 1 == kNumStages) ? 0 : slot + 1;
+    f32x16_t sc[TPW];
+    int tl[TPW];
+    bool ac[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      tl[j] = t_lo + (it * KG + kg) * TPW + j;
+      ac[j] = group_active && tl[j] < t_hi;
+      if (ac[j]) sc[j] = qk(st + (kg * TPW + j) * kTileBytes);
     }
-  } else {
-    // Two slots, loop unrolled by two so each slot is named statically:
-    // even iterations compute buf0 while slot 1 waits and slot 0 refills.
-    load_stage(S0{}, t_lo);
-    if (n_iter > 1) load_stage(S1{}, t_lo + KG);
-    store_stage(S0{}, buf0);
-    uint64_t mw = mword_pre[0];
-    __syncthreads();
-    for (int it = 0; it < n_iter; it += 2) {
-      if (it + 2 < n_iter) load_stage(S0{}, t_lo + (it + 2) * KG);
-      compute(buf0, it, mw);
-      if (it + 1 < n_iter) {
-        store_stage(S1{}, buf1);
-        mw = mword_pre[DEPTH - 1];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      if (ac[j]) {
+        const uint32_t mbits =
+            *reinterpret_cast<const uint32_t*>(st + kMaskOff + (wave * TPW + j) * 256 + lane * 4);
+        softmax_pv(sc[j], st + (kg * TPW + j) * kTileBytes + kTileKV, tl[j], mbits);
       }
-      __syncthreads();
-      if (it + 1 >= n_iter) break;
-      if (it + 3 < n_iter) load_stage(S1{}, t_lo + (it + 3) * KG);
-      compute(buf1, it + 1, mw);
-      if (it + 2 < n_iter) {
-        store_stage(S0{}, buf0);
-        mw = mword_pre[0];
-      }
-      __syncthreads();
     }
   }
+  __syncthreads();
 
   if (KG > 1) {
     // Merge the key groups through LDS (the stage buffers are free now):
@@ -561,17 +612,16 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
     P.lse[(size_t)(sq.n0 + node) * P.Hq + head] = lsum > 0.f ? M * P.scale + logf(lsum) : kNegInf;
 }
 
-template <int RG, int KG, int DEPTH>
+template <int RG, int KG, int TPW>
 hipError_t launch_shape(const KParams& kp, long long grid, long long merge_grid, hipStream_t stream) {
-  const size_t lds = 2 * (size_t)KG * kTileBytes;
+  const size_t lds = (size_t)kNumStages * (KG * TPW * kTileBytes + RG * KG * TPW * 256);
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&fwd_bf16_kernel<RG, KG, DEPTH>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_bf16_kernel<RG, KG, TPW>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((fwd_bf16_kernel<RG, KG, DEPTH>), dim3((unsigned)grid), dim3(RG * KG * 64),
-                     lds, stream, kp);
+  hipLaunchKernelGGL((fwd_bf16_kernel<RG, KG, TPW>), dim3((unsigned)grid), dim3(RG * KG * 64), lds,
+                     stream, kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || merge_grid == 0) return e;
   hipLaunchKernelGGL((merge_bf16_kernel<RG>), dim3((unsigned)merge_grid), dim3(256), 0, stream, kp);
@@ -657,7 +707,7 @@ hipError_t launch_forward_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t s
   switch (p.rg * 16 + p.kg) {
     case 1 * 16 + 2: return launch_shape<1, 2, 1>(kp, grid, merge_grid, stream);
     case 2 * 16 + 2: return launch_shape<2, 2, 1>(kp, grid, merge_grid, stream);
-    case 4 * 16 + 2: return launch_shape<4, 2, 2>(kp, grid, merge_grid, stream);
+    case 4 * 16 + 2: return launch_shape<4, 2, 1>(kp, grid, merge_grid, stream);
     case 8 * 16 + 1: return launch_shape<8, 1, 2>(kp, grid, merge_grid, stream);
     default: return hipErrorInvalidValue;
   }
