@@ -45,6 +45,10 @@ def parse():
     p.add_argument("--sets", type=int, default=32)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--calib-copy", action="store_true",
+                   help="only run a plain 256 MiB device-to-device copy (counter calibration)")
+    p.add_argument("--summarize-profiles", metavar="DIR",
+                   help="write profiles/ summaries from rocprofv3 CSV output under DIR")
     return p.parse_args()
 
 
@@ -70,8 +74,128 @@ def load_traffic(kernel_key, current_hash):
     return rec.get("hbm_bytes_per_launch")
 
 
+CALIB_BYTES = 256 * 2**20
+
+
+def calib_copy():
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings scale
+    the counters of the library's kernels to bytes."""
+    import torch
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": CALIB_BYTES}))
+
+
+def _read_csvs(root, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(root, "**", "*" + suffix), recursive=True)):
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _pmc_means(root, counter):
+    """Mean counter value per kernel name over all dispatches (KiB for
+    FETCH_SIZE / WRITE_SIZE)."""
+    acc = {}
+    for r in _read_csvs(root, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize_profiles(root):
+    """Turn rocprofv3 CSV output (runs made by the commands in PROFILE_CMDS,
+    written under root/<name>) into profiles/*.md and profiles/pmc_traffic.json."""
+    os.makedirs(PROFILES, exist_ok=True)
+    # kernel trace summary
+    stats = _read_csvs(os.path.join(root, "prof_trace"), "kernel_stats.csv")
+    lines = ["# Kernel trace: one verification step, Llama-3-8B-shaped layer (N=64, L=4096)", "",
+             "Command (run from the repository root on the MI355X box):", "",
+             "    " + PROFILE_CMDS["prof_trace"], "",
+             "| kernel | calls | avg us | min us | max us | % |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r["Name"]
+        short = name.replace("ta::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.3f} | "
+                     f"{float(r['MinNs'])/1e3:.3f} | {float(r['MaxNs'])/1e3:.3f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    with open(os.path.join(PROFILES, "tree_attn_step_llama3_8b_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    # HBM traffic from FETCH_SIZE / WRITE_SIZE, scaled by the copy calibration
+    fetch = _pmc_means(os.path.join(root, "prof_fetch"), "FETCH_SIZE")
+    write = _pmc_means(os.path.join(root, "prof_write"), "WRITE_SIZE")
+    cf = _pmc_means(os.path.join(root, "prof_calib_fetch"), "FETCH_SIZE")
+    cw = _pmc_means(os.path.join(root, "prof_calib_write"), "WRITE_SIZE")
+    copy_f = max((v for k, v in cf.items() if "copy" in k.lower() or "elementwise" in k.lower()),
+                 default=None)
+    copy_w = max((v for k, v in cw.items() if "copy" in k.lower() or "elementwise" in k.lower()),
+                 default=None)
+    sf = (CALIB_BYTES / 1024) / copy_f if copy_f else 1.0
+    sw = (CALIB_BYTES / 1024) / copy_w if copy_w else 1.0
+    groups = {"tree_attn_forward": ("fwd_bf16_kernel", "merge_bf16_kernel"),
+              "tree_verify_greedy": ("argmax_partial_kernel", "path_select_kernel"),
+              "tree_attn_build_mask": ("build_mask_kernel",)}
+    hashes = {"tree_attn_forward": src_hash("attn_fwd.hip"),
+              "tree_verify_greedy": src_hash("verify.hip"),
+              "tree_attn_build_mask": src_hash("mask_build.hip")}
+    rec = {"calibration": {"copy_bytes": CALIB_BYTES, "fetch_kib": copy_f, "write_kib": copy_w,
+                           "fetch_scale": sf, "write_scale": sw}}
+    md = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+          "Workload: one verification step of the Llama-3-8B-shaped layer (N=64, L=4096, bf16).",
+          "Counters are KiB per dispatch; each is scaled by what the same counter reads for a",
+          f"plain {CALIB_BYTES >> 20} MiB device copy (fetch x{sf:.3f}, write x{sw:.3f}).", "",
+          "Commands (repository root, MI355X box):", ""]
+    md += ["    " + PROFILE_CMDS[k] for k in ("prof_fetch", "prof_write", "prof_calib_fetch",
+                                             "prof_calib_write")]
+    md += ["", "| call | kernel | fetch KiB | write KiB | HBM bytes (scaled) |", "|---|---|---|---|---|"]
+    for call, kernels in groups.items():
+        total = 0.0
+        for kn in kernels:
+            fk = next((v for k, v in fetch.items() if kn in k), None)
+            wk = next((v for k, v in write.items() if kn in k), None)
+            if fk is None or wk is None:
+                continue
+            b = fk * 1024 * sf + wk * 1024 * sw
+            total += b
+            md.append(f"| {call} | `{kn}` | {fk:.1f} | {wk:.1f} | {b / 1e6:.3f} MB |")
+        rec[call] = {"source_hash": hashes[call], "hbm_bytes_per_launch": round(total)}
+    with open(os.path.join(PROFILES, "tree_attn_step_llama3_8b_hbm_traffic.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    with open(os.path.join(PROFILES, "pmc_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+PROFILE_CMDS = {
+    "prof_trace": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o run -- "
+                  "python -u bench.py --steps 50 --warmup 5 --no-cpu-baseline",
+    "prof_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch -o run -- "
+                  "python -u bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+    "prof_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_write -o run -- "
+                  "python -u bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+    "prof_calib_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_calib_fetch -o run -- "
+                        "python -u bench.py --calib-copy",
+    "prof_calib_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_calib_write -o run -- "
+                        "python -u bench.py --calib-copy",
+}
+
+
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
+    if args.calib_copy:
+        calib_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path: sequences, KV heads or prefix chunks would shard across GPUs "

@@ -62,9 +62,14 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const void* __
   const int c = blockIdx.x % cpr;
   const int lo = c * chunk;
   const int hi = min(V, lo + chunk);
+  // In-thread scans visit increasing indices, so a strict '>' keeps the
+  // lowest index of equal values; starting from this thread's first index
+  // with -inf keeps it for a range of -inf as well.
   float bv = kNegInf;
   int bi = 0x7fffffff;
   if (VEC > 1) {
+    const int first = lo + threadIdx.x * VEC;
+    if (first < hi) bi = first;
     for (int base = lo; base < hi; base += kThreads * VEC * kUnroll) {
       u32x4_t u[kUnroll];
 #pragma unroll
@@ -78,36 +83,35 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const void* __
             u[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
                 static_cast<const float*>(logits) + row * V + e));
         } else {
-          u[k] = u32x4_t{0u, 0u, 0u, 0u};   // never compared: e >= hi
+          u[k] = u32x4_t{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};   // -inf, never taken
         }
       }
 #pragma unroll
       for (int k = 0; k < kUnroll; ++k) {
         const int e = base + (k * kThreads + threadIdx.x) * VEC;
-        if (e >= hi) continue;
-        const uint32_t w[4] = {u[k][0], u[k][1], u[k][2], u[k][3]};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if (BF16) {
-            const float a = __uint_as_float(w[j] << 16);
-            const float b = __uint_as_float(w[j] & 0xffff0000u);
-            if (better(a, e + 2 * j, bv, bi)) { bv = a; bi = e + 2 * j; }
-            if (better(b, e + 2 * j + 1, bv, bi)) { bv = b; bi = e + 2 * j + 1; }
+            const float a = __uint_as_float(u[k][j] << 16);
+            const float b = __uint_as_float(u[k][j] & 0xffff0000u);
+            if (a > bv) { bv = a; bi = e + 2 * j; }
+            if (b > bv) { bv = b; bi = e + 2 * j + 1; }
           } else {
-            const float a = __uint_as_float(w[j]);
-            if (better(a, e + j, bv, bi)) { bv = a; bi = e + j; }
+            const float a = __uint_as_float(u[k][j]);
+            if (a > bv) { bv = a; bi = e + j; }
           }
         }
       }
     }
   } else {
+    if (lo + (int)threadIdx.x < hi) bi = lo + threadIdx.x;
     for (int e = lo + threadIdx.x; e < hi; e += kThreads) {
       float a;
       if (BF16)
         a = __uint_as_float((uint32_t)static_cast<const uint16_t*>(logits)[row * V + e] << 16);
       else
         a = static_cast<const float*>(logits)[row * V + e];
-      if (better(a, e, bv, bi)) { bv = a; bi = e; }
+      if (a > bv) { bv = a; bi = e; }
     }
   }
   // Ties (including -0 == +0 and rows of -inf) resolve to the lower index at
