@@ -18,10 +18,11 @@
 // Workgroup = RG row groups x KG key groups of one wave each.  A wave owns 32
 // query rows; the KG waves that share those rows take alternate tiles of the
 // workgroup's key range, and are merged through LDS at the end.  Grid items
-// are (sequence, KV head, key split, row tile); splits cut the tile range in
-// balanced pieces (the tree tiles ride with the last prefix tiles).  Items
-// that share a KV chunk have consecutive ids and land on one XCD, so the
-// second row tile reads the chunk from that XCD's L2.
+// are (sequence, key split, KV head, row tile), row tile fastest; splits cut
+// the tile range in balanced pieces (the tree tiles ride with the last prefix
+// tiles).  Each XCD runs a contiguous run of item ids: the row tiles that
+// share a KV chunk read it once from HBM and once from that XCD's L2, and the
+// XCD streams whole key rows (all KV heads) of one key range.
 //
 // Per 32-key tile and wave:
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T
@@ -35,8 +36,9 @@
 //     registers (rounded to bf16), A = V^T is read from the row-major V tile
 //     with ds_read_b64_tr_b16, whose 16-lane 4x16 transpose hands each lane
 //     four consecutive keys of one head dimension.
-// K and V tiles are staged through LDS with 16-byte coalesced loads, double
-// buffered, one barrier per stage.  Items with one split write bf16 output
+// K and V tiles (and, ahead of the first stage, the query rows) are staged
+// through LDS with direct 16-byte global->LDS loads in a three-stage ring, one
+// barrier per stage.  Items with one split write bf16 output
 // (and lse) directly; otherwise each leaves (unnormalised O, max, sum) in the
 // workspace (normalised O in bf16, max and sum in fp32), in the MFMA register
 // layout so every store is coalesced, and a merge kernel combines the splits
@@ -67,6 +69,7 @@ constexpr int kRow = kD * 2;                  // LDS bytes per K or V row (unpad
 constexpr int kTileKV = kKT * kRow;           // 8192: one K or one V tile
 constexpr int kTileBytes = 2 * kTileKV;       // K tile then V tile
 constexpr int kNumStages = 3;                 // LDS ring: stage it in use, it+1 and it+2 in flight
+constexpr int kLdsMax = 160 * 1024;           // LDS per workgroup on gfx950
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazyLog2 = 8.f;              // running-max slack: probabilities stay <= 256
@@ -160,15 +163,31 @@ __device__ inline i16x4_t lds_read_tr16(const unsigned char* p) {
       (__attribute__((address_space(3))) i16x4_t*)(p));
 }
 
+// LDS map of one workgroup: a ring of kNumStages stages, each KG*TPW x
+// (K tile, V tile) followed by TPW mask dwords per lane per wave, and the
+// workgroup's query rows (32*RG rows, laid out like a K tile).  The query
+// block sits after the ring when both fit, otherwise over ring slot 2, which
+// is first written only after every wave has copied its rows to registers.
+template <int RG, int KG, int TPW>
+struct LdsMap {
+  static constexpr int kMaskOff = KG * TPW * kTileBytes;
+  static constexpr int kStage = kMaskOff + RG * KG * TPW * 256;
+  static constexpr int kRing = kNumStages * kStage;
+  static constexpr int kQBytes = RG * 32 * kRow;
+  static constexpr bool kQAlias = kRing + kQBytes > kLdsMax;
+  static constexpr int kQOff = kQAlias ? 2 * kStage : kRing;
+  static constexpr int kBytes = kQOff + kQBytes > kRing ? kQOff + kQBytes : kRing;
+  static_assert(kBytes <= kLdsMax, "LDS budget");
+};
+
 template <int RG, int KG, int TPW>
 __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
   constexpr int NW = RG * KG;
   constexpr int NT = NW * 64;
   constexpr int kTilesPerStage = KG * TPW;
-  // Stage layout: KG*TPW x (K tile, V tile), then TPW mask dwords per lane
-  // per wave.
-  constexpr int kMaskOff = kTilesPerStage * kTileBytes;
-  constexpr int kStage = kMaskOff + NW * TPW * 256;
+  using Map = LdsMap<RG, KG, TPW>;
+  constexpr int kMaskOff = Map::kMaskOff;
+  constexpr int kStage = Map::kStage;
   extern __shared__ __align__(16) unsigned char lds[];
 
   const int tid = threadIdx.x;
@@ -189,10 +208,10 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
   if (item >= P.n_items) return;
   const int r = (int)(item % P.R);
   long long t = item / P.R;
-  const int s = (int)(t % P.S);
-  t /= P.S;
   const int g = (int)(t % P.Hkv);
-  const int b = (int)(t / P.Hkv);
+  t /= P.Hkv;
+  const int s = (int)(t % P.S);
+  const int b = (int)(t / P.S);
 
   Seq sq;
   if (!decode_seq(P, b, sq)) return;
@@ -213,29 +232,30 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
   const int head = g * P.G + (row_ok ? my_row % P.G : 0);
 
   bf16x8_t qf[8];
-  {
-    // Rows past the tile's end read row 0 of the tile (in bounds) and are
-    // zeroed; their outputs are never written.
-    const uint16_t* qrow = P.q + ((size_t)(sq.n0 + node) * P.Hq + head) * kD + 8 * hh;
-    u32x4_t qv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qv[i] = *reinterpret_cast<const u32x4_t*>(qrow + 16 * i);
-    // Retire the query loads here, before any pipeline load is issued, so
-    // the compiler never needs a later catch-all wait for them.
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (!row_ok) qv[i] = u32x4_t{0u, 0u, 0u, 0u};
-      qf[i] = __builtin_bit_cast(bf16x8_t, qv[i]);
-    }
-  }
-  const uint64_t* mrow = P.mask + (size_t)(sq.n0 + node) * P.W;
 
   const size_t kv_row = (size_t)P.Hkv * kD;   // elements between consecutive key rows
   const uint16_t* kp = P.k_prefix + ((size_t)sq.p0 * P.Hkv + g) * kD;
   const uint16_t* vp = P.v_prefix + ((size_t)sq.p0 * P.Hkv + g) * kD;
   const uint16_t* kt = P.k_tree + ((size_t)sq.n0 * P.Hkv + g) * kD;
   const uint16_t* vt = P.v_tree + ((size_t)sq.n0 * P.Hkv + g) * kD;
+
+  // Query rows go to LDS with the same direct loads, ahead of stage 0, so
+  // they arrive in the same round trip as the first K/V tiles.  Block u of
+  // wave w is rows 4(w + NW*u) .. +3 of the workgroup, swizzled like a K
+  // tile; rows past the tile's end read the tile's first row (in bounds,
+  // finite) and their outputs are never written.
+  static_assert((RG * 8) % NW == 0, "query blocks must split evenly over the waves");
+  auto issue_q = [&]() {
+#pragma unroll
+    for (int u = 0; u < RG * 8 / NW; ++u) {
+      const int blk = wave + NW * u;
+      const int qr = 4 * blk + (lane >> 4);
+      const int mr = row0 + qr < row0 + rgn.rows_here ? row0 + qr : row0;
+      const uint16_t* src = P.q + ((size_t)(sq.n0 + mr / P.G) * P.Hq + g * P.G + mr % P.G) * kD +
+                            (((lane & 15) ^ (qr & 15)) << 3);
+      dma_b128(src, lds_addr(lds + Map::kQOff + blk * 1024));
+    }
+  };
 
   // Stage loader: direct global -> LDS loads (no staging registers).  For each
   // tile of the stage and each of K, V, wave w writes rows 4w + 4*NW*u ..
@@ -441,11 +461,27 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
   // tiles per stage: all their scores first, then softmax + PV of each, in
   // one basic block, so the scheduler can fill the MFMA chains of one tile
   // with the VALU work of the other.
+  // The query loads precede stage 0, so the first stage wait retires them.
+  issue_q();
   issue_stage(0);
   if (n_iter > 1) issue_stage(1);
   int slot = 0;   // it % kNumStages, kept in a scalar register
   for (int it = 0; it < n_iter; ++it) {
     wait_stage(it, n_iter);
+    if (it == 0) {
+      const unsigned char* qb = lds + Map::kQOff + rg * 32 * kRow;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        qf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qb + koff[i]));
+      if (Map::kQAlias) {
+        // Ring slot 2 holds the query block: every wave has its rows in
+        // registers before stage 2 is issued over it.
+        __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4));   // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+    }
     if (it + 2 < n_iter) issue_stage(it + 2);
     // Stage base as one uniform value, so each LDS read needs one add.
     const unsigned char* st = lds + __builtin_amdgcn_readfirstlane(slot * kStage);
@@ -556,50 +592,58 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
   t /= P.R;
   const int g = (int)(t % P.Hkv);
   const int b = (int)(t / P.Hkv);
-  Seq sq;
-  if (!decode_seq(P, b, sq)) return;
-  Range rgn;
-  if (!row_tile_range(P, sq, r, rgn)) return;
-  if (rgn.Sb <= 1 || rg * 32 >= rgn.rows_here) return;
   const int lane = threadIdx.x & 63;
   const int j = threadIdx.x >> 6;
   const int hh = lane >> 5;
   const int rl = rg * 32 + (lane & 31);
-  if (rl >= rgn.rows_here) return;
+  const long long item0 = ((long long)b * P.S * P.Hkv + g) * P.R + r;   // split s adds s*Hkv*R
+  const long long split_stride = (long long)P.Hkv * P.R;
+
+  // The partial slots do not depend on the offsets: issue the loads of the
+  // first kMaxS splits before decoding the sequence, so both round trips
+  // overlap.  Slots past this row tile's split count are never written by
+  // this call and are ignored below.
+  constexpr int kMaxS = 16;
+  float2 ml[kMaxS];
+  u32x2_t h[kMaxS];
+#pragma unroll
+  for (int k = 0; k < kMaxS; ++k) {
+    if (k < P.S) {
+      const long long it = item0 + k * split_stride;
+      ml[k] = P.ws_ml[(size_t)it * P.rows_wg + rl];
+      h[k] = P.ws_o[(((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane];
+    }
+  }
+
+  Seq sq;
+  if (!decode_seq(P, b, sq)) return;
+  Range rgn;
+  if (!row_tile_range(P, sq, r, rgn)) return;
+  if (rgn.Sb <= 1 || rl >= rgn.rows_here) return;
   const float c2 = P.scale_log2;
-  const long long item0 = ((long long)(b * P.Hkv + g) * P.S) * P.R + r;   // split s adds s*R
   const int Sb = rgn.Sb;
 
-  // Online merge, eight splits' loads in flight per batch.
-  constexpr int kBatch = 8;
   float M = kNegInf;
   float lsum = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < Sb; s0 += kBatch) {
-    float2 ml[kBatch];
-    f32x4_t o[kBatch];
+  auto add = [&](float2 m_l, u32x2_t hv) {
+    const f32x4_t o = {__uint_as_float(hv[0] << 16), __uint_as_float(hv[0] & 0xffff0000u),
+                       __uint_as_float(hv[1] << 16), __uint_as_float(hv[1] & 0xffff0000u)};
+    const float m_new = fmaxf(M, m_l.x);
+    const float mu = (m_new == kNegInf) ? 0.f : m_new;
+    const float a = fast_exp2((M - mu) * c2);
+    const float w = fast_exp2((m_l.x - mu) * c2) * m_l.y;
+    acc = acc * a + w * o;
+    lsum = lsum * a + w;
+    M = m_new;
+  };
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      ml[k] = make_float2(kNegInf, 0.f);
-      o[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if (s0 + k < Sb) {
-        const long long it = item0 + (long long)(s0 + k) * P.R;
-        ml[k] = P.ws_ml[(size_t)it * P.rows_wg + rl];
-        const u32x2_t h = P.ws_o[(((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane];
-        o[k] = f32x4_t{__uint_as_float(h[0] << 16), __uint_as_float(h[0] & 0xffff0000u),
-                       __uint_as_float(h[1] << 16), __uint_as_float(h[1] & 0xffff0000u)};
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const float m_new = fmaxf(M, ml[k].x);
-      const float mu = (m_new == kNegInf) ? 0.f : m_new;
-      const float a = fast_exp2((M - mu) * c2);
-      const float w = fast_exp2((ml[k].x - mu) * c2) * ml[k].y;
-      acc = acc * a + w * o[k];
-      lsum = lsum * a + w;
-      M = m_new;
-    }
+  for (int k = 0; k < kMaxS; ++k)
+    if (k < Sb) add(ml[k], h[k]);
+  for (int s = kMaxS; s < Sb; ++s) {
+    const long long it = item0 + s * split_stride;
+    add(P.ws_ml[(size_t)it * P.rows_wg + rl],
+        P.ws_o[(((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane]);
   }
   const int my_row = r * P.rows_wg + rl;
   const int node = my_row / P.G;
@@ -614,7 +658,7 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
 
 template <int RG, int KG, int TPW>
 hipError_t launch_shape(const KParams& kp, long long grid, long long merge_grid, hipStream_t stream) {
-  const size_t lds = (size_t)kNumStages * (KG * TPW * kTileBytes + RG * KG * TPW * 256);
+  const size_t lds = LdsMap<RG, KG, TPW>::kBytes;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_bf16_kernel<RG, KG, TPW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
