@@ -2,23 +2,35 @@
 //
 // Follows "Tree Attention" (inferensys.com glossary), Modified Causal
 // Attention Mask: a node sees itself and every node on its path back to the
-// root, never a sibling branch.  The premlal listing (build_tree_attention_mask)
-// builds the same relation as a dense N x N boolean matrix by walking parent
-// pointers; here it is packed to one bit per node (64 nodes per uint64 word)
-// and built level by level on the GPU:
+// root, never a sibling branch.  The premlal article builds the same relation
+// as a dense N x N boolean matrix by walking parent pointers; here it is
+// packed to one bit per node (64 nodes per uint64 word) and built on the GPU
+// by pointer jumping, one workgroup per sequence with the rows in LDS
+// (max_nodes * W * 8 bytes, 128 KiB at the 1024-node limit):
 //
-//   row(root) = bit(root);   row(i) = row(parent(i)) | bit(i)
+//   R(i) = {i},  J(i) = parent(i)                          (round 0)
+//   R(i) |= R(J(i)),  J(i) = J(J(i))   while some J(i) >= 0
 //
-// Nodes are topologically ordered (parent < child), so after round d every
-// node of depth <= d holds its final row.  One workgroup per sequence keeps
-// the rows in LDS (max_nodes * W * 8 bytes, 128 KiB at the 1024-node limit),
-// then writes them out coalesced.  Rounds = tree depth + 1.
+// After round k, R(i) holds every ancestor of i closer than 2^(k+1) and J(i)
+// is the ancestor exactly 2^(k+1) steps up (or -1), so a tree of depth d
+// needs ceil(log2(d + 1)) rounds.  R is updated in place: a row read while
+// its owner is extending it is still a subset of that node's ancestors, and
+// J is double buffered, so the covered distance never falls behind J.  The
+// depth of i is |R(i)| - 1.
 #include "internal.h"
 
 namespace ta {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kPerThread = TA_MAX_NODES / kThreads;
+
+__device__ inline uint64_t lds_load(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ inline void lds_store(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 
 __global__ __launch_bounds__(kThreads) void build_mask_kernel(
     const int32_t* __restrict__ parents, const int32_t* __restrict__ node_offsets,
@@ -27,6 +39,15 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
   extern __shared__ uint64_t smem[];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
+  // Sequence 0 starts at node 0 whenever its offsets are well formed, so its
+  // parent loads go out together with the offset loads.
+  const int spec_n = min(max_nodes, total_nodes);
+  int pv[kPerThread];
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int i = tid + k * kThreads;
+    pv[k] = (b == 0 && i < spec_n) ? parents[i] : -1;
+  }
   const int n0 = node_offsets[b];
   const int n1 = node_offsets[b + 1];
   const int n = n1 - n0;
@@ -34,18 +55,29 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
     if (tid == 0 && status) status[b] = 1;  // TA_ERR_INVALID_ARG
     return;
   }
-  uint64_t* rows = smem;                                          // [n][W]
-  int32_t* par = reinterpret_cast<int32_t*>(smem + (size_t)max_nodes * W);  // [n]
-  int32_t* dep = par + max_nodes;                                 // [n]
+  if (b != 0 || n0 != 0) {
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      const int i = tid + k * kThreads;
+      pv[k] = i < n ? parents[n0 + i] : -1;
+    }
+  }
+  uint64_t* rows = smem;                                                    // [n][W]
+  int32_t* jmp0 = reinterpret_cast<int32_t*>(smem + (size_t)max_nodes * W);  // [n]
+  int32_t* jmp1 = jmp0 + max_nodes;                                          // [n]
 
   int bad = 0;
-  for (int i = tid; i < n; i += kThreads) {
-    const int p = parents[n0 + i];
-    if (p < -1 || p >= i) bad = 1;
-    par[i] = p;
-    dep[i] = (p == -1) ? 0 : -1;
-    for (int w = 0; w < W; ++w)
-      rows[i * W + w] = (p == -1 && (i >> 6) == w) ? (1ull << (i & 63)) : 0ull;
+  int any = 0;
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < n) {
+      const int p = pv[k];
+      bad |= (p < -1 || p >= i);
+      any |= (p >= 0);
+      jmp0[i] = p;
+      for (int w = 0; w < W; ++w) rows[i * W + w] = (i >> 6) == w ? 1ull << (i & 63) : 0ull;
+    }
   }
   bad = __syncthreads_or(bad);
   if (bad) {
@@ -56,31 +88,39 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
     if (tid == 0 && status) status[b] = 2;  // TA_ERR_INVALID_TREE
     return;
   }
+  any = __syncthreads_or(any);
 
-  // Level rounds: a node whose parent reached depth d-1 in the previous round
-  // takes depth d and its row.  Rows written in round d are read only in
-  // later rounds, so one barrier per round suffices.
-  for (int d = 1; d <= n; ++d) {
-    int changed = 0;
-    for (int i = tid; i < n; i += kThreads) {
-      if (dep[i] >= 0) continue;
-      const int p = par[i];
-      if (dep[p] != d - 1) continue;
-      for (int w = 0; w < W; ++w) {
-        uint64_t v = rows[p * W + w];
-        if ((i >> 6) == w) v |= 1ull << (i & 63);
-        rows[i * W + w] = v;
+  int32_t* jcur = jmp0;
+  int32_t* jnext = jmp1;
+  while (any) {
+    for (int idx = tid; idx < n * W; idx += kThreads) {
+      const int i = idx / W;
+      const int j = jcur[i];
+      if (j >= 0) {
+        const int w = idx - i * W;
+        lds_store(&rows[idx], lds_load(&rows[idx]) | lds_load(&rows[j * W + w]));
       }
-      dep[i] = d;
-      changed = 1;
     }
-    if (!__syncthreads_or(changed)) break;
+    int more = 0;
+    for (int i = tid; i < n; i += kThreads) {
+      const int j = jcur[i];
+      const int jj = j >= 0 ? jcur[j] : -1;
+      jnext[i] = jj;
+      more |= (jj >= 0);
+    }
+    any = __syncthreads_or(more);
+    int32_t* t = jcur;
+    jcur = jnext;
+    jnext = t;
   }
 
-  for (int idx = tid; idx < n * W; idx += kThreads)
-    mask[(size_t)n0 * W + idx] = rows[idx];
+  for (int idx = tid; idx < n * W; idx += kThreads) mask[(size_t)n0 * W + idx] = rows[idx];
   if (depth)
-    for (int i = tid; i < n; i += kThreads) depth[n0 + i] = dep[i];
+    for (int i = tid; i < n; i += kThreads) {
+      int c = 0;
+      for (int w = 0; w < W; ++w) c += __popcll(rows[i * W + w]);
+      depth[n0 + i] = c - 1;
+    }
   if (tid == 0 && status) status[b] = 0;
 }
 

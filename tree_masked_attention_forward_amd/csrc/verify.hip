@@ -135,36 +135,70 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const void* __
   }
 }
 
+// Inputs of one sequence that path_select_kernel keeps in registers: slot k
+// of thread t holds item t + 256k of the chunk results, of the draft tokens
+// and of the mask words.  Items past kSpec slots are read where they are used.
+constexpr int kSpec = 4;
+
+struct SeqRegs {
+  float2 x[kSpec];
+  int32_t d[kSpec];
+  uint64_t m[kSpec];
+};
+
+__device__ inline void load_seq_regs(SeqRegs& r, const float2* ws, const int32_t* draft,
+                                     const uint64_t* mask, int cpr, int W, int base, int cnt) {
+#pragma unroll
+  for (int k = 0; k < kSpec; ++k) {
+    const int q = threadIdx.x + k * kThreads;
+    if (q < cnt * cpr) r.x[k] = ws[(size_t)base * cpr + q];
+    if (q < cnt) r.d[k] = draft[base + q];
+    if (q < cnt * W) r.m[k] = mask[(size_t)base * W + q];
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void path_select_kernel(
     const float2* __restrict__ ws, int cpr, const int32_t* __restrict__ draft,
     const uint64_t* __restrict__ mask, const int32_t* __restrict__ node_offsets,
     int total_nodes, int max_nodes, int W, int32_t* __restrict__ target_argmax,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
     int32_t* __restrict__ accept_tokens) {
+  extern __shared__ uint64_t rows[];   // [nn][W] mask rows of the sequence
+  __shared__ int32_t tgt[TA_MAX_NODES];
   __shared__ uint64_t match_w[(TA_MAX_NODES + 63) / 64];
   __shared__ unsigned long long red[kThreads / 64];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+
+  // Sequence 0 starts at node 0 whenever its offsets are well formed: its
+  // inputs are requested together with the offsets, so the whole kernel
+  // waits on one memory round trip.
+  SeqRegs r;
+  if (b == 0) load_seq_regs(r, ws, draft, mask, cpr, W, 0, min(max_nodes, total_nodes));
   const int n0 = node_offsets[b];
   const int n1 = node_offsets[b + 1];
   int nn = n1 - n0;
-  if (n0 < 0 || nn < 0 || nn > max_nodes || n1 > total_nodes) nn = -1;   // skip this sequence
+  if (n0 < 0 || nn < 0 || nn > max_nodes || n1 > total_nodes) nn = 0;   // nothing accepted
+  if (b != 0 || n0 != 0) load_seq_regs(r, ws, draft, mask, cpr, W, n0, nn);
 
-  for (int w = tid; w < W; w += kThreads) match_w[w] = 0ull;
-  __syncthreads();
+  const int words = nn * W;
+#pragma unroll
+  for (int k = 0; k < kSpec; ++k) {
+    const int q = tid + k * kThreads;
+    if (q < words) rows[q] = r.m[k];
+  }
+  for (int q = tid + kSpec * kThreads; q < words; q += kThreads) rows[q] = mask[(size_t)n0 * W + q];
 
   // Target argmax per node: the cpr chunk results of one node sit in cpr
   // consecutive lanes of one wave (cpr is a power of two <= 64); a segmented
   // butterfly leaves the winner in the node's first lane.
-  const int pairs = nn > 0 ? nn * cpr : 0;
-  for (int p0 = 0; p0 < pairs; p0 += kThreads) {
-    const int pidx = p0 + tid;
+  const int pairs = nn * cpr;
+  auto reduce_pass = [&](int pidx, float2 x) {
     float bv = kNegInf;
     int bi = 0x7fffffff;
     if (pidx < pairs) {
-      const float2 x = ws[(size_t)n0 * cpr + pidx];
       bv = x.x;
       bi = __float_as_int(x.y);
     }
@@ -178,18 +212,43 @@ __global__ __launch_bounds__(kThreads) void path_select_kernel(
     }
     if (pidx < pairs && (pidx & (cpr - 1)) == 0) {
       const int i = pidx / cpr;
+      tgt[i] = bi;
       if (target_argmax) target_argmax[n0 + i] = bi;
-      if (draft[n0 + i] == bi) atomicOr(&match_w[i >> 6], 1ull << (i & 63));
     }
+  };
+#pragma unroll
+  for (int k = 0; k < kSpec; ++k)
+    if (k * kThreads < pairs) reduce_pass(tid + k * kThreads, r.x[k]);
+  for (int p0 = kSpec * kThreads; p0 < pairs; p0 += kThreads) {
+    const int pidx = p0 + tid;
+    reduce_pass(pidx, pidx < pairs ? ws[(size_t)n0 * cpr + pidx] : make_float2(0.f, 0.f));
   }
   __syncthreads();
 
+  // Match set: node i matches iff its draft token is the target's argmax.
+  // Thread t, slot k holds node t + 256k, so wave w's ballot is word 4k + w.
+  auto match_pass = [&](int i, int32_t d) {
+    const bool m = i < nn && d == tgt[i < nn ? i : 0];
+    const uint64_t bits = __ballot(m);
+    if (lane == 0 && 64 * (i >> 6) < nn) match_w[i >> 6] = bits;
+  };
+#pragma unroll
+  for (int k = 0; k < kSpec; ++k)
+    if (k * kThreads < nn) match_pass(tid + k * kThreads, r.d[k]);
+  for (int i0 = kSpec * kThreads; i0 < nn; i0 += kThreads) {
+    const int i = i0 + tid;
+    match_pass(i, i < nn ? draft[n0 + i] : -1);
+  }
+  __syncthreads();
+
+  // Node i is accepted iff its whole root path matches (mask row within the
+  // match set); the longest accepted path wins, lowest index on ties.
   unsigned long long key = 0ull;
   for (int i = tid; i < nn; i += kThreads) {
     bool ok = true;
     int len = 0;
     for (int w = 0; w < W; ++w) {
-      uint64_t mw = mask[(size_t)(n0 + i) * W + w];
+      uint64_t mw = rows[i * W + w];
       const int base = 64 * w;
       if (base >= nn) mw = 0ull;
       else if (nn - base < 64) mw &= (1ull << (nn - base)) - 1ull;
@@ -213,6 +272,9 @@ __global__ __launch_bounds__(kThreads) void path_select_kernel(
   const int len = (int)(key >> 32);
   const int best = (int)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
 
+  // The accepted path is the set bits of the best node's row in increasing
+  // order (root to leaf); each of its nodes is placed by the thread that
+  // holds its draft token.
   int32_t* an = accept_nodes + (size_t)b * max_nodes;
   int32_t* at = accept_tokens + (size_t)b * max_nodes;
   for (int pos = tid; pos < max_nodes; pos += kThreads)
@@ -221,15 +283,23 @@ __global__ __launch_bounds__(kThreads) void path_select_kernel(
       at[pos] = -1;
     }
   if (len > 0) {
-    const uint64_t* brow = mask + (size_t)(n0 + best) * W;
-    for (int j = tid; j < nn; j += kThreads) {
+    const uint64_t* brow = rows + (size_t)best * W;
+    auto place = [&](int j, int32_t d) {
+      if (j >= nn) return;
       const int wj = j >> 6;
       const uint64_t mw = brow[wj];
-      if (!((mw >> (j & 63)) & 1ull)) continue;
+      if (!((mw >> (j & 63)) & 1ull)) return;
       int pos = __popcll(mw & ((1ull << (j & 63)) - 1ull));
       for (int w = 0; w < wj; ++w) pos += __popcll(brow[w]);
       an[pos] = j;
-      at[pos] = draft[n0 + j];
+      at[pos] = d;
+    };
+#pragma unroll
+    for (int k = 0; k < kSpec; ++k)
+      if (k * kThreads < nn) place(tid + k * kThreads, r.d[k]);
+    for (int j0 = kSpec * kThreads; j0 < nn; j0 += kThreads) {
+      const int j = j0 + tid;
+      place(j, j < nn ? draft[n0 + j] : -1);
     }
   }
   if (tid == 0) accept_len[b] = len;
@@ -283,7 +353,13 @@ hipError_t launch_verify(bool bf16, const void* logits, const int32_t* draft,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(path_select_kernel, dim3(B), dim3(kThreads), 0, stream, ws, p.cpr, draft,
+  const size_t lds = (size_t)max_nodes * W * sizeof(uint64_t);
+  if (lds > 32 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&path_select_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(path_select_kernel, dim3(B), dim3(kThreads), lds, stream, ws, p.cpr, draft,
                      mask, node_offsets, total_nodes, max_nodes, W, target_argmax, accept_len,
                      accept_nodes, accept_tokens);
   return hipGetLastError();
