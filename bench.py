@@ -9,7 +9,10 @@ the target argmax with probability 0.6).
 
 Inputs are resident in HBM before timing starts.  To keep the 256 MB Infinity
 Cache from serving repeated reads, the step rotates over --sets copies of every
-input (16 x ~35 MB by default), so each step reads cold data.
+input (16 x ~35 MB by default), so each step reads cold data.  Each step is
+captured once per copy into a HIP graph and replayed (--eager launches every
+call from Python instead); the graphs are checked bit for bit against eager
+steps before timing.
 
 Prints ONE JSON line: tree-tokens/s of the whole step (value), plus per-call
 device times from HIP events on the launch stream, the roofline of the
@@ -43,6 +46,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="llama3_8b")
     p.add_argument("--sets", type=int, default=32)
+    p.add_argument("--eager", action="store_true",
+                   help="launch every call from Python instead of replaying captured HIP graphs")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calib-copy", action="store_true",
@@ -262,33 +267,96 @@ def main():
         do_forward(s)
         do_verify(s)
 
-    # --- whole-step timing ----------------------------------------------------------------
+    # --- HIP graphs ------------------------------------------------------------------------
+    # The Python binding costs tens of microseconds of host time per call, about as
+    # much as the whole step on the GPU, so by default each step is captured once per
+    # rotation set into a HIP graph (torch.cuda.CUDAGraph) and replayed: every replay
+    # runs all the kernels of the step on that set's inputs.  The warmup runs eagerly
+    # first (it also sets the kernels' LDS limits, which capture must not do).
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+
+    def outputs():
+        return [t.clone() for t in (mask, depth, status, out, pred, alen, anodes, atok)]
+
+    def capture(fn, idx):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in idx:
+                fn(sets[i])
+        return g
+
+    use_graphs = not args.eager
+    n_rot = len(sets)
+    one_step = lambda s: (do_mask(s), do_forward(s), do_verify(s))
+    if use_graphs:
+        # A graph launch itself costs host time comparable to a step, so one graph holds
+        # the steps of all rotation sets in order; single-step graphs cover the rest.
+        step_graphs = [capture(one_step, [i]) for i in range(n_rot)]
+        round_graph = capture(one_step, range(n_rot))
+        # Every graph must reproduce the eager step bit for bit, replayed twice with eager
+        # work on other inputs in between.
+        for k, g in ((0, step_graphs[0]), (n_rot - 1, step_graphs[n_rot - 1]),
+                     (n_rot - 1, round_graph)):
+            step(k)
+            torch.cuda.synchronize()
+            ref = outputs()
+            for rep in range(2):
+                step(k + 1)
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                for a, b in zip(outputs(), ref):
+                    if not torch.equal(a, b):
+                        raise SystemExit(f"graph replay {rep} (last set {k}) differs from the "
+                                         "eager step")
+
+        def run_steps(k):
+            for _ in range(k // n_rot):
+                round_graph.replay()
+            for i in range(k % n_rot):
+                step_graphs[i].replay()
+    else:
+        def run_steps(k):
+            for i in range(k):
+                step(i)
+
+    # --- whole-step timing ----------------------------------------------------------------
+    run_steps(n_rot)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
+    run_steps(args.steps)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     value = sum_n * args.steps / elapsed
-    print(f"[bench] {args.steps} steps in {elapsed:.4f} s", file=sys.stderr, flush=True)
+    print(f"[bench] {args.steps} steps in {elapsed:.4f} s ({'graphs' if use_graphs else 'eager'})",
+          file=sys.stderr, flush=True)
 
     # --- per-call device time with HIP events on the launch stream ------------------------
+    # One graph holds one call per rotation set; events bracket whole replays.
     stream = torch.cuda.current_stream(dev)
 
     def event_time(fn, n):
-        for i in range(3):
-            fn(sets[i % len(sets)])
+        if use_graphs:
+            g = capture(fn, range(len(sets)))
+            reps = max(1, -(-n // len(sets)))
+            calls = reps * len(sets)
+            run = lambda i: g.replay()
+        else:
+            reps = calls = n
+            run = lambda i: fn(sets[i % len(sets)])
+        for i in range(2):
+            run(i)
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         start.record(stream)
-        for i in range(n):
-            fn(sets[i % len(sets)])
+        for i in range(reps):
+            run(i)
         end.record(stream)
         end.synchronize()
-        return start.elapsed_time(end) * 1e3 / n   # microseconds per call
+        return start.elapsed_time(end) * 1e3 / calls   # microseconds per call
 
     do_mask(sets[0])
     t_mask = event_time(do_mask, args.steps)
@@ -355,7 +423,9 @@ def main():
             "workload": f"{args.config}: B={B} Hq={Hq} Hkv={Hkv} D={D} L={max_prefix} N={max_nodes} "
                         f"(sum_L={sum_l}, sum_N={sum_n}); greedy verify over V={V} bf16 logits",
             "step": "build_mask + forward + verify_greedy, inputs rotated over "
-                    f"{len(sets)} resident copies of {set_bytes / 2**20:.1f} MiB",
+                    f"{len(sets)} resident copies of {set_bytes / 2**20:.1f} MiB, "
+                    + ("replayed from captured HIP graphs (one per round over the copies)"
+                       if use_graphs else "launched eagerly from Python"),
             "global_batch": B, "seq_len": max_prefix, "tree_nodes": sum_n,
         },
         "roofline": roof(dominant),

@@ -1,0 +1,93 @@
+"""The whole step (mask -> forward -> verify) captured in a HIP graph and
+replayed must reproduce the eager calls bit for bit, on every replay, with
+eager work on other inputs (that overwrites the same output buffers) and
+synchronisations in between."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from helpers import lib
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed):
+    rng = np.random.default_rng(seed)
+    trees = [synthetic.random_tree(rng, 64, 1, 6, 4).tolist(),
+             synthetic.random_tree(rng, 37, 2, 5, None).tolist()]
+    c = synthetic.make_case("graph", prefix_lens=[700, 2001], trees=trees, Hq=32, Hkv=8, D=128,
+                            dtype=torch.bfloat16, seed=seed, vocab=5000, p_match=0.7)
+    d = torch.device("cuda")
+    t = {"parents": torch.from_numpy(c.parents).to(d),
+         "noffs": torch.from_numpy(c.node_offsets).to(d),
+         "poffs": torch.from_numpy(c.prefix_offsets).to(d),
+         "q": c.q.to(d), "kt": c.k_tree.to(d), "vt": c.v_tree.to(d), "kp": c.k_prefix.to(d),
+         "vp": c.v_prefix.to(d), "logits": c.logits.to(d),
+         "draft": torch.from_numpy(c.draft).to(d)}
+    return c, t
+
+
+def test_step_graph_replays_match_eager():
+    ta = lib()
+    ca, a = _inputs(11)
+    cb, b = _inputs(12)
+    # Both cases must have the same node counts so they can share output buffers.
+    assert ca.total_nodes == cb.total_nodes and ca.max_nodes == cb.max_nodes
+    d = torch.device("cuda")
+    n, max_nodes, B = ca.total_nodes, ca.max_nodes, ca.B
+    W = ta.mask_words(max_nodes)
+    bufs = {
+        "mask": torch.empty((n, W), dtype=torch.uint64, device=d),
+        "depth": torch.empty(n, dtype=torch.int32, device=d),
+        "status": torch.empty(B, dtype=torch.int32, device=d),
+        "out": torch.empty_like(a["q"]),
+        "lse": torch.empty((n, 32), dtype=torch.float32, device=d),
+        "pred": torch.empty(n, dtype=torch.int32, device=d),
+        "alen": torch.empty(B, dtype=torch.int32, device=d),
+        "anodes": torch.empty((B, max_nodes), dtype=torch.int32, device=d),
+        "atok": torch.empty((B, max_nodes), dtype=torch.int32, device=d),
+    }
+    sum_l = int(ca.prefix_offsets[-1])
+    fws = torch.empty(max(ta.forward_workspace_size(torch.bfloat16, B, n, max_nodes, 32, 8, 128,
+                                                    sum_l, ca.max_prefix), 16),
+                      dtype=torch.uint8, device=d)
+    vws = torch.empty(max(ta.verify_workspace_size(n, max_nodes, 5000), 16), dtype=torch.uint8,
+                      device=d)
+
+    def step(t, c):
+        ta.build_mask(t["parents"], t["noffs"], max_nodes, mask=bufs["mask"],
+                      depth=bufs["depth"], status=bufs["status"])
+        ta.forward(t["q"], t["kt"], t["vt"], t["kp"], t["vp"], t["poffs"], t["noffs"],
+                   bufs["mask"], max_nodes, c.max_prefix, c.scale, out=bufs["out"],
+                   lse=bufs["lse"], workspace=fws)
+        ta.verify_greedy(t["logits"], t["draft"], bufs["mask"], t["noffs"], max_nodes,
+                         workspace=vws, target_argmax=bufs["pred"], accept_len=bufs["alen"],
+                         accept_nodes=bufs["anodes"], accept_tokens=bufs["atok"])
+
+    def snapshot():
+        return {k: v.clone() for k, v in bufs.items()}
+
+    step(a, ca)   # eager first: sets kernel attributes outside capture
+    torch.cuda.synchronize()
+    ref = snapshot()
+    rp, rlen, rnodes, rtok = oracle.verify_greedy(ca.logits, ca.draft, ca.parents,
+                                                  ca.node_offsets, max_nodes)
+    np.testing.assert_array_equal(ref["alen"].cpu().numpy(), rlen)
+    np.testing.assert_array_equal(ref["anodes"].cpu().numpy(), rnodes)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(a, ca)
+    for rep in range(4):
+        step(b, cb)                      # eager work on the other inputs
+        torch.cuda.synchronize()
+        assert not torch.equal(bufs["out"], ref["out"])
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        for k in bufs:
+            assert torch.equal(got[k], ref[k]), f"replay {rep}: {k} differs from the eager step"

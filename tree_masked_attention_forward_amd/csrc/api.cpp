@@ -4,7 +4,33 @@
 // nothing and touches no device state.
 #include <math.h>
 
+#include <mutex>
+#include <vector>
+
 #include "internal.h"
+
+namespace ta {
+
+hipError_t raise_dynamic_lds(const void* kernel, int bytes) {
+  struct Entry {
+    const void* kernel;
+    int device;
+    int bytes;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& x : done)
+    if (x.kernel == kernel && x.device == dev && x.bytes >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.push_back(Entry{kernel, dev, bytes});
+  return e;
+}
+
+}  // namespace ta
 
 namespace {
 

@@ -660,8 +660,7 @@ template <int RG, int KG, int TPW>
 hipError_t launch_shape(const KParams& kp, long long grid, long long merge_grid, hipStream_t stream) {
   const size_t lds = LdsMap<RG, KG, TPW>::kBytes;
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_bf16_kernel<RG, KG, TPW>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = raise_dynamic_lds(reinterpret_cast<const void*>(&fwd_bf16_kernel<RG, KG, TPW>), (int)lds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((fwd_bf16_kernel<RG, KG, TPW>), dim3((unsigned)grid), dim3(RG * KG * 64), lds,

@@ -42,6 +42,12 @@ struct FwdArgs {
   void* workspace;
 };
 
+// Raises a kernel's dynamic LDS limit to at least `bytes` on the current
+// device.  The attribute is set once per (kernel, device) and cached, so
+// launches after the first make no runtime call here (safe under stream
+// capture once the kernel has run eagerly).
+hipError_t raise_dynamic_lds(const void* kernel, int bytes);
+
 FwdPlan plan_forward_bf16(int B, int total_nodes, int max_nodes, int Hq, int Hkv,
                           long long total_prefix, long long max_prefix);
 

@@ -132,8 +132,7 @@ hipError_t launch_build_mask(const int32_t* parents, const int32_t* node_offsets
   const int W = (max_nodes + 63) / 64;
   const size_t lds = (size_t)max_nodes * W * sizeof(uint64_t) + 2 * (size_t)max_nodes * sizeof(int32_t);
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&build_mask_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = raise_dynamic_lds(reinterpret_cast<const void*>(&build_mask_kernel), (int)lds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(build_mask_kernel, dim3(B), dim3(kThreads), lds, stream, parents,

@@ -355,8 +355,7 @@ hipError_t launch_verify(bool bf16, const void* logits, const int32_t* draft,
   }
   const size_t lds = (size_t)max_nodes * W * sizeof(uint64_t);
   if (lds > 32 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&path_select_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = raise_dynamic_lds(reinterpret_cast<const void*>(&path_select_kernel), (int)lds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(path_select_kernel, dim3(B), dim3(kThreads), lds, stream, ws, p.cpr, draft,
