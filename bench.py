@@ -126,12 +126,22 @@ def summarize_profiles(root):
              "Command (run from the repository root on the MI355X box):", "",
              "    " + PROFILE_CMDS["prof_trace"], "",
              "| kernel | calls | avg us | min us | max us | % |", "|---|---|---|---|---|---|"]
+    other_calls, other_ns = 0, 0.0
     for r in stats:
         name = r["Name"]
+        if "ta::" not in name:
+            # torch kernels of input setup and of the graph-vs-eager checks, outside the
+            # timed region
+            other_calls += int(r["Calls"])
+            other_ns += float(r["TotalDurationNs"])
+            continue
         short = name.replace("ta::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.3f} | "
                      f"{float(r['MinNs'])/1e3:.3f} | {float(r['MaxNs'])/1e3:.3f} | "
                      f"{float(r['Percentage']):.1f} |")
+    if other_calls:
+        lines += ["", f"Other kernels (input setup and the graph-vs-eager checks, outside the timed "
+                      f"region): {other_calls} calls, {other_ns / 1e3:.1f} us in total."]
     with open(os.path.join(PROFILES, "tree_attn_step_llama3_8b_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     # HBM traffic from FETCH_SIZE / WRITE_SIZE, scaled by the copy calibration

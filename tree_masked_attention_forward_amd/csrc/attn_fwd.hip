@@ -68,7 +68,6 @@ constexpr int kKT = 32;                       // keys per tile
 constexpr int kRow = kD * 2;                  // LDS bytes per K or V row (unpadded, chunks swizzled)
 constexpr int kTileKV = kKT * kRow;           // 8192: one K or one V tile
 constexpr int kTileBytes = 2 * kTileKV;       // K tile then V tile
-constexpr int kNumStages = 3;                 // LDS ring: stage it in use, it+1 and it+2 in flight
 constexpr int kLdsMax = 160 * 1024;           // LDS per workgroup on gfx950
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
@@ -137,6 +136,15 @@ __device__ inline bool row_tile_range(const KParams& P, const Seq& sq, int r, Ra
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt immediate that waits for vmcnt <= N and nothing else (gfx9
+// encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and
+// lgkmcnt at their maxima).
+template <int N>
+constexpr int vmcnt_imm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  return (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
 // Direct global -> LDS loads, issued through inline asm so that the only
 // waits on them are the explicit vmcnt waits of the pipeline (the compiler
 // would otherwise wait for every pending load before each LDS read).  The
@@ -163,29 +171,30 @@ __device__ inline i16x4_t lds_read_tr16(const unsigned char* p) {
       (__attribute__((address_space(3))) i16x4_t*)(p));
 }
 
-// LDS map of one workgroup: a ring of kNumStages stages, each KG*TPW x
-// (K tile, V tile) followed by TPW mask dwords per lane per wave, and the
-// workgroup's query rows (32*RG rows, laid out like a K tile).  The query
-// block sits after the ring when both fit, otherwise over ring slot 2, which
-// is first written only after every wave has copied its rows to registers.
-template <int RG, int KG, int TPW>
+// LDS map of one workgroup: a ring of NS stages, each KG*TPW x (K tile,
+// V tile) followed by TPW mask dwords per lane per wave, and the workgroup's
+// query rows (32*RG rows, laid out like a K tile).  The query block sits
+// after the ring when both fit, otherwise over the last ring slot, which is
+// first written only after every wave has copied its rows to registers.
+template <int RG, int KG, int TPW, int NS>
 struct LdsMap {
   static constexpr int kMaskOff = KG * TPW * kTileBytes;
   static constexpr int kStage = kMaskOff + RG * KG * TPW * 256;
-  static constexpr int kRing = kNumStages * kStage;
+  static constexpr int kRing = NS * kStage;
   static constexpr int kQBytes = RG * 32 * kRow;
   static constexpr bool kQAlias = kRing + kQBytes > kLdsMax;
-  static constexpr int kQOff = kQAlias ? 2 * kStage : kRing;
+  static constexpr int kQOff = kQAlias ? (NS - 1) * kStage : kRing;
   static constexpr int kBytes = kQOff + kQBytes > kRing ? kQOff + kQBytes : kRing;
   static_assert(kBytes <= kLdsMax, "LDS budget");
 };
 
-template <int RG, int KG, int TPW>
+template <int RG, int KG, int TPW, int NS>
 __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
+  static_assert(NS >= 3 && NS <= 4, "ring depth");
   constexpr int NW = RG * KG;
   constexpr int NT = NW * 64;
   constexpr int kTilesPerStage = KG * TPW;
-  using Map = LdsMap<RG, KG, TPW>;
+  using Map = LdsMap<RG, KG, TPW, NS>;
   constexpr int kMaskOff = Map::kMaskOff;
   constexpr int kStage = Map::kStage;
   extern __shared__ __align__(16) unsigned char lds[];
@@ -292,7 +301,7 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
   const uint32_t* mrow_dw = reinterpret_cast<const uint32_t*>(
       P.mask + (size_t)(sq.n0 + (row_ok ? node : 0)) * P.W);
   auto issue_stage = [&](int it) {
-    unsigned char* st = lds + (it % kNumStages) * kStage;
+    unsigned char* st = lds + (it % NS) * kStage;
 #pragma unroll
     for (int tk = 0; tk < kTilesPerStage; ++tk) {
       const int tile = t_lo + it * kTilesPerStage + tk;
@@ -331,11 +340,16 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
   // to stage it and all have passed the barrier.  The barrier carries no
   // memory fence (a fence would wait for the stages still in flight); the
   // empty asm statements keep the compiler from moving LDS accesses across.
+  // Stages issued after stage it: min(NS - 2, n_iter - 1 - it).
+  static_assert((NS - 2) * kLoads <= 63, "vmcnt range");
   auto wait_stage = [&](int it, int n_iter) {
-    if (it + 1 < n_iter)
-      __builtin_amdgcn_s_waitcnt((kLoads & 15) | ((kLoads >> 4) << 14) | (7 << 4) | (15 << 8));
+    const int later = min(NS - 2, n_iter - 1 - it);
+    if (NS > 3 && later >= 2)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * kLoads>());
+    else if (later >= 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<kLoads>());
     else
-      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -455,17 +469,18 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
     }
   };
 
-  // Pipeline: stage it is computed while stages it+1 and it+2 are in flight;
-  // the LDS ring reuses slot (it+2) % kNumStages, which every wave finished
+  // Pipeline: stage it is computed while stages it+1 .. it+NS-2 are in
+  // flight; stage it+NS-1 goes to slot (it-1) % NS, which every wave finished
   // reading before the barrier of stage it.  Each wave takes TPW consecutive
   // tiles per stage: all their scores first, then softmax + PV of each, in
   // one basic block, so the scheduler can fill the MFMA chains of one tile
   // with the VALU work of the other.
   // The query loads precede stage 0, so the first stage wait retires them.
   issue_q();
-  issue_stage(0);
-  if (n_iter > 1) issue_stage(1);
-  int slot = 0;   // it % kNumStages, kept in a scalar register
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k)
+    if (k < n_iter) issue_stage(k);
+  int slot = 0;   // it % NS, kept in a scalar register
   for (int it = 0; it < n_iter; ++it) {
     wait_stage(it, n_iter);
     if (it == 0) {
@@ -474,18 +489,18 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
       for (int i = 0; i < 8; ++i)
         qf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qb + koff[i]));
       if (Map::kQAlias) {
-        // Ring slot 2 holds the query block: every wave has its rows in
-        // registers before stage 2 is issued over it.
+        // The last ring slot holds the query block: every wave has its rows
+        // in registers before stage NS-1 is issued over it.
         __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4));   // lgkmcnt(0)
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
       }
     }
-    if (it + 2 < n_iter) issue_stage(it + 2);
+    if (it + NS - 1 < n_iter) issue_stage(it + NS - 1);
     // Stage base as one uniform value, so each LDS read needs one add.
     const unsigned char* st = lds + __builtin_amdgcn_readfirstlane(slot * kStage);
-    slot = (slot + 1 == kNumStages) ? 0 : slot + 1;
+    slot = (slot + 1 == NS) ? 0 : slot + 1;
     f32x16_t sc[TPW];
     int tl[TPW];
     bool ac[TPW];
@@ -506,37 +521,55 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
   }
   __syncthreads();
 
-  if (KG > 1) {
-    // Merge the key groups through LDS (the stage buffers are free now):
-    // O in register order [rg][v][lane], then max and per-lane sum.
+  // Dim blocks (32 dims each) this wave combines and stores.
+  bool keep_lo = true, keep_hi = true;
+  if constexpr (KG > 1) {
+    // The two key groups of a row group swap halves through LDS (the stage
+    // buffers are free now): wave kg keeps dim blocks 2kg, 2kg+1, hands the
+    // other two to its partner with its running max and sum, and both
+    // combine and store half of the rows' dims.  Layout [rg][kg][v][lane].
+    static_assert(KG == 2, "key groups are merged in pairs");
     float* xo = reinterpret_cast<float*>(lds);
-    float* xm = xo + RG * 64 * 64;
-    float* xl = xm + RG * 64;
-    if (kg == 1 && group_active) {
+    float* xm = xo + RG * 2 * 32 * 64;
+    float* xl = xm + RG * 2 * 64;
+    const int mine = rg * 2 + kg;
+    const int other = rg * 2 + (kg ^ 1);
+    if (group_active) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int e2 = 0; e2 < 2; ++e2)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) xo[(rg * 64 + 16 * e + v) * 64 + lane] = oacc[e][v];
-      xm[rg * 64 + lane] = m_run;
-      xl[rg * 64 + lane] = l_run;
+        for (int v = 0; v < 16; ++v)
+          xo[(mine * 32 + 16 * e2 + v) * 64 + lane] = kg == 0 ? oacc[2 + e2][v] : oacc[e2][v];
+      xm[mine * 64 + lane] = m_run;
+      xl[mine * 64 + lane] = l_run;
     }
     __syncthreads();
-    if (kg != 0 || !group_active) return;
-    const float m1 = xm[rg * 64 + lane];
-    const float l1 = xl[rg * 64 + lane];
+    if (!group_active) return;
+    const float m1 = xm[other * 64 + lane];
+    const float l1 = xl[other * 64 + lane];
     const float mm = fmaxf(m_run, m1);
     const float mu = (mm == kNegInf) ? 0.f : mm;
     const float a0 = fast_exp2((m_run - mu) * c2);
     const float a1 = fast_exp2((m1 - mu) * c2);
+    if (kg == 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+      for (int e2 = 0; e2 < 2; ++e2)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        oacc[e][v] = oacc[e][v] * a0 + xo[(rg * 64 + 16 * e + v) * 64 + lane] * a1;
+        for (int v = 0; v < 16; ++v)
+          oacc[e2][v] = oacc[e2][v] * a0 + xo[(other * 32 + 16 * e2 + v) * 64 + lane] * a1;
+    } else {
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          oacc[2 + e2][v] = oacc[2 + e2][v] * a0 + xo[(other * 32 + 16 * e2 + v) * 64 + lane] * a1;
+    }
     l_run = l_run * a0 + l1 * a1;
     m_run = mm;
-  } else if (!group_active) {
-    return;
+    keep_lo = kg == 0;
+    keep_hi = kg == 1;
+  } else {
+    if (!group_active) return;
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -546,7 +579,8 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
     const float inv = 1.f / l_tot;
     uint16_t* orow = P.out + ((size_t)(sq.n0 + node) * P.Hq + head) * kD;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < 4; ++e) {
+      if (!(e < 2 ? keep_lo : keep_hi)) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         f32x4_t f;
@@ -555,22 +589,32 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
         const bf16x4_t h4 = __builtin_convertvector(f, bf16x4_t);
         *reinterpret_cast<u32x2_t*>(orow + 32 * e + 8 * j + 4 * hh) = __builtin_bit_cast(u32x2_t, h4);
       }
-    if (P.lse && hh == 0) P.lse[(size_t)(sq.n0 + node) * P.Hq + head] = m_run * P.scale + logf(l_tot);
+    }
+    if (P.lse && hh == 0 && keep_lo)
+      P.lse[(size_t)(sq.n0 + node) * P.Hq + head] = m_run * P.scale + logf(l_tot);
   } else {
     // Normalised partial O in bf16 (the merge reweights by l), lane-major so
-    // each store instruction writes 512 contiguous bytes.
+    // each store instruction writes 512 contiguous bytes.  Streaming stores:
+    // the partials are read once, by the merge kernel, so they should not sit
+    // dirty in L2 when this kernel ends.
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     u32x2_t* wo = P.ws_o + ((size_t)item * RG + rg) * 16 * 64 + lane;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < 4; ++e) {
+      if (!(e < 2 ? keep_lo : keep_hi)) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         f32x4_t f;
 #pragma unroll
         for (int x = 0; x < 4; ++x) f[x] = oacc[e][4 * j + x] * inv;
-        wo[(4 * e + j) * 64] = __builtin_bit_cast(u32x2_t, __builtin_convertvector(f, bf16x4_t));
+        __builtin_nontemporal_store(
+            __builtin_bit_cast(u32x2_t, __builtin_convertvector(f, bf16x4_t)), &wo[(4 * e + j) * 64]);
       }
-    if (hh == 0) P.ws_ml[(size_t)item * P.rows_wg + rg * 32 + l32] = make_float2(m_run, l_tot);
+    }
+    if (hh == 0 && keep_lo)
+      __builtin_nontemporal_store(
+          __builtin_bit_cast(u32x2_t, make_float2(m_run, l_tot)),
+          reinterpret_cast<u32x2_t*>(P.ws_ml + (size_t)item * P.rows_wg + rg * 32 + l32));
   }
 }
 
@@ -656,15 +700,16 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
     P.lse[(size_t)(sq.n0 + node) * P.Hq + head] = lsum > 0.f ? M * P.scale + logf(lsum) : kNegInf;
 }
 
-template <int RG, int KG, int TPW>
+template <int RG, int KG, int TPW, int NS>
 hipError_t launch_shape(const KParams& kp, long long grid, long long merge_grid, hipStream_t stream) {
-  const size_t lds = LdsMap<RG, KG, TPW>::kBytes;
+  const size_t lds = LdsMap<RG, KG, TPW, NS>::kBytes;
   if (lds > 64 * 1024) {
-    hipError_t e = raise_dynamic_lds(reinterpret_cast<const void*>(&fwd_bf16_kernel<RG, KG, TPW>), (int)lds);
+    hipError_t e =
+        raise_dynamic_lds(reinterpret_cast<const void*>(&fwd_bf16_kernel<RG, KG, TPW, NS>), (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((fwd_bf16_kernel<RG, KG, TPW>), dim3((unsigned)grid), dim3(RG * KG * 64), lds,
-                     stream, kp);
+  hipLaunchKernelGGL((fwd_bf16_kernel<RG, KG, TPW, NS>), dim3((unsigned)grid), dim3(RG * KG * 64),
+                     lds, stream, kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || merge_grid == 0) return e;
   hipLaunchKernelGGL((merge_bf16_kernel<RG>), dim3((unsigned)merge_grid), dim3(256), 0, stream, kp);
@@ -748,10 +793,11 @@ hipError_t launch_forward_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t s
   const long long grid = (p.n_items + 7) / 8 * 8;
   const long long merge_grid = p.S > 1 ? (long long)a.B * a.Hkv * p.R * p.rg * 4 : 0;
   switch (p.rg * 16 + p.kg) {
-    case 1 * 16 + 2: return launch_shape<1, 2, 1>(kp, grid, merge_grid, stream);
-    case 2 * 16 + 2: return launch_shape<2, 2, 1>(kp, grid, merge_grid, stream);
-    case 4 * 16 + 2: return launch_shape<4, 2, 1>(kp, grid, merge_grid, stream);
-    case 8 * 16 + 1: return launch_shape<8, 1, 2>(kp, grid, merge_grid, stream);
+    // A three-stage ring measured as fast as four on every shape here.
+    case 1 * 16 + 2: return launch_shape<1, 2, 1, 3>(kp, grid, merge_grid, stream);
+    case 2 * 16 + 2: return launch_shape<2, 2, 1, 3>(kp, grid, merge_grid, stream);
+    case 4 * 16 + 2: return launch_shape<4, 2, 1, 3>(kp, grid, merge_grid, stream);
+    case 8 * 16 + 1: return launch_shape<8, 1, 2, 3>(kp, grid, merge_grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
