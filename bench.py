@@ -249,7 +249,7 @@ def main():
     depth = torch.empty(sum_n, dtype=torch.int32, device=dev)
     status = torch.empty(B, dtype=torch.int32, device=dev)
     out = torch.empty_like(base["q"])
-    fws = torch.empty(max(ta.forward_workspace_size(case.dtype, B, sum_n, max_nodes, Hq, Hkv, D,
+    fws = torch.zeros(max(ta.forward_workspace_size(case.dtype, B, sum_n, max_nodes, Hq, Hkv, D,
                                                     sum_l, max_prefix), 16),
                       dtype=torch.uint8, device=dev)
     vws = torch.empty(max(ta.verify_workspace_size(sum_n, max_nodes, V), 16), dtype=torch.uint8,

@@ -128,9 +128,16 @@ TA_API size_t tree_attn_forward_workspace_size(int dtype, int32_t B, int32_t tot
  *   out            out [sum_N][Hq][D], dtype as the inputs.
  *   lse            out fp32 [sum_N][Hq], nullable.
  *   workspace      device buffer of at least tree_attn_forward_workspace_size()
- *                  bytes (may be NULL when that size is 0); contents on entry
- *                  do not matter; calls sharing one workspace must be ordered
- *                  on one stream.
+ *                  bytes (may be NULL when that size is 0).  It must be
+ *                  zero-filled before its first use; every call that runs to
+ *                  completion leaves it ready for the next call (a few
+ *                  per-group counters, used when the splits of the key range
+ *                  are merged inside the same kernel, return to zero; the
+ *                  rest is scratch).  A workspace whose counters are not zero
+ *                  does not hang a call: the affected outputs are written as
+ *                  NaN after a bounded wait (about 0.3 s) and the counters
+ *                  are zeroed for the next call.  Calls sharing one
+ *                  workspace must be ordered on one stream.
  */
 TA_API int tree_attn_forward(int dtype, const void* q, const void* k_tree, const void* v_tree,
                       const void* k_prefix, const void* v_prefix,

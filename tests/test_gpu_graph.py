@@ -15,11 +15,17 @@ from helpers import lib
 pytestmark = pytest.mark.gpu
 
 
-def _inputs(seed):
+# Two sequences (splits merged by a separate kernel) and one sequence (splits
+# merged inside the forward kernel, through counters in the workspace).
+SHAPES = {"two_sequences": ([700, 2001], [(64, 1, 6, 4), (37, 2, 5, None)]),
+          "one_sequence": ([3000], [(64, 1, 6, 4)])}
+
+
+def _inputs(seed, shape):
     rng = np.random.default_rng(seed)
-    trees = [synthetic.random_tree(rng, 64, 1, 6, 4).tolist(),
-             synthetic.random_tree(rng, 37, 2, 5, None).tolist()]
-    c = synthetic.make_case("graph", prefix_lens=[700, 2001], trees=trees, Hq=32, Hkv=8, D=128,
+    lens, specs = SHAPES[shape]
+    trees = [synthetic.random_tree(rng, *spec).tolist() for spec in specs]
+    c = synthetic.make_case("graph", prefix_lens=lens, trees=trees, Hq=32, Hkv=8, D=128,
                             dtype=torch.bfloat16, seed=seed, vocab=5000, p_match=0.7)
     d = torch.device("cuda")
     t = {"parents": torch.from_numpy(c.parents).to(d),
@@ -31,10 +37,11 @@ def _inputs(seed):
     return c, t
 
 
-def test_step_graph_replays_match_eager():
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_step_graph_replays_match_eager(shape):
     ta = lib()
-    ca, a = _inputs(11)
-    cb, b = _inputs(12)
+    ca, a = _inputs(11, shape)
+    cb, b = _inputs(12, shape)
     # Both cases must have the same node counts so they can share output buffers.
     assert ca.total_nodes == cb.total_nodes and ca.max_nodes == cb.max_nodes
     d = torch.device("cuda")
@@ -52,7 +59,7 @@ def test_step_graph_replays_match_eager():
         "atok": torch.empty((B, max_nodes), dtype=torch.int32, device=d),
     }
     sum_l = int(ca.prefix_offsets[-1])
-    fws = torch.empty(max(ta.forward_workspace_size(torch.bfloat16, B, n, max_nodes, 32, 8, 128,
+    fws = torch.zeros(max(ta.forward_workspace_size(torch.bfloat16, B, n, max_nodes, 32, 8, 128,
                                                     sum_l, ca.max_prefix), 16),
                       dtype=torch.uint8, device=d)
     vws = torch.empty(max(ta.verify_workspace_size(n, max_nodes, 5000), 16), dtype=torch.uint8,

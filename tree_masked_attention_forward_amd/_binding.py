@@ -189,7 +189,8 @@ def forward(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor,
     ws_bytes = forward_workspace_size(dtype, B, total, max_nodes, Hq, Hkv, D, total_prefix,
                                       max_prefix)
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        # zero-filled once: the library keeps its counters at zero between calls
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     code = TA_BF16 if dtype == torch.bfloat16 else TA_F32
     _check("tree_attn_forward", load_library().tree_attn_forward(

@@ -30,6 +30,21 @@ hipError_t raise_dynamic_lds(const void* kernel, int bytes) {
   return e;
 }
 
+int device_cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cus;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cus.size() <= dev) cus.resize(dev + 1, -1);
+  if (cus[dev] < 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 }  // namespace ta
 
 namespace {

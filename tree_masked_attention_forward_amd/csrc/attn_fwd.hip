@@ -38,11 +38,12 @@
 //     four consecutive keys of one head dimension.
 // K and V tiles (and, ahead of the first stage, the query rows) are staged
 // through LDS with direct 16-byte global->LDS loads in a three-stage ring, one
-// barrier per stage.  Items with one split write bf16 output
-// (and lse) directly; otherwise each leaves (unnormalised O, max, sum) in the
-// workspace (normalised O in bf16, max and sum in fp32), in the MFMA register
-// layout so every store is coalesced, and a merge kernel combines the splits
-// by log-sum-exp.
+// barrier per stage.  Items with one split write bf16 output (and lse)
+// directly; otherwise each leaves its normalised O (bf16) and running max and
+// sum (fp32) in the workspace, in the MFMA register layout so every store is
+// coalesced, and the splits are combined by log-sum-exp: by merge workgroups
+// at the end of the same grid when there are few groups (see
+// merge_in_kernel), else by a separate merge kernel.
 #include "internal.h"
 
 #include <math.h>
@@ -86,7 +87,15 @@ struct KParams {
   float* lse;
   u32x2_t* ws_o;   // [n_items][RG][16][64] 4 x bf16: O / l in register layout
   float2* ws_ml;   // [n_items][rows_wg]   (running max in score units, sum)
+  // In-kernel merge: per (sequence, KV head, row tile) group, the number of
+  // splits that have stored their partial and the number of merge workgroups
+  // done; null when a separate merge kernel combines the splits.
+  unsigned long long* cnt;
   long long total_prefix, max_prefix, n_items;
+  long long n_split_blocks;   // workgroups [0, n_split_blocks) run splits
+  int merge_wpg;              // merge workgroups per group (in-kernel merge)
+  long long groups;           // B * Hkv * R (sequence, KV head, row tile) groups
+  int head_major;             // item order: (b, g, s, r) if set, else (b, s, g, r)
   int total_nodes, max_nodes;
   int Hq, Hkv, G, W;
   int rows_wg, R, S, tmax;
@@ -136,6 +145,49 @@ __device__ inline bool row_tile_range(const KParams& P, const Seq& sq, int r, Ra
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Grid item of (sequence b, KV head g, split s, row tile r).  Split-major
+// order (b, s, g, r) lets one XCD stream whole key rows of a key range; the
+// in-kernel merge uses head-major order (b, g, s, r) so that every split of a
+// (sequence, KV head) lands on one XCD, next to its merge workgroups.
+__device__ inline long long item_index(const KParams& P, int b, int g, int s, int r) {
+  return P.head_major ? (((long long)b * P.Hkv + g) * P.S + s) * P.R + r
+                      : (((long long)b * P.S + s) * P.Hkv + g) * P.R + r;
+}
+
+// Hardware id of the XCD this wave runs on (HW_REG_XCC_ID, bits 3:0).
+__device__ inline int xcc_id() { return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & 15; }
+
+// Arrival word of one group: bits 0..7 count the splits that stored their
+// partial, and 7 bits per XCD (from bit 8) count them per XCD, so the merge
+// can check that every split ran on its own XCD.
+__device__ inline unsigned long long arrival_word(int xcc) {
+  return 1ull + (1ull << (8 + 7 * xcc));
+}
+
+// Log-sum-exp merge of the splits of one (sequence, KV head, row tile, row
+// group, 32-dim block e, 8-dim slice j): split s left its normalised output
+// O_s (bf16), its running max m_s and sum l_s; with M = max_s m_s and
+// w_s = l_s * exp(scale*(m_s - M)),
+//   out = sum_s w_s O_s / sum_s w_s,  lse = scale*M + log(sum_s w_s).
+// Splits that saw no visible key carry m = -inf and weigh nothing.  Lane
+// owns dims 32e + 8j + 4*(lane/32) .. +3 of row lane%32 of the row group.
+struct MergeAcc {
+  float M = kNegInf;
+  float lsum = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  __device__ void add(float2 m_l, u32x2_t hv, float c2) {
+    const f32x4_t o = {__uint_as_float(hv[0] << 16), __uint_as_float(hv[0] & 0xffff0000u),
+                       __uint_as_float(hv[1] << 16), __uint_as_float(hv[1] & 0xffff0000u)};
+    const float m_new = fmaxf(M, m_l.x);
+    const float mu = (m_new == kNegInf) ? 0.f : m_new;
+    const float a = fast_exp2((M - mu) * c2);
+    const float w = fast_exp2((m_l.x - mu) * c2) * m_l.y;
+    acc = acc * a + w * o;
+    lsum = lsum * a + w;
+    M = m_new;
+  }
+};
+
 // s_waitcnt immediate that waits for vmcnt <= N and nothing else (gfx9
 // encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and
 // lgkmcnt at their maxima).
@@ -169,6 +221,120 @@ __device__ inline void dma_b32(const void* g, uint32_t lds_base) {
 __device__ inline i16x4_t lds_read_tr16(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4_t*)(p));
+}
+
+__device__ inline void store_merged(const KParams& P, const Seq& sq, int g, int r, int rl, int e,
+                                    int j, int hh, const MergeAcc& ma) {
+  const int my_row = r * P.rows_wg + rl;
+  const int node = my_row / P.G;
+  const int head = g * P.G + my_row % P.G;
+  const float inv = ma.lsum > 0.f ? 1.f / ma.lsum : 0.f;
+  const bf16x4_t h4 = __builtin_convertvector(ma.acc * inv, bf16x4_t);
+  *reinterpret_cast<u32x2_t*>(P.out + ((size_t)(sq.n0 + node) * P.Hq + head) * kD + 32 * e + 8 * j +
+                              4 * hh) = __builtin_bit_cast(u32x2_t, h4);
+  if (P.lse && e == 0 && j == 0 && hh == 0)
+    P.lse[(size_t)(sq.n0 + node) * P.Hq + head] =
+        ma.lsum > 0.f ? ma.M * P.scale + logf(ma.lsum) : kNegInf;
+}
+
+// In-kernel merge, used when few (sequence, KV head, row tile) groups carry
+// the splits.  Merge workgroups follow the split workgroups in the grid and
+// never hold up a split (a split never waits).  Workgroups are dealt to the
+// 8 XCDs round-robin by id, and the item order puts all splits of a
+// (sequence, KV head) on one XCD; merge workgroup m also runs on XCD m % 8 and
+// takes groups of that XCD.  Partials then stay in that XCD's L2, which is
+// coherent for all its CUs, so no L2 write-back or invalidate is needed: a
+// split stores its partial, waits for the stores to be acknowledged, and
+// adds its arrival word (count + per-XCD count) to the group's counter; the
+// merge workgroup polls the counter until the count reaches the group's
+// split count, checks that every split ran on its own XCD, and merges
+// RG*16/NW (row group, 32-dim block, 8-dim slice) units, one per wave.  If
+// the XCD check fails (workgroups not dealt as assumed) it writes NaN instead
+// of a possibly stale result.  The last merge workgroup of a group returns
+// the group's counters to zero for the next call.  The wait is bounded
+// (about 0.3 s), so counters that were not zero at entry cannot hang a call:
+// a merge workgroup that times out writes NaN and zeroes the counters, so
+// the next call starts clean.
+constexpr int kSpinMax = 1 << 18;
+
+template <int RG, int NW>
+__device__ void merge_in_kernel(const KParams& P, long long m) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long long groups_per_xcd = P.groups / 8;
+  const long long i = m >> 3;
+  const long long gi = (m & 7) * groups_per_xcd + i / P.merge_wpg;
+  const int unit = (int)(i % P.merge_wpg) * NW + wave;   // (rg, e, j) of this wave
+  const int r = (int)(gi % P.R);
+  const int g = (int)((gi / P.R) % P.Hkv);
+  const int b = (int)(gi / ((long long)P.R * P.Hkv));
+  Seq sq;
+  Range rgn;
+  if (!decode_seq(P, b, sq) || !row_tile_range(P, sq, r, rgn) || rgn.Sb <= 1) return;
+  unsigned long long* word = P.cnt + 2 * gi;
+  __shared__ unsigned long long seen_word;
+  __shared__ int timed_out;
+  if (tid == 0) {
+    // Poll with an atomic add of zero, written out because the compiler turns
+    // an idempotent read-modify-write into a plain load, which could keep
+    // reading a stale copy of the counter.
+    unsigned long long seen = 0;
+    int n = 0;
+    for (; n < kSpinMax; ++n) {
+      asm volatile("global_atomic_add_x2 %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)"
+                   : "=v"(seen)
+                   : "v"(word), "v"(0ull)
+                   : "memory");
+      if ((seen & 255) == (unsigned long long)rgn.Sb) break;
+      __builtin_amdgcn_s_sleep(4);
+    }
+    seen_word = seen;
+    timed_out = n == kSpinMax;
+  }
+  __syncthreads();
+  const bool coherent =
+      !timed_out && seen_word == (unsigned long long)rgn.Sb * arrival_word(xcc_id());
+
+  const int rg = unit >> 4;
+  const int e = (unit >> 2) & 3;
+  const int j = unit & 3;
+  const int hh = lane >> 5;
+  const int rl = rg * 32 + (lane & 31);
+  const long long item0 = item_index(P, b, g, 0, r);
+  const long long split_stride = item_index(P, b, g, 1, r) - item0;
+  if (rl < rgn.rows_here) {
+    MergeAcc ma;
+    if (coherent) {
+      for (int s = 0; s < rgn.Sb; ++s) {
+        const long long it = item0 + s * split_stride;
+        // agent-scope loads skip the CU's L1 and read this XCD's L2
+        const unsigned long long ml = __hip_atomic_load(
+            reinterpret_cast<const unsigned long long*>(P.ws_ml + (size_t)it * P.rows_wg + rl),
+            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long o = __hip_atomic_load(
+            reinterpret_cast<const unsigned long long*>(
+                P.ws_o + (((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane),
+            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ma.add(__builtin_bit_cast(float2, ml), __builtin_bit_cast(u32x2_t, o), P.scale_log2);
+      }
+    } else {
+      ma.M = __builtin_nanf("");
+      ma.lsum = 1.f;
+      ma.acc = f32x4_t{ma.M, ma.M, ma.M, ma.M};
+    }
+    store_merged(P, sq, g, r, rl, e, j, hh, ma);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned long long done =
+        timed_out ? 0ull
+                  : __hip_atomic_fetch_add(word + 1, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (timed_out || done + 1 == (unsigned long long)P.merge_wpg) {
+      __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(word + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 // LDS map of one workgroup: a ring of NS stages, each KG*TPW x (K tile,
@@ -209,18 +375,31 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
   const int hh = lane >> 5;   // lane half: which 8 of each 16 contraction elements
   const int l32 = lane & 31;
 
+  if (blockIdx.x >= P.n_split_blocks) {
+    merge_in_kernel<RG, NW>(P, (long long)blockIdx.x - P.n_split_blocks);
+    return;
+  }
+
   // Workgroup ids are dealt round-robin over the 8 XCDs; remap so that
   // consecutive items (same sequence and KV head, same key split, different
   // row tiles) run on one XCD.
-  const long long nb = gridDim.x;
+  const long long nb = P.n_split_blocks;
   const long long item = (long long)(blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
   if (item >= P.n_items) return;
   const int r = (int)(item % P.R);
   long long t = item / P.R;
-  const int g = (int)(t % P.Hkv);
-  t /= P.Hkv;
-  const int s = (int)(t % P.S);
-  const int b = (int)(t / P.S);
+  int g, s, b;
+  if (P.head_major) {
+    s = (int)(t % P.S);
+    t /= P.S;
+    g = (int)(t % P.Hkv);
+    b = (int)(t / P.Hkv);
+  } else {
+    g = (int)(t % P.Hkv);
+    t /= P.Hkv;
+    s = (int)(t % P.S);
+    b = (int)(t / P.S);
+  }
 
   Seq sq;
   if (!decode_seq(P, b, sq)) return;
@@ -544,14 +723,15 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
       xl[mine * 64 + lane] = l_run;
     }
     __syncthreads();
-    if (!group_active) return;
     const float m1 = xm[other * 64 + lane];
     const float l1 = xl[other * 64 + lane];
     const float mm = fmaxf(m_run, m1);
     const float mu = (mm == kNegInf) ? 0.f : mm;
     const float a0 = fast_exp2((m_run - mu) * c2);
     const float a1 = fast_exp2((m1 - mu) * c2);
-    if (kg == 0) {
+    if (!group_active) {
+      // idle row group: nothing to combine (its outputs are never written)
+    } else if (kg == 0) {
 #pragma unroll
       for (int e2 = 0; e2 < 2; ++e2)
 #pragma unroll
@@ -568,12 +748,12 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
     m_run = mm;
     keep_lo = kg == 0;
     keep_hi = kg == 1;
-  } else {
-    if (!group_active) return;
   }
 
+  // No wave leaves early from here on: with the in-kernel merge every wave
+  // takes part in the arrival barrier below.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!row_ok) return;
+  if (!(group_active && row_ok)) keep_lo = keep_hi = false;
   // Accumulator v of oacc[e] holds dim 32e + 8*(v/4) + 4*hh + v%4 of this row.
   if (rgn.Sb == 1) {
     const float inv = 1.f / l_tot;
@@ -595,9 +775,10 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
   } else {
     // Normalised partial O in bf16 (the merge reweights by l), lane-major so
     // each store instruction writes 512 contiguous bytes.  Streaming stores:
-    // the partials are read once, by the merge kernel, so they should not sit
-    // dirty in L2 when this kernel ends.
+    // the partials are read once (by the merge), so they should not sit dirty
+    // in L2 when this kernel ends.
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    auto put = [&](u32x2_t* p, u32x2_t v) { __builtin_nontemporal_store(v, p); };
     u32x2_t* wo = P.ws_o + ((size_t)item * RG + rg) * 16 * 64 + lane;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -607,24 +788,27 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
         f32x4_t f;
 #pragma unroll
         for (int x = 0; x < 4; ++x) f[x] = oacc[e][4 * j + x] * inv;
-        __builtin_nontemporal_store(
-            __builtin_bit_cast(u32x2_t, __builtin_convertvector(f, bf16x4_t)), &wo[(4 * e + j) * 64]);
+        put(&wo[(4 * e + j) * 64], __builtin_bit_cast(u32x2_t, __builtin_convertvector(f, bf16x4_t)));
       }
     }
     if (hh == 0 && keep_lo)
-      __builtin_nontemporal_store(
-          __builtin_bit_cast(u32x2_t, make_float2(m_run, l_tot)),
-          reinterpret_cast<u32x2_t*>(P.ws_ml + (size_t)item * P.rows_wg + rg * 32 + l32));
+      put(reinterpret_cast<u32x2_t*>(P.ws_ml + (size_t)item * P.rows_wg + rg * 32 + l32),
+          __builtin_bit_cast(u32x2_t, make_float2(m_run, l_tot)));
+    if (P.cnt) {
+      // Arrival: every thread's partial is in this XCD's L2 (its stores are
+      // acknowledged) before the group's counter moves.
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_fetch_add(P.cnt + 2 * (((size_t)b * P.Hkv + g) * P.R + r),
+                               arrival_word(xcc_id()), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
-// Log-sum-exp merge of the splits of one (sequence, KV head, row tile, row
-// group, 32-dim block): split s left its normalised output O_s (bf16), its
-// running max m_s and sum l_s; with M = max_s m_s and
-// w_s = l_s * exp(scale*(m_s - M)),
-//   out = sum_s w_s O_s / sum_s w_s,  lse = scale*M + log(sum_s w_s).
-// Splits that saw no visible key carry m = -inf and weigh nothing.  Thread
-// (wave j, lane) owns dims 32e + 8j + 4*(lane/32) .. +3 of row lane%32.
+// Separate merge kernel: one workgroup per (sequence, KV head, row tile, row
+// group, 32-dim block), wave j = 8-dim slice.
 template <int RG>
 __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
   long long t = blockIdx.x;
@@ -640,8 +824,8 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
   const int j = threadIdx.x >> 6;
   const int hh = lane >> 5;
   const int rl = rg * 32 + (lane & 31);
-  const long long item0 = ((long long)b * P.S * P.Hkv + g) * P.R + r;   // split s adds s*Hkv*R
-  const long long split_stride = (long long)P.Hkv * P.R;
+  const long long item0 = item_index(P, b, g, 0, r);
+  const long long split_stride = item_index(P, b, g, 1, r) - item0;
 
   // The partial slots do not depend on the offsets: issue the loads of the
   // first kMaxS splits before decoding the sequence, so both round trips
@@ -667,37 +851,16 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
   const float c2 = P.scale_log2;
   const int Sb = rgn.Sb;
 
-  float M = kNegInf;
-  float lsum = 0.f;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  auto add = [&](float2 m_l, u32x2_t hv) {
-    const f32x4_t o = {__uint_as_float(hv[0] << 16), __uint_as_float(hv[0] & 0xffff0000u),
-                       __uint_as_float(hv[1] << 16), __uint_as_float(hv[1] & 0xffff0000u)};
-    const float m_new = fmaxf(M, m_l.x);
-    const float mu = (m_new == kNegInf) ? 0.f : m_new;
-    const float a = fast_exp2((M - mu) * c2);
-    const float w = fast_exp2((m_l.x - mu) * c2) * m_l.y;
-    acc = acc * a + w * o;
-    lsum = lsum * a + w;
-    M = m_new;
-  };
+  MergeAcc ma;
 #pragma unroll
   for (int k = 0; k < kMaxS; ++k)
-    if (k < Sb) add(ml[k], h[k]);
+    if (k < Sb) ma.add(ml[k], h[k], c2);
   for (int s = kMaxS; s < Sb; ++s) {
     const long long it = item0 + s * split_stride;
-    add(P.ws_ml[(size_t)it * P.rows_wg + rl],
-        P.ws_o[(((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane]);
+    ma.add(P.ws_ml[(size_t)it * P.rows_wg + rl],
+           P.ws_o[(((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane], c2);
   }
-  const int my_row = r * P.rows_wg + rl;
-  const int node = my_row / P.G;
-  const int head = g * P.G + my_row % P.G;
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  const bf16x4_t h4 = __builtin_convertvector(acc * inv, bf16x4_t);
-  *reinterpret_cast<u32x2_t*>(P.out + ((size_t)(sq.n0 + node) * P.Hq + head) * kD + 32 * e + 8 * j +
-                              4 * hh) = __builtin_bit_cast(u32x2_t, h4);
-  if (P.lse && e == 0 && j == 0 && hh == 0)
-    P.lse[(size_t)(sq.n0 + node) * P.Hq + head] = lsum > 0.f ? M * P.scale + logf(lsum) : kNegInf;
+  store_merged(P, sq, g, r, rl, e, j, hh, ma);
 }
 
 template <int RG, int KG, int TPW, int NS>
@@ -715,6 +878,10 @@ hipError_t launch_shape(const KParams& kp, long long grid, long long merge_grid,
   hipLaunchKernelGGL((merge_bf16_kernel<RG>), dim3((unsigned)merge_grid), dim3(256), 0, stream, kp);
   return hipGetLastError();
 }
+
+// Largest in-kernel merge grid: half of MI355X's 256 CUs (checked against the
+// device's CU count at launch).
+constexpr long long kMaxMergeBlocks = 128;
 
 int pow2_ceil(int x) {
   int p = 1;
@@ -754,7 +921,22 @@ FwdPlan plan_forward_bf16(int B, int total_nodes, int max_nodes, int Hq, int Hkv
   S = std::min<long long>(S, std::max(1, p.tmax / (2 * p.kg)));
   p.S = (int)std::max<long long>(1, S);
   p.n_items = units * p.S;
-  p.ws_bytes = p.S > 1 ? (size_t)p.n_items * p.rows_wg * (kD * 2 + 8) : 0;
+  p.groups = units;
+  p.merge_wpg = 16 / p.kg;   // RG*16 (row group, dim block, slice) units over RG*KG waves
+  // Merge in the same kernel when the merge workgroups are few: they then
+  // never occupy more than half of the CUs, so the splits they wait for
+  // always find room to run.
+  // Each XCD must hold whole (sequence, KV head) blocks of items, and the
+  // arrival word counts at most 127 splits per XCD.
+  p.merge_in_kernel = p.S > 1 && p.S < 128 && p.groups * p.merge_wpg <= kMaxMergeBlocks &&
+                      ((long long)B * Hkv) % 8 == 0;
+  p.ws_bytes = 0;
+  if (p.S > 1) {
+    const size_t partials = (size_t)p.n_items * p.rows_wg * (kD * 2 + 8);
+    p.cnt_off = (partials + 255) / 256 * 256;
+    p.ws_bytes =
+        p.merge_in_kernel ? p.cnt_off + (size_t)p.groups * 2 * sizeof(unsigned long long) : partials;
+  }
   return p;
 }
 
@@ -770,11 +952,22 @@ hipError_t launch_forward_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t s
   kp.mask = a.mask;
   kp.out = static_cast<uint16_t*>(a.out);
   kp.lse = a.lse;
+  long long merge_blocks = 0;
   if (p.S > 1) {
     kp.ws_o = static_cast<u32x2_t*>(a.workspace);
     kp.ws_ml = reinterpret_cast<float2*>(static_cast<unsigned char*>(a.workspace) +
                                          (size_t)p.n_items * p.rows_wg * kD * 2);
+    // The in-kernel merge relies on the 8-XCD round-robin dealing of
+    // MI355X (256 CUs); elsewhere the separate merge kernel runs.
+    if (p.merge_in_kernel && device_cu_count() == 256) {
+      kp.cnt = reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(a.workspace) +
+                                                     p.cnt_off);
+      merge_blocks = p.groups * p.merge_wpg;
+      kp.head_major = 1;
+    }
   }
+  kp.merge_wpg = p.merge_wpg;
+  kp.groups = p.groups;
   kp.total_prefix = a.total_prefix;
   kp.max_prefix = a.max_prefix;
   kp.n_items = p.n_items;
@@ -790,8 +983,10 @@ hipError_t launch_forward_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t s
   kp.tmax = p.tmax;
   kp.scale = a.scale;
   kp.scale_log2 = a.scale * kLog2e;
-  const long long grid = (p.n_items + 7) / 8 * 8;
-  const long long merge_grid = p.S > 1 ? (long long)a.B * a.Hkv * p.R * p.rg * 4 : 0;
+  kp.n_split_blocks = (p.n_items + 7) / 8 * 8;
+  const long long grid = kp.n_split_blocks + merge_blocks;
+  const long long merge_grid =
+      (p.S > 1 && merge_blocks == 0) ? (long long)a.B * a.Hkv * p.R * p.rg * 4 : 0;
   switch (p.rg * 16 + p.kg) {
     // A three-stage ring measured as fast as four on every shape here.
     case 1 * 16 + 2: return launch_shape<1, 2, 1, 3>(kp, grid, merge_grid, stream);

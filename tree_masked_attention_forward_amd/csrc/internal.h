@@ -21,7 +21,11 @@ struct FwdPlan {
   int S;           // key splits for the longest possible tile range
   int tmax;        // that longest range, in 32-key tiles
   long long n_items;   // B * Hkv * S * R
-  size_t ws_bytes;     // partial (O, m, l) storage; 0 when S == 1
+  long long groups;    // B * Hkv * R (sequence, KV head, row tile) groups
+  int merge_wpg;       // merge workgroups per group when the merge runs in-kernel
+  bool merge_in_kernel;  // splits merged by trailing workgroups of the same grid
+  size_t cnt_off;      // byte offset of the per-group counters (in-kernel merge)
+  size_t ws_bytes;     // partial (O, m, l) storage [+ counters]; 0 when S == 1
 };
 
 struct FwdArgs {
@@ -47,6 +51,9 @@ struct FwdArgs {
 // launches after the first make no runtime call here (safe under stream
 // capture once the kernel has run eagerly).
 hipError_t raise_dynamic_lds(const void* kernel, int bytes);
+
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cu_count();
 
 FwdPlan plan_forward_bf16(int B, int total_nodes, int max_nodes, int Hq, int Hkv,
                           long long total_prefix, long long max_prefix);
