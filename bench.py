@@ -1,7 +1,10 @@
 """Benchmark: one verification step of tree attention on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-tree_attn_build_mask -> tree_attn_forward -> tree_verify_greedy.  The default
+the ancestor mask, the attention and the greedy verifier.  By default the mask
+is built inside the forward kernel (tree_attn_mask_and_forward ->
+tree_verify_greedy); --separate-mask runs tree_attn_build_mask ->
+tree_attn_forward -> tree_verify_greedy instead.  The default
 workload is the Llama-3-8B-shaped layer (B=1, Hq=32, Hkv=8, D=128, prefix
 L=4096, a 64-node draft tree of depth <= 6 and branching <= 4, bf16), with
 greedy verification over a 64 x 128256 bf16 logits block (draft token equal to
@@ -46,6 +49,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="llama3_8b")
     p.add_argument("--sets", type=int, default=32)
+    p.add_argument("--separate-mask", action="store_true",
+                   help="build the mask with its own call (tree_attn_build_mask) instead of "
+                        "inside the forward (tree_attn_mask_and_forward)")
     p.add_argument("--eager", action="store_true",
                    help="launch every call from Python instead of replaying captured HIP graphs")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -155,10 +161,12 @@ def summarize_profiles(root):
                  default=None)
     sf = (CALIB_BYTES / 1024) / copy_f if copy_f else 1.0
     sw = (CALIB_BYTES / 1024) / copy_w if copy_w else 1.0
-    groups = {"tree_attn_forward": ("fwd_bf16_kernel", "merge_bf16_kernel"),
+    # The profiled runs take the default step, whose forward call is
+    # tree_attn_mask_and_forward (the mask is built inside the forward kernel).
+    groups = {"tree_attn_mask_and_forward": ("fwd_bf16_kernel", "merge_bf16_kernel"),
               "tree_verify_greedy": ("argmax_partial_kernel", "path_select_kernel"),
               "tree_attn_build_mask": ("build_mask_kernel",)}
-    hashes = {"tree_attn_forward": src_hash("attn_fwd.hip"),
+    hashes = {"tree_attn_mask_and_forward": src_hash("attn_fwd.hip"),
               "tree_verify_greedy": src_hash("verify.hip"),
               "tree_attn_build_mask": src_hash("mask_build.hip")}
     rec = {"calibration": {"copy_bytes": CALIB_BYTES, "fetch_kib": copy_f, "write_kib": copy_w,
@@ -266,16 +274,32 @@ def main():
         ta.forward(s["q"], s["kt"], s["vt"], s["kp"], s["vp"], s["poffs"], s["noffs"], mask,
                    max_nodes, max_prefix, case.scale, out=out, workspace=fws)
 
+    def do_mask_forward(s):
+        ta.mask_and_forward(s["parents"], s["q"], s["kt"], s["vt"], s["kp"], s["vp"], s["poffs"],
+                            s["noffs"], max_nodes, max_prefix, case.scale, out=out, mask=mask,
+                            depth=depth, status=status, workspace=fws)
+
     def do_verify(s):
         ta.verify_greedy(s["logits"], s["draft"], mask, s["noffs"], max_nodes, workspace=vws,
                          target_argmax=pred, accept_len=alen, accept_nodes=anodes,
                          accept_tokens=atok)
 
+    # A step: the ancestor mask (a1), the attention (a2-a4) and the greedy verifier (a5-a6).
+    # By default the mask is built inside the forward kernel (one launch fewer).
+    if args.separate_mask:
+        calls = [("tree_attn_build_mask", do_mask), ("tree_attn_forward", do_forward),
+                 ("tree_verify_greedy", do_verify)]
+    else:
+        calls = [("tree_attn_mask_and_forward", do_mask_forward),
+                 ("tree_verify_greedy", do_verify)]
+    fwd_call, fwd_fn = calls[-2]
+
+    def one_step(s):
+        for _, fn in calls:
+            fn(s)
+
     def step(i):
-        s = sets[i % len(sets)]
-        do_mask(s)
-        do_forward(s)
-        do_verify(s)
+        one_step(sets[i % len(sets)])
 
     # --- HIP graphs ------------------------------------------------------------------------
     # The Python binding costs tens of microseconds of host time per call, about as
@@ -299,7 +323,6 @@ def main():
 
     use_graphs = not args.eager
     n_rot = len(sets)
-    one_step = lambda s: (do_mask(s), do_forward(s), do_verify(s))
     if use_graphs:
         # A graph launch itself costs host time comparable to a step, so one graph holds
         # the steps of all rotation sets in order; single-step graphs cover the rest.
@@ -370,7 +393,7 @@ def main():
 
     do_mask(sets[0])
     t_mask = event_time(do_mask, args.steps)
-    t_fwd = event_time(do_forward, args.steps)
+    t_fwd = event_time(fwd_fn, args.steps)
     t_ver = event_time(do_verify, args.steps)
     print(f"[bench] per call us: mask {t_mask:.2f} forward {t_fwd:.2f} verify {t_ver:.2f}",
           file=sys.stderr, flush=True)
@@ -379,6 +402,8 @@ def main():
     depth_h = depth.cpu().numpy().astype(np.int64)
     kv_bytes = 2 * sum_l * Hkv * D * 2 + 2 * sum_n * Hkv * D * 2
     fwd_bytes = kv_bytes + 2 * sum_n * Hq * D * 2 + sum_n * W * 8
+    if not args.separate_mask:
+        fwd_bytes += sum_n * 4 + sum_n * 4 + B * 4   # parents in; depth and status out
     lens = np.diff(case.prefix_offsets).astype(np.int64)
     nn = np.diff(case.node_offsets).astype(np.int64)
     fwd_flops = 4 * Hq * D * (int((nn * lens).sum()) + int((depth_h + 1).sum()))
@@ -400,8 +425,8 @@ def main():
             else:
                 r = {"bound": "mfma", "achieved": round(fwd_tfs, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
-            r["traffic"] = load_traffic("tree_attn_forward", fwd_hash)
-            r["kernel"] = "tree_attn_forward"
+            r["traffic"] = load_traffic(fwd_call, fwd_hash)
+            r["kernel"] = fwd_call
             return r
         r = {"bound": "hbm", "achieved": round(ver_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
              "frac": round(ver_gbs / HBM_PEAK_GBS, 4),
@@ -432,7 +457,7 @@ def main():
         "config": {
             "workload": f"{args.config}: B={B} Hq={Hq} Hkv={Hkv} D={D} L={max_prefix} N={max_nodes} "
                         f"(sum_L={sum_l}, sum_N={sum_n}); greedy verify over V={V} bf16 logits",
-            "step": "build_mask + forward + verify_greedy, inputs rotated over "
+            "step": " + ".join(n for n, _ in calls) + ", inputs rotated over "
                     f"{len(sets)} resident copies of {set_bytes / 2**20:.1f} MiB, "
                     + ("replayed from captured HIP graphs (one per round over the copies)"
                        if use_graphs else "launched eagerly from Python"),
@@ -441,8 +466,8 @@ def main():
         "roofline": roof(dominant),
         "cpu_baseline": cpu,
         "detail": {
-            "us_per_call": {"build_mask": round(t_mask, 3), "forward": round(t_fwd, 3),
-                            "verify": round(t_ver, 3)},
+            "us_per_call": {fwd_call: round(t_fwd, 3), "tree_verify_greedy": round(t_ver, 3),
+                            "tree_attn_build_mask (standalone)": round(t_mask, 3)},
             "forward": {"tree_tokens_per_s": round(sum_n / (t_fwd * 1e-6), 1),
                         "kv_GBps": round(kv_bytes / (t_fwd * 1e-6) / 1e9, 1),
                         "alg_GBps": round(fwd_gbs, 1), "alg_TFLOPs": round(fwd_tfs, 2),

@@ -128,16 +128,18 @@ TA_API size_t tree_attn_forward_workspace_size(int dtype, int32_t B, int32_t tot
  *   out            out [sum_N][Hq][D], dtype as the inputs.
  *   lse            out fp32 [sum_N][Hq], nullable.
  *   workspace      device buffer of at least tree_attn_forward_workspace_size()
- *                  bytes (may be NULL when that size is 0).  It must be
- *                  zero-filled before its first use; every call that runs to
- *                  completion leaves it ready for the next call (a few
- *                  per-group counters, used when the splits of the key range
- *                  are merged inside the same kernel, return to zero; the
- *                  rest is scratch).  A workspace whose counters are not zero
- *                  does not hang a call: the affected outputs are written as
- *                  NaN after a bounded wait (about 0.3 s) and the counters
- *                  are zeroed for the next call.  Calls sharing one
- *                  workspace must be ordered on one stream.
+ *                  bytes (may be NULL when that size is 0), 16-byte aligned.
+ *                  It must be zero-filled before its first use.  Its first
+ *                  2 KiB hold per-group counters, used when the splits of the
+ *                  key range are merged inside the same kernel; every call
+ *                  that runs to completion leaves them at zero, whatever its
+ *                  shape, and the rest is scratch, so one buffer (of the
+ *                  largest size needed) serves calls of any shapes.  A
+ *                  workspace whose counters are not zero does not hang a
+ *                  call: the affected outputs are written as NaN after a
+ *                  bounded wait (about 0.3 s) and the counters are zeroed for
+ *                  the next call.  Calls sharing one workspace must be ordered
+ *                  on one stream.
  */
 TA_API int tree_attn_forward(int dtype, const void* q, const void* k_tree, const void* v_tree,
                       const void* k_prefix, const void* v_prefix,
@@ -146,6 +148,40 @@ TA_API int tree_attn_forward(int dtype, const void* q, const void* k_tree, const
                       int64_t total_prefix, int64_t max_prefix, int32_t Hq, int32_t Hkv,
                       int32_t D, float scale, void* out, float* lse, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * Ancestor mask and tree attention in one call: the same results as
+ * tree_attn_build_mask(parents, node_offsets, B, total_nodes, max_nodes, mask,
+ * depth, tree_status) followed by tree_attn_forward(..., mask, ...) with the
+ * other arguments unchanged.  For bf16 inputs and max_nodes <= 128 it is one
+ * kernel launch: each forward workgroup builds the ancestor rows of its own
+ * nodes from the parents (while its first K/V tiles load) and keeps them in
+ * registers, and one workgroup per row tile writes mask, depth and status for
+ * tree_verify_greedy; otherwise it runs the two calls in order.
+ *
+ * Follows: inferensys "Tree Attention", Modified Causal Attention Mask (the
+ * mask is the ancestor relation of the parent array) and Batched Parallel
+ * Verification (one pass scores every node).
+ *
+ *   parents        int32 [sum_N], as for tree_attn_build_mask.
+ *   mask           out uint64 [sum_N][W], W = ceil(max_nodes / 64).
+ *   depth          out int32 [sum_N], nullable.
+ *   tree_status    out int32 [B], nullable: 0 ok, 1 offsets out of range,
+ *                  2 invalid parent (that sequence's rows are all zero).
+ *   everything else as for tree_attn_forward (workspace: the same size query,
+ *                  the same zero-filled requirement).
+ * Returns the first non-OK status of the checks of either call.
+ */
+TA_API int tree_attn_mask_and_forward(int dtype, const int32_t* parents, const void* q,
+                                      const void* k_tree, const void* v_tree,
+                                      const void* k_prefix, const void* v_prefix,
+                                      const int64_t* prefix_offsets, const int32_t* node_offsets,
+                                      int32_t B, int32_t total_nodes, int32_t max_nodes,
+                                      int64_t total_prefix, int64_t max_prefix, int32_t Hq,
+                                      int32_t Hkv, int32_t D, float scale, uint64_t* mask,
+                                      int32_t* depth, int32_t* tree_status, void* out,
+                                      float* lse, void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /*
  * Bytes of device workspace tree_verify_greedy needs.  Pure host arithmetic.

@@ -23,9 +23,10 @@ def lib():
 
 def test_header_declares_the_three_calls():
     names = _declared_functions()
-    for n in ("tree_attn_build_mask", "tree_attn_forward", "tree_verify_greedy"):
+    for n in ("tree_attn_build_mask", "tree_attn_forward", "tree_verify_greedy",
+              "tree_attn_mask_and_forward"):
         assert n in names
-    assert len(names) == 6, names
+    assert len(names) == 7, names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -94,3 +95,28 @@ def test_build_mask_and_verify_host_validation(lib):
     assert v(*no_len) == 1
     big = list(ok); big[7] = 5000
     assert v(*big) == 3
+
+
+def _mfwd(lib, **kw):
+    args = dict(dtype=1, par=1 << 20, q=1 << 20, kt=1 << 20, vt=1 << 20, kp=1 << 20, vp=1 << 20,
+                po=1 << 20, no=1 << 20, B=1, total=64, maxn=64, tp=4096, mp=4096, Hq=32, Hkv=8,
+                D=128, scale=0.088, mask=1 << 20, depth=None, status=None, out=1 << 20, lse=None,
+                ws=None, wsb=0, stream=None)
+    args.update(kw)
+    a = args
+    return lib.tree_attn_mask_and_forward(
+        a["dtype"], a["par"], a["q"], a["kt"], a["vt"], a["kp"], a["vp"], a["po"], a["no"],
+        a["B"], a["total"], a["maxn"], a["tp"], a["mp"], a["Hq"], a["Hkv"], a["D"], a["scale"],
+        a["mask"], a["depth"], a["status"], a["out"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_mask_and_forward_host_validation(lib):
+    assert _mfwd(lib, dtype=7) == 3
+    assert _mfwd(lib, Hq=30, Hkv=8) == 1
+    assert _mfwd(lib, maxn=2000) == 3
+    assert _mfwd(lib, q=None) == 1
+    assert _mfwd(lib, par=None) == 1               # parents are required
+    assert _mfwd(lib, mask=None) == 1              # the mask is an output here
+    assert _mfwd(lib, ws=None, wsb=0) == 4         # split partials need a workspace
+    assert _mfwd(lib, maxn=200, ws=None, wsb=0) == 4   # two-call path checks it too
+    assert _mfwd(lib, total=0) == 0                # nothing to do, nothing launched

@@ -18,7 +18,8 @@ pytestmark = pytest.mark.gpu
 # Two sequences (splits merged by a separate kernel) and one sequence (splits
 # merged inside the forward kernel, through counters in the workspace).
 SHAPES = {"two_sequences": ([700, 2001], [(64, 1, 6, 4), (37, 2, 5, None)]),
-          "one_sequence": ([3000], [(64, 1, 6, 4)])}
+          "one_sequence": ([3000], [(64, 1, 6, 4)]),
+          "one_sequence_fused_mask": ([3000], [(64, 1, 6, 4)])}
 
 
 def _inputs(seed, shape):
@@ -65,12 +66,20 @@ def test_step_graph_replays_match_eager(shape):
     vws = torch.empty(max(ta.verify_workspace_size(n, max_nodes, 5000), 16), dtype=torch.uint8,
                       device=d)
 
+    fused = shape.endswith("fused_mask")
+
     def step(t, c):
-        ta.build_mask(t["parents"], t["noffs"], max_nodes, mask=bufs["mask"],
-                      depth=bufs["depth"], status=bufs["status"])
-        ta.forward(t["q"], t["kt"], t["vt"], t["kp"], t["vp"], t["poffs"], t["noffs"],
-                   bufs["mask"], max_nodes, c.max_prefix, c.scale, out=bufs["out"],
-                   lse=bufs["lse"], workspace=fws)
+        if fused:
+            ta.mask_and_forward(t["parents"], t["q"], t["kt"], t["vt"], t["kp"], t["vp"],
+                                t["poffs"], t["noffs"], max_nodes, c.max_prefix, c.scale,
+                                out=bufs["out"], lse=bufs["lse"], mask=bufs["mask"],
+                                depth=bufs["depth"], status=bufs["status"], workspace=fws)
+        else:
+            ta.build_mask(t["parents"], t["noffs"], max_nodes, mask=bufs["mask"],
+                          depth=bufs["depth"], status=bufs["status"])
+            ta.forward(t["q"], t["kt"], t["vt"], t["kp"], t["vp"], t["poffs"], t["noffs"],
+                       bufs["mask"], max_nodes, c.max_prefix, c.scale, out=bufs["out"],
+                       lse=bufs["lse"], workspace=fws)
         ta.verify_greedy(t["logits"], t["draft"], bufs["mask"], t["noffs"], max_nodes,
                          workspace=vws, target_argmax=bufs["pred"], accept_len=bufs["alen"],
                          accept_nodes=bufs["anodes"], accept_tokens=bufs["atok"])

@@ -1,9 +1,11 @@
 """The split merge that runs inside the forward kernel (few sequence x KV
-head x row-tile groups, as in the 8B-shaped layer) keeps per-group counters in
-the caller's workspace and returns them to zero: one workspace serves many
-calls, and a workspace whose counters were not zero still gives the right
-answer after a bounded wait."""
+head x row-tile groups, as in the 8B-shaped layer) keeps per-group counters at
+the start of the caller's workspace and returns them to zero: one workspace
+serves many calls, also of different shapes, and a workspace whose counters
+were not zero gives NaN after a bounded wait, then is right again."""
 from __future__ import annotations
+
+import time
 
 import numpy as np
 import pytest
@@ -73,3 +75,28 @@ def test_in_kernel_merge_with_nonzero_workspace_fails_loudly_then_recovers():
     assert torch.equal(o[~bad], ref_o[~bad]), "finite outputs must be the right ones"
     o, l = _forward(ta, dc, mask, dirty)
     assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
+def test_workspace_shared_across_shapes():
+    """A call of another shape (its splits merged by the separate kernel, its
+    partials larger) on the same buffer leaves the counters at zero, so the
+    in-kernel merge that follows needs no wait and gives the same bits."""
+    ta = lib()
+    ca = config_case("llama3_8b")
+    da, ma, na = _setup(ta, ca)
+    cb = config_case("batched")
+    db, mb, nb = _setup(ta, cb)
+    ws = torch.zeros(max(na, nb), dtype=torch.uint8, device="cuda")
+    oa, la = _forward(ta, da, ma, ws)
+    oa, la = oa.clone(), la.clone()
+    ob, lb = _forward(ta, db, mb, ws)
+    ob, lb = ob.clone(), lb.clone()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    o, l = _forward(ta, da, ma, ws)
+    torch.cuda.synchronize()
+    assert time.perf_counter() - t0 < 0.1, "the in-kernel merge waited out its bound"
+    assert torch.equal(o, oa) and torch.equal(l, la)
+    o, l = _forward(ta, db, mb, ws)
+    assert torch.equal(o, ob) and torch.equal(l, lb)
+    assert torch.isfinite(oa.float()).all() and torch.isfinite(ob.float()).all()

@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     forward,
     forward_workspace_size,
     load_library,
+    mask_and_forward,
     mask_words,
     status_string,
     verify_greedy,
@@ -32,4 +33,5 @@ load_library()
 # The C names, for readers who know the ABI.
 tree_attn_build_mask = build_mask
 tree_attn_forward = forward
+tree_attn_mask_and_forward = mask_and_forward
 tree_verify_greedy = verify_greedy

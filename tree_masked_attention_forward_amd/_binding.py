@@ -62,6 +62,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tree_attn_forward.argtypes = [ctypes.c_int] + [_c_void_p] * 8 + [
         _i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32, ctypes.c_float, _c_void_p, _c_void_p,
         _c_void_p, ctypes.c_size_t, _c_void_p]
+    lib.tree_attn_mask_and_forward.restype = ctypes.c_int
+    lib.tree_attn_mask_and_forward.argtypes = [ctypes.c_int] + [_c_void_p] * 8 + [
+        _i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32, ctypes.c_float] + [_c_void_p] * 6 + [
+        ctypes.c_size_t, _c_void_p]
     lib.tree_verify_greedy_workspace_size.restype = ctypes.c_size_t
     lib.tree_verify_greedy_workspace_size.argtypes = [_i32, _i32, _i32]
     lib.tree_verify_greedy.restype = ctypes.c_int
@@ -146,12 +150,10 @@ def forward_workspace_size(dtype: torch.dtype, B: int, total_nodes: int, max_nod
         code, B, total_nodes, max_nodes, Hq, Hkv, D, total_prefix, max_prefix))
 
 
-def forward(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor,
-            k_prefix: torch.Tensor, v_prefix: torch.Tensor, prefix_offsets: torch.Tensor,
-            node_offsets: torch.Tensor, mask: torch.Tensor, max_nodes: int, max_prefix: int,
-            scale: float, *, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-            return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
-    """tree_attn_forward.  Returns out (and lse when asked or given)."""
+def _forward_args(q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets, node_offsets,
+                  max_nodes, max_prefix, out, lse, return_lse, workspace):
+    """Checks shared by forward() and mask_and_forward(); allocates outputs and
+    the (zero-filled) workspace when they are not given."""
     dev = _device_of(q)
     dtype = q.dtype
     if dtype not in (torch.bfloat16, torch.float32):
@@ -170,12 +172,9 @@ def forward(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor,
         raise ValueError("k_prefix/v_prefix must be [sum_L, Hkv, D]")
     _need(prefix_offsets, "prefix_offsets", torch.int64, dev, 1)
     _need(node_offsets, "node_offsets", torch.int32, dev, 1)
-    _need(mask, "mask", torch.uint64, dev, 2)
     B = node_offsets.numel() - 1
     if prefix_offsets.numel() != B + 1:
         raise ValueError("prefix_offsets and node_offsets must both hold B+1 entries")
-    if mask.shape != (total, mask_words(max_nodes)):
-        raise ValueError("mask must be [sum_N, ceil(max_nodes/64)]")
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", dtype, dev, 3)
@@ -193,12 +192,64 @@ def forward(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor,
         workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     code = TA_BF16 if dtype == torch.bfloat16 else TA_F32
+    return dict(dev=dev, code=code, B=B, total=total, Hq=Hq, Hkv=Hkv, D=D,
+                total_prefix=total_prefix, out=out, lse=lse, workspace=workspace, ws_len=ws_len)
+
+
+def forward(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor,
+            k_prefix: torch.Tensor, v_prefix: torch.Tensor, prefix_offsets: torch.Tensor,
+            node_offsets: torch.Tensor, mask: torch.Tensor, max_nodes: int, max_prefix: int,
+            scale: float, *, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+            return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
+    """tree_attn_forward.  Returns out (and lse when asked or given).  A
+    workspace passed in must have been zero-filled before its first use."""
+    a = _forward_args(q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets, node_offsets,
+                      max_nodes, max_prefix, out, lse, return_lse, workspace)
+    _need(mask, "mask", torch.uint64, a["dev"], 2)
+    if mask.shape != (a["total"], mask_words(max_nodes)):
+        raise ValueError("mask must be [sum_N, ceil(max_nodes/64)]")
     _check("tree_attn_forward", load_library().tree_attn_forward(
-        code, _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_prefix), _ptr(v_prefix),
-        _ptr(prefix_offsets), _ptr(node_offsets), _ptr(mask), B, total, int(max_nodes),
-        total_prefix, int(max_prefix), Hq, Hkv, D, float(scale), _ptr(out), _ptr(lse),
-        _ptr(workspace), ws_len, _stream(dev)))
-    return (out, lse) if (return_lse or lse is not None) else out
+        a["code"], _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_prefix), _ptr(v_prefix),
+        _ptr(prefix_offsets), _ptr(node_offsets), _ptr(mask), a["B"], a["total"], int(max_nodes),
+        a["total_prefix"], int(max_prefix), a["Hq"], a["Hkv"], a["D"], float(scale),
+        _ptr(a["out"]), _ptr(a["lse"]), _ptr(a["workspace"]), a["ws_len"], _stream(a["dev"])))
+    return (a["out"], a["lse"]) if (return_lse or lse is not None) else a["out"]
+
+
+def mask_and_forward(parents: torch.Tensor, q: torch.Tensor, k_tree: torch.Tensor,
+                     v_tree: torch.Tensor, k_prefix: torch.Tensor, v_prefix: torch.Tensor,
+                     prefix_offsets: torch.Tensor, node_offsets: torch.Tensor, max_nodes: int,
+                     max_prefix: int, scale: float, *, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, return_lse: bool = False,
+                     mask: Optional[torch.Tensor] = None, depth: Optional[torch.Tensor] = None,
+                     status: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """tree_attn_mask_and_forward: the ancestor mask and the attention in one
+    call.  Returns (out, [lse,] mask, depth, status)."""
+    a = _forward_args(q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets, node_offsets,
+                      max_nodes, max_prefix, out, lse, return_lse, workspace)
+    dev, total, B = a["dev"], a["total"], a["B"]
+    _need(parents, "parents", torch.int32, dev, 1)
+    if parents.numel() != total:
+        raise ValueError("parents must hold one entry per tree node")
+    W = mask_words(max_nodes)
+    if mask is None:
+        mask = torch.empty((total, W), dtype=torch.uint64, device=dev)
+    if depth is None:
+        depth = torch.empty(total, dtype=torch.int32, device=dev)
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(mask, "mask", torch.uint64, dev, 2)
+    if tuple(mask.shape) != (total, W):
+        raise ValueError(f"mask must be [{total}, {W}]")
+    _check("tree_attn_mask_and_forward", load_library().tree_attn_mask_and_forward(
+        a["code"], _ptr(parents), _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_prefix),
+        _ptr(v_prefix), _ptr(prefix_offsets), _ptr(node_offsets), B, total, int(max_nodes),
+        a["total_prefix"], int(max_prefix), a["Hq"], a["Hkv"], a["D"], float(scale), _ptr(mask),
+        _ptr(depth), _ptr(status), _ptr(a["out"]), _ptr(a["lse"]), _ptr(a["workspace"]),
+        a["ws_len"], _stream(dev)))
+    head = (a["out"], a["lse"]) if (return_lse or lse is not None) else (a["out"],)
+    return head + (mask, depth, status)
 
 
 def verify_workspace_size(total_nodes: int, max_nodes: int, V: int) -> int:

@@ -92,13 +92,20 @@ size_t tree_attn_forward_workspace_size(int dtype, int32_t B, int32_t total_node
       .ws_bytes;
 }
 
-int tree_attn_forward(int dtype, const void* q, const void* k_tree, const void* v_tree,
-                      const void* k_prefix, const void* v_prefix,
-                      const int64_t* prefix_offsets, const int32_t* node_offsets,
-                      const uint64_t* mask, int32_t B, int32_t total_nodes, int32_t max_nodes,
-                      int64_t total_prefix, int64_t max_prefix, int32_t Hq, int32_t Hkv,
-                      int32_t D, float scale, void* out, float* lse, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Host checks shared by tree_attn_forward and tree_attn_mask_and_forward.
+// Returns TA_OK with `a` filled (mask left null), or the status to return.
+// `empty` is set when there is nothing to compute (total_nodes == 0).
+int check_forward(int dtype, const void* q, const void* k_tree, const void* v_tree,
+                  const void* k_prefix, const void* v_prefix, const int64_t* prefix_offsets,
+                  const int32_t* node_offsets, int32_t B, int32_t total_nodes, int32_t max_nodes,
+                  int64_t total_prefix, int64_t max_prefix, int32_t Hq, int32_t Hkv, int32_t D,
+                  float scale, void* out, float* lse, void* workspace, ta::FwdArgs& a,
+                  bool& empty) {
+  empty = false;
   if (dtype != TA_BF16 && dtype != TA_F32) return TA_ERR_UNSUPPORTED;
   if (B <= 0 || total_nodes < 0 || max_nodes < 1 || Hq <= 0 || Hkv <= 0 || D <= 0 ||
       total_prefix < 0 || max_prefix < 0 || max_prefix > total_prefix)
@@ -109,8 +116,11 @@ int tree_attn_forward(int dtype, const void* q, const void* k_tree, const void* 
   if (dtype == TA_BF16 && D != 128) return TA_ERR_UNSUPPORTED;
   if (dtype == TA_F32 && D > kMaxF32HeadDim) return TA_ERR_UNSUPPORTED;
   if (!prefix_offsets || !node_offsets) return TA_ERR_INVALID_ARG;
-  if (total_nodes == 0) return TA_OK;
-  if (!q || !k_tree || !v_tree || !mask || !out) return TA_ERR_INVALID_ARG;
+  if (total_nodes == 0) {
+    empty = true;
+    return TA_OK;
+  }
+  if (!q || !k_tree || !v_tree || !out) return TA_ERR_INVALID_ARG;
   if (total_prefix > 0 && (!k_prefix || !v_prefix)) return TA_ERR_INVALID_ARG;
   if (dtype == TA_BF16 &&
       (misaligned16(q) || misaligned16(k_tree) || misaligned16(v_tree) ||
@@ -120,8 +130,7 @@ int tree_attn_forward(int dtype, const void* q, const void* k_tree, const void* 
   // and row counts their 32-bit node/row indices.
   if ((long long)max_nodes * (Hq / Hkv) > (1LL << 30) || total_prefix > (1LL << 40))
     return TA_ERR_UNSUPPORTED;
-
-  ta::FwdArgs a{};
+  a = ta::FwdArgs{};
   a.q = q;
   a.k_tree = k_tree;
   a.v_tree = v_tree;
@@ -129,7 +138,6 @@ int tree_attn_forward(int dtype, const void* q, const void* k_tree, const void* 
   a.v_prefix = v_prefix;
   a.prefix_offsets = prefix_offsets;
   a.node_offsets = node_offsets;
-  a.mask = mask;
   a.B = B;
   a.total_nodes = total_nodes;
   a.max_nodes = max_nodes;
@@ -143,14 +151,86 @@ int tree_attn_forward(int dtype, const void* q, const void* k_tree, const void* 
   a.out = out;
   a.lse = lse;
   a.workspace = workspace;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == TA_F32) return hip_status(ta::launch_forward_f32(a, s));
+  return TA_OK;
+}
 
-  const ta::FwdPlan p =
-      ta::plan_forward_bf16(B, total_nodes, max_nodes, Hq, Hkv, total_prefix, max_prefix);
-  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes || misaligned16(workspace)))
+int run_forward(int dtype, const ta::FwdArgs& a, size_t workspace_bytes, hipStream_t s) {
+  if (dtype == TA_F32) return hip_status(ta::launch_forward_f32(a, s));
+  const ta::FwdPlan p = ta::plan_forward_bf16(a.B, a.total_nodes, a.max_nodes, a.Hq, a.Hkv,
+                                              a.total_prefix, a.max_prefix);
+  if (p.ws_bytes > 0 &&
+      (!a.workspace || workspace_bytes < p.ws_bytes || misaligned16(a.workspace)))
     return TA_ERR_WORKSPACE;
   return hip_status(ta::launch_forward_bf16(a, p, s));
+}
+
+// Largest tree the forward kernel builds its own mask for (rows in registers).
+constexpr int kFusedMaskMaxNodes = 128;
+
+}  // namespace
+
+extern "C" {
+
+int tree_attn_forward(int dtype, const void* q, const void* k_tree, const void* v_tree,
+                      const void* k_prefix, const void* v_prefix,
+                      const int64_t* prefix_offsets, const int32_t* node_offsets,
+                      const uint64_t* mask, int32_t B, int32_t total_nodes, int32_t max_nodes,
+                      int64_t total_prefix, int64_t max_prefix, int32_t Hq, int32_t Hkv,
+                      int32_t D, float scale, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  ta::FwdArgs a;
+  bool empty = false;
+  const int st = check_forward(dtype, q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets,
+                               node_offsets, B, total_nodes, max_nodes, total_prefix, max_prefix,
+                               Hq, Hkv, D, scale, out, lse, workspace, a, empty);
+  if (st != TA_OK || empty) return st;
+  if (!mask) return TA_ERR_INVALID_ARG;
+  a.mask = mask;
+  return run_forward(dtype, a, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int tree_attn_mask_and_forward(int dtype, const int32_t* parents, const void* q,
+                               const void* k_tree, const void* v_tree, const void* k_prefix,
+                               const void* v_prefix, const int64_t* prefix_offsets,
+                               const int32_t* node_offsets, int32_t B, int32_t total_nodes,
+                               int32_t max_nodes, int64_t total_prefix, int64_t max_prefix,
+                               int32_t Hq, int32_t Hkv, int32_t D, float scale, uint64_t* mask,
+                               int32_t* depth, int32_t* tree_status, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  ta::FwdArgs a;
+  bool empty = false;
+  const int st = check_forward(dtype, q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets,
+                               node_offsets, B, total_nodes, max_nodes, total_prefix, max_prefix,
+                               Hq, Hkv, D, scale, out, lse, workspace, a, empty);
+  if (st != TA_OK) return st;
+  if (empty) {
+    if (tree_status && B > 0)   // same as tree_attn_build_mask on zero nodes
+      return hip_status(ta::launch_build_mask(parents, node_offsets, B, total_nodes, max_nodes,
+                                              mask, depth, tree_status,
+                                              static_cast<hipStream_t>(stream)));
+    return TA_OK;
+  }
+  if (!parents || !mask) return TA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == TA_BF16 && max_nodes <= kFusedMaskMaxNodes) {
+    a.build_mask = true;
+    a.parents = parents;
+    a.mask_out = mask;
+    a.depth_out = depth;
+    a.status_out = tree_status;
+    return run_forward(dtype, a, workspace_bytes, s);
+  }
+  // Larger trees (or fp32): the mask builder, then the forward.
+  const ta::FwdPlan p = ta::plan_forward_bf16(B, total_nodes, max_nodes, Hq, Hkv, total_prefix,
+                                              max_prefix);
+  if (dtype == TA_BF16 && p.ws_bytes > 0 &&
+      (!workspace || workspace_bytes < p.ws_bytes || misaligned16(workspace)))
+    return TA_ERR_WORKSPACE;
+  const int ms = hip_status(ta::launch_build_mask(parents, node_offsets, B, total_nodes,
+                                                  max_nodes, mask, depth, tree_status, s));
+  if (ms != TA_OK) return ms;
+  a.mask = mask;
+  return run_forward(dtype, a, workspace_bytes, s);
 }
 
 size_t tree_verify_greedy_workspace_size(int32_t total_nodes, int32_t max_nodes, int32_t V) {

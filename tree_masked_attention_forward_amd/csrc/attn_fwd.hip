@@ -82,9 +82,16 @@ struct KParams {
   const uint16_t* v_prefix;
   const int64_t* prefix_offsets;
   const int32_t* node_offsets;
-  const uint64_t* mask;
+  const uint64_t* mask;      // ancestor rows (null when the kernel builds them)
   uint16_t* out;
   float* lse;
+  // Mask built in the kernel (tree_attn_mask_and_forward): parents in, rows,
+  // depths and per-sequence status out.
+  const int32_t* parents;
+  uint64_t* mask_out;
+  int32_t* depth_out;
+  int32_t* status_out;
+  int build;
   u32x2_t* ws_o;   // [n_items][RG][16][64] 4 x bf16: O / l in register layout
   float2* ws_ml;   // [n_items][rows_wg]   (running max in score units, sum)
   // In-kernel merge: per (sequence, KV head, row tile) group, the number of
@@ -338,29 +345,34 @@ __device__ void merge_in_kernel(const KParams& P, long long m) {
 }
 
 // LDS map of one workgroup: a ring of NS stages, each KG*TPW x (K tile,
-// V tile) followed by TPW mask dwords per lane per wave, and the workgroup's
-// query rows (32*RG rows, laid out like a K tile).  The query block sits
-// after the ring when both fit, otherwise over the last ring slot, which is
-// first written only after every wave has copied its rows to registers.
-template <int RG, int KG, int TPW, int NS>
+// V tile), followed (when the mask rows are not held in registers, MR false)
+// by TPW mask dwords per lane per wave; the workgroup's query rows (32*RG
+// rows, laid out like a K tile); and, with MR, a small block for the lanes'
+// mask words or the sequence's parents.  The query block sits after the ring
+// when it fits, otherwise over the last ring slot, which is first written
+// only after every wave has copied its rows to registers.
+template <int RG, int KG, int TPW, int NS, bool MR>
 struct LdsMap {
   static constexpr int kMaskOff = KG * TPW * kTileBytes;
-  static constexpr int kStage = kMaskOff + RG * KG * TPW * 256;
+  static constexpr int kStage = kMaskOff + (MR ? 0 : RG * KG * TPW * 256);
   static constexpr int kRing = NS * kStage;
   static constexpr int kQBytes = RG * 32 * kRow;
-  static constexpr bool kQAlias = kRing + kQBytes > kLdsMax;
+  static constexpr int kAuxBytes = MR ? RG * KG * 1024 : 0;   // 4 dwords per lane per wave
+  static constexpr bool kQAlias = kRing + kQBytes + kAuxBytes > kLdsMax;
   static constexpr int kQOff = kQAlias ? (NS - 1) * kStage : kRing;
-  static constexpr int kBytes = kQOff + kQBytes > kRing ? kQOff + kQBytes : kRing;
+  static constexpr int kQEnd = kQOff + kQBytes > kRing ? kQOff + kQBytes : kRing;
+  static constexpr int kAuxOff = kQEnd;
+  static constexpr int kBytes = kQEnd + kAuxBytes;
   static_assert(kBytes <= kLdsMax, "LDS budget");
 };
 
-template <int RG, int KG, int TPW, int NS>
+template <int RG, int KG, int TPW, int NS, bool MR>
 __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
   static_assert(NS >= 3 && NS <= 4, "ring depth");
   constexpr int NW = RG * KG;
   constexpr int NT = NW * 64;
   constexpr int kTilesPerStage = KG * TPW;
-  using Map = LdsMap<RG, KG, TPW, NS>;
+  using Map = LdsMap<RG, KG, TPW, NS, MR>;
   constexpr int kMaskOff = Map::kMaskOff;
   constexpr int kStage = Map::kStage;
   extern __shared__ __align__(16) unsigned char lds[];
@@ -402,7 +414,11 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
   }
 
   Seq sq;
-  if (!decode_seq(P, b, sq)) return;
+  if (!decode_seq(P, b, sq)) {
+    if (P.build && P.status_out && g == 0 && s == 0 && r == 0 && tid == 0)
+      P.status_out[b] = TA_ERR_INVALID_ARG;
+    return;
+  }
   Range rgn;
   if (!row_tile_range(P, sq, r, rgn)) return;
   if (s >= rgn.Sb) return;
@@ -459,7 +475,7 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
   constexpr int kRowsPerPass = NT / 16;
   constexpr int kPasses = kKT / kRowsPerPass;   // per tile and per K/V
   static_assert(kPasses * kRowsPerPass == kKT, "tile rows must split evenly");
-  constexpr int kLoads = kTilesPerStage * 2 * kPasses + TPW;
+  constexpr int kLoads = kTilesPerStage * 2 * kPasses + (MR ? 0 : TPW);
   static_assert(kLoads <= 63, "vmcnt range");
   const int ld_key = tid >> 4;
   const int ld_slot = tid & 15;
@@ -477,8 +493,9 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
     pv[u] = vp + (size_t)row * kv_row + ((ld_slot ^ ((row & 3) << 2)) << 3);
   }
   const int L_full = L / kKT;                         // tiles entirely inside the prefix
-  const uint32_t* mrow_dw = reinterpret_cast<const uint32_t*>(
-      P.mask + (size_t)(sq.n0 + (row_ok ? node : 0)) * P.W);
+  const uint32_t* mrow_dw =
+      P.mask ? reinterpret_cast<const uint32_t*>(P.mask + (size_t)(sq.n0 + (row_ok ? node : 0)) * P.W)
+             : nullptr;
   auto issue_stage = [&](int it) {
     unsigned char* st = lds + (it % NS) * kStage;
 #pragma unroll
@@ -508,11 +525,34 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
     }
     // The 32-bit half of this lane's mask word that covers each of its
     // wave's tiles (any in-bounds word for prefix tiles and idle rows).
+    if constexpr (!MR) {
 #pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-      const int my_tile = t_lo + (it * KG + kg) * TPW + j;
-      const int dw = (my_tile >= Lt && my_tile < t_hi) ? my_tile - Lt : 0;
-      dma_b32(mrow_dw + dw, lds_addr(st + kMaskOff + (wave * TPW + j) * 256));
+      for (int j = 0; j < TPW; ++j) {
+        const int my_tile = t_lo + (it * KG + kg) * TPW + j;
+        const int dw = (my_tile >= Lt && my_tile < t_hi) ? my_tile - Lt : 0;
+        dma_b32(mrow_dw + dw, lds_addr(st + kMaskOff + (wave * TPW + j) * 256));
+      }
+    }
+  };
+
+  // MR: the whole mask row of this lane's node (at most 128 nodes, 4 dwords)
+  // lives in registers.  Ahead of the query rows, each wave copies its lanes'
+  // mask dwords to LDS, or, when the kernel builds the mask, wave 0 copies
+  // the sequence's parents; both are retired by the first stage wait.
+  unsigned char* aux = lds + Map::kAuxOff;
+  auto issue_aux = [&]() {
+    if constexpr (MR) {
+      if (P.build) {
+        if (wave == 0) {
+          for (int h = 0; h * 64 < sq.nn; ++h) {
+            const int k = h * 64 + lane;
+            dma_b32(P.parents + sq.n0 + (k < sq.nn ? k : 0), lds_addr(aux + h * 256));
+          }
+        }
+      } else {
+        for (int d = 0; d < 2 * P.W; ++d)
+          dma_b32(mrow_dw + d, lds_addr(aux + wave * 1024 + d * 256));
+      }
     }
   };
   // Stage it is in LDS for every wave once each has retired its own loads up
@@ -654,11 +694,62 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
   // tiles per stage: all their scores first, then softmax + PV of each, in
   // one basic block, so the scheduler can fill the MFMA chains of one tile
   // with the VALU work of the other.
-  // The query loads precede stage 0, so the first stage wait retires them.
+  // The query (and mask) loads precede stage 0, so the first stage wait
+  // retires them.
+  uint32_t mw[4] = {0u, 0u, 0u, 0u};   // MR: this lane's mask row, 32 nodes per dword
+  bool tree_bad = false;               // built mask: the sequence's parents are invalid
+  issue_aux();
   issue_q();
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k)
     if (k < n_iter) issue_stage(k);
+  if constexpr (MR) {
+    if (P.build) {
+      // Wave 0's parent loads were issued first: wait for them alone (the
+      // query and stage loads issued after them stay in flight), share them
+      // through the barrier, and build the rows while the first stages load.
+      constexpr int kQLoads = RG * 8 / NW;
+      const int staged = n_iter < NS - 1 ? n_iter : NS - 1;   // stages issued so far
+      if (staged >= 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm<kQLoads + 2 * kLoads>());
+      else if (staged == 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm<kQLoads + kLoads>());
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm<kQLoads>());
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // Ancestor rows from the parents (scope of tree_attn_build_mask):
+      // node i sees itself and every node on its path to the root.  A
+      // tree is valid iff every parent p of node k satisfies -1 <= p < k
+      // (each workgroup checks the whole sequence, so all agree); an
+      // invalid tree gets all-zero rows, depth -1 and status 2.
+      const int32_t* par = reinterpret_cast<const int32_t*>(aux);
+      bool bad = false;
+      for (int h = 0; h * 64 < sq.nn; ++h) {
+        const int k = h * 64 + lane;
+        if (k < sq.nn) {
+          const int p = par[k];
+          bad = bad || p < -1 || p >= k;
+        }
+      }
+      bad = __ballot(bad) != 0;
+      uint64_t lo = 0, hi = 0;
+      if (!bad) {
+        for (int cur = node; cur >= 0; cur = par[cur]) {   // parents strictly decrease
+          if (cur < 64)
+            lo |= 1ull << cur;
+          else
+            hi |= 1ull << (cur - 64);
+        }
+      }
+      mw[0] = (uint32_t)lo;
+      mw[1] = (uint32_t)(lo >> 32);
+      mw[2] = (uint32_t)hi;
+      mw[3] = (uint32_t)(hi >> 32);
+      tree_bad = bad;
+    }
+  }
   int slot = 0;   // it % NS, kept in a scalar register
   for (int it = 0; it < n_iter; ++it) {
     wait_stage(it, n_iter);
@@ -667,6 +758,15 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         qf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qb + koff[i]));
+      if constexpr (MR) {
+        if (!P.build) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            mw[d] = d < 2 * P.W ? *reinterpret_cast<const uint32_t*>(aux + wave * 1024 + d * 256 +
+                                                                     lane * 4)
+                                : 0u;
+        }
+      }
       if (Map::kQAlias) {
         // The last ring slot holds the query block: every wave has its rows
         // in registers before stage NS-1 is issued over it.
@@ -692,11 +792,32 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
       if (ac[j]) {
-        const uint32_t mbits =
-            *reinterpret_cast<const uint32_t*>(st + kMaskOff + (wave * TPW + j) * 256 + lane * 4);
+        uint32_t mbits;
+        if constexpr (MR) {
+          const int d = tl[j] - Lt;   // uniform; only tree tiles (d >= 0) use the bits
+          mbits = d <= 0 ? mw[0] : d == 1 ? mw[1] : d == 2 ? mw[2] : mw[3];
+        } else {
+          mbits = *reinterpret_cast<const uint32_t*>(st + kMaskOff + (wave * TPW + j) * 256 +
+                                                     lane * 4);
+        }
         softmax_pv(sc[j], st + (kg * TPW + j) * kTileBytes + kTileKV, tl[j], mbits);
       }
     }
+  }
+  if (MR && P.build && g == 0 && s == 0) {
+    // One writer per node: the workgroups of KV head 0 and split 0, the lane
+    // holding the node's first query head.  An invalid tree's rows are zero,
+    // so its depths come out as -1.
+    if (row_ok && my_row % P.G == 0) {
+      uint64_t* mo = P.mask_out + (size_t)(sq.n0 + node) * P.W;
+      const uint64_t lo = (uint64_t)mw[1] << 32 | mw[0];
+      const uint64_t hi = (uint64_t)mw[3] << 32 | mw[2];
+      mo[0] = lo;
+      if (P.W > 1) mo[1] = hi;
+      if (P.depth_out) P.depth_out[sq.n0 + node] = __popcll(lo) + __popcll(hi) - 1;
+    }
+    if (r == 0 && tid == 0 && P.status_out)
+      P.status_out[b] = tree_bad ? TA_ERR_INVALID_TREE : 0;
   }
   __syncthreads();
 
@@ -863,16 +984,16 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
   store_merged(P, sq, g, r, rl, e, j, hh, ma);
 }
 
-template <int RG, int KG, int TPW, int NS>
+template <int RG, int KG, int TPW, int NS, bool MR>
 hipError_t launch_shape(const KParams& kp, long long grid, long long merge_grid, hipStream_t stream) {
-  const size_t lds = LdsMap<RG, KG, TPW, NS>::kBytes;
+  const size_t lds = LdsMap<RG, KG, TPW, NS, MR>::kBytes;
   if (lds > 64 * 1024) {
-    hipError_t e =
-        raise_dynamic_lds(reinterpret_cast<const void*>(&fwd_bf16_kernel<RG, KG, TPW, NS>), (int)lds);
+    hipError_t e = raise_dynamic_lds(
+        reinterpret_cast<const void*>(&fwd_bf16_kernel<RG, KG, TPW, NS, MR>), (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((fwd_bf16_kernel<RG, KG, TPW, NS>), dim3((unsigned)grid), dim3(RG * KG * 64),
-                     lds, stream, kp);
+  hipLaunchKernelGGL((fwd_bf16_kernel<RG, KG, TPW, NS, MR>), dim3((unsigned)grid),
+                     dim3(RG * KG * 64), lds, stream, kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || merge_grid == 0) return e;
   hipLaunchKernelGGL((merge_bf16_kernel<RG>), dim3((unsigned)merge_grid), dim3(256), 0, stream, kp);
@@ -882,6 +1003,8 @@ hipError_t launch_shape(const KParams& kp, long long grid, long long merge_grid,
 // Largest in-kernel merge grid: half of MI355X's 256 CUs (checked against the
 // device's CU count at launch).
 constexpr long long kMaxMergeBlocks = 128;
+// Bytes of group counters at the start of a workspace that holds partials.
+constexpr size_t kCounterBytes = 2048;
 
 int pow2_ceil(int x) {
   int p = 1;
@@ -929,13 +1052,15 @@ FwdPlan plan_forward_bf16(int B, int total_nodes, int max_nodes, int Hq, int Hkv
   // Each XCD must hold whole (sequence, KV head) blocks of items, and the
   // arrival word counts at most 127 splits per XCD.
   p.merge_in_kernel = p.S > 1 && p.S < 128 && p.groups * p.merge_wpg <= kMaxMergeBlocks &&
-                      ((long long)B * Hkv) % 8 == 0;
+                      ((long long)B * Hkv) % 8 == 0 &&
+                      p.groups * 2 * sizeof(unsigned long long) <= kCounterBytes;
   p.ws_bytes = 0;
   if (p.S > 1) {
-    const size_t partials = (size_t)p.n_items * p.rows_wg * (kD * 2 + 8);
-    p.cnt_off = (partials + 255) / 256 * 256;
-    p.ws_bytes =
-        p.merge_in_kernel ? p.cnt_off + (size_t)p.groups * 2 * sizeof(unsigned long long) : partials;
+    // [group counters | O partials | max and sum partials].  The counter
+    // block leads every workspace that holds partials, whichever merge runs,
+    // so a buffer shared by calls of different shapes never has partials
+    // written over the counters (which every call leaves at zero).
+    p.ws_bytes = kCounterBytes + (size_t)p.n_items * p.rows_wg * (kD * 2 + 8);
   }
   return p;
 }
@@ -952,16 +1077,27 @@ hipError_t launch_forward_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t s
   kp.mask = a.mask;
   kp.out = static_cast<uint16_t*>(a.out);
   kp.lse = a.lse;
+  kp.parents = a.parents;
+  kp.mask_out = a.mask_out;
+  kp.depth_out = a.depth_out;
+  kp.status_out = a.status_out;
+  kp.build = a.build_mask ? 1 : 0;
+  // Mask rows in registers: required when the rows are built here; for a
+  // given mask they pay off only on the eight-row-block shape (measured: a
+  // few per cent faster there, slower on the smaller shapes, whose extra
+  // scalar spills cost more than the mask DMA they save).
+  if (a.build_mask && a.W > 2) return hipErrorInvalidValue;
+  const bool mr = a.build_mask || (a.W <= 2 && p.rg == 8);
   long long merge_blocks = 0;
   if (p.S > 1) {
-    kp.ws_o = static_cast<u32x2_t*>(a.workspace);
-    kp.ws_ml = reinterpret_cast<float2*>(static_cast<unsigned char*>(a.workspace) +
+    unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+    kp.ws_o = reinterpret_cast<u32x2_t*>(ws + kCounterBytes);
+    kp.ws_ml = reinterpret_cast<float2*>(ws + kCounterBytes +
                                          (size_t)p.n_items * p.rows_wg * kD * 2);
     // The in-kernel merge relies on the 8-XCD round-robin dealing of
     // MI355X (256 CUs); elsewhere the separate merge kernel runs.
     if (p.merge_in_kernel && device_cu_count() == 256) {
-      kp.cnt = reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(a.workspace) +
-                                                     p.cnt_off);
+      kp.cnt = reinterpret_cast<unsigned long long*>(ws);
       merge_blocks = p.groups * p.merge_wpg;
       kp.head_major = 1;
     }
@@ -988,11 +1124,16 @@ hipError_t launch_forward_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t s
   const long long merge_grid =
       (p.S > 1 && merge_blocks == 0) ? (long long)a.B * a.Hkv * p.R * p.rg * 4 : 0;
   switch (p.rg * 16 + p.kg) {
-    // A three-stage ring measured as fast as four on every shape here.
-    case 1 * 16 + 2: return launch_shape<1, 2, 1, 3>(kp, grid, merge_grid, stream);
-    case 2 * 16 + 2: return launch_shape<2, 2, 1, 3>(kp, grid, merge_grid, stream);
-    case 4 * 16 + 2: return launch_shape<4, 2, 1, 3>(kp, grid, merge_grid, stream);
-    case 8 * 16 + 1: return launch_shape<8, 1, 2, 3>(kp, grid, merge_grid, stream);
+    // A three-stage ring measured as fast as four on every shape here.  With
+    // MR the mask rows (at most 128 nodes) sit in registers.
+    case 1 * 16 + 2: return mr ? launch_shape<1, 2, 1, 3, true>(kp, grid, merge_grid, stream)
+                               : launch_shape<1, 2, 1, 3, false>(kp, grid, merge_grid, stream);
+    case 2 * 16 + 2: return mr ? launch_shape<2, 2, 1, 3, true>(kp, grid, merge_grid, stream)
+                               : launch_shape<2, 2, 1, 3, false>(kp, grid, merge_grid, stream);
+    case 4 * 16 + 2: return mr ? launch_shape<4, 2, 1, 3, true>(kp, grid, merge_grid, stream)
+                               : launch_shape<4, 2, 1, 3, false>(kp, grid, merge_grid, stream);
+    case 8 * 16 + 1: return mr ? launch_shape<8, 1, 2, 3, true>(kp, grid, merge_grid, stream)
+                               : launch_shape<8, 1, 2, 3, false>(kp, grid, merge_grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

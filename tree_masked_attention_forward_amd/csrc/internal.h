@@ -24,7 +24,6 @@ struct FwdPlan {
   long long groups;    // B * Hkv * R (sequence, KV head, row tile) groups
   int merge_wpg;       // merge workgroups per group when the merge runs in-kernel
   bool merge_in_kernel;  // splits merged by trailing workgroups of the same grid
-  size_t cnt_off;      // byte offset of the per-group counters (in-kernel merge)
   size_t ws_bytes;     // partial (O, m, l) storage [+ counters]; 0 when S == 1
 };
 
@@ -44,6 +43,14 @@ struct FwdArgs {
   void* out;
   float* lse;
   void* workspace;
+  // Mask built inside the forward kernel (tree_attn_mask_and_forward; bf16,
+  // at most 128 nodes per sequence): parents in, mask rows, depths and
+  // per-sequence status out, `mask` unused.
+  bool build_mask;
+  const int32_t* parents;
+  uint64_t* mask_out;
+  int32_t* depth_out;
+  int32_t* status_out;
 };
 
 // Raises a kernel's dynamic LDS limit to at least `bytes` on the current
