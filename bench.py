@@ -372,29 +372,58 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def event_time(fn, n):
+        """Mean device time per call (us) over about n calls, and the p10 / p50 /
+        p90 over replays of the per-call time of one replay (one call per
+        rotation set with graphs, one call without)."""
         if use_graphs:
             g = capture(fn, range(len(sets)))
-            reps = max(1, -(-n // len(sets)))
-            calls = reps * len(sets)
+            per = len(sets)
+            reps = max(20, -(-n // per))
             run = lambda i: g.replay()
         else:
-            reps = calls = n
+            per, reps = 1, max(20, n)
             run = lambda i: fn(sets[i % len(sets)])
         for i in range(2):
             run(i)
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
         for i in range(reps):
             run(i)
-        end.record(stream)
-        end.synchronize()
-        return start.elapsed_time(end) * 1e3 / calls   # microseconds per call
+            ev[i + 1].record(stream)
+        ev[-1].synchronize()
+        each = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 / per for i in range(reps))
+        pct = lambda q: each[min(reps - 1, int(round(q * (reps - 1))))]
+        mean = ev[0].elapsed_time(ev[-1]) * 1e3 / (reps * per)
+        return mean, {"p10": round(pct(0.1), 3), "p50": round(pct(0.5), 3),
+                      "p90": round(pct(0.9), 3), "replays": reps, "calls_per_replay": per}
+
+    # The commit of the accepted path (the step after verification): the accepted rows
+    # of each set's tree are appended to one cache slot per sequence, sized so that
+    # every timed call finds room.
+    one_step(sets[0])
+    torch.cuda.synchronize()
+    calls_max = 4 * max(20 * len(sets), args.steps) + 64   # above what event_time makes
+    room = max(1, int(alen.max())) * calls_max
+    L_b = torch.diff(base["poffs"])
+    cache_offs = torch.zeros(B + 1, dtype=torch.int64, device=dev)
+    cache_offs[1:] = torch.cumsum(L_b + room, 0)
+    k_cache = torch.empty((int(cache_offs[-1]), Hkv, D), dtype=base["kt"].dtype, device=dev)
+    v_cache = torch.empty_like(k_cache)
+    cache_lens = L_b.clone()
+    commit_status = torch.empty(B, dtype=torch.int32, device=dev)
+    acc_len, acc_nodes = alen.clone(), anodes.clone()
+
+    def do_commit(s):
+        ta.kv_commit(s["kt"], s["vt"], s["noffs"], acc_len, acc_nodes, k_cache, v_cache,
+                     cache_offs, cache_lens, status=commit_status)
 
     do_mask(sets[0])
-    t_mask = event_time(do_mask, args.steps)
-    t_fwd = event_time(fwd_fn, args.steps)
-    t_ver = event_time(do_verify, args.steps)
+    t_mask, d_mask = event_time(do_mask, args.steps)
+    t_fwd, d_fwd = event_time(fwd_fn, args.steps)
+    t_ver, d_ver = event_time(do_verify, args.steps)
+    t_commit, d_commit = event_time(do_commit, args.steps)
+    if not bool((commit_status == 0).all()):
+        raise SystemExit("tree_kv_commit reported a failure in the timing loop")
     print(f"[bench] per call us: mask {t_mask:.2f} forward {t_fwd:.2f} verify {t_ver:.2f}",
           file=sys.stderr, flush=True)
 
@@ -467,7 +496,13 @@ def main():
         "cpu_baseline": cpu,
         "detail": {
             "us_per_call": {fwd_call: round(t_fwd, 3), "tree_verify_greedy": round(t_ver, 3),
-                            "tree_attn_build_mask (standalone)": round(t_mask, 3)},
+                            "tree_attn_build_mask (standalone)": round(t_mask, 3),
+                            "tree_kv_commit (standalone)": round(t_commit, 3)},
+            "us_per_call_spread": {fwd_call: d_fwd, "tree_verify_greedy": d_ver,
+                                   "tree_attn_build_mask (standalone)": d_mask,
+                                   "tree_kv_commit (standalone)": d_commit},
+            "commit": {"accepted_rows": int(acc_len.sum()),
+                       "alg_bytes": int(acc_len.sum()) * Hkv * D * base["kt"].element_size() * 4},
             "forward": {"tree_tokens_per_s": round(sum_n / (t_fwd * 1e-6), 1),
                         "kv_GBps": round(kv_bytes / (t_fwd * 1e-6) / 1e9, 1),
                         "alg_GBps": round(fwd_gbs, 1), "alg_TFLOPs": round(fwd_tfs, 2),

@@ -122,6 +122,11 @@ TA_API size_t tree_attn_forward_workspace_size(int dtype, int32_t B, int32_t tot
  *                  packed back to back.
  *   prefix_offsets int64 [B+1]  sequence b's prefix rows are
  *                  prefix_offsets[b] .. prefix_offsets[b+1]-1 (L_b may be 0).
+ *   prefix_lens    int64 [B], nullable: when given, sequence b's prefix is
+ *                  only the first prefix_lens[b] rows of that range (a cache
+ *                  slot with room to grow, as tree_kv_commit appends to; the
+ *                  rows past the length are never read).  max_prefix bounds
+ *                  the lengths, total_prefix = prefix_offsets[B] the slots.
  *   node_offsets   int32 [B+1]  as for tree_attn_build_mask.
  *   mask           uint64 [sum_N][W] from tree_attn_build_mask.
  *   B, total_nodes, max_nodes, total_prefix, max_prefix, Hq, Hkv, D, scale [host].
@@ -143,8 +148,9 @@ TA_API size_t tree_attn_forward_workspace_size(int dtype, int32_t B, int32_t tot
  */
 TA_API int tree_attn_forward(int dtype, const void* q, const void* k_tree, const void* v_tree,
                       const void* k_prefix, const void* v_prefix,
-                      const int64_t* prefix_offsets, const int32_t* node_offsets,
-                      const uint64_t* mask, int32_t B, int32_t total_nodes, int32_t max_nodes,
+                      const int64_t* prefix_offsets, const int64_t* prefix_lens,
+                      const int32_t* node_offsets, const uint64_t* mask, int32_t B,
+                      int32_t total_nodes, int32_t max_nodes,
                       int64_t total_prefix, int64_t max_prefix, int32_t Hq, int32_t Hkv,
                       int32_t D, float scale, void* out, float* lse, void* workspace,
                       size_t workspace_bytes, void* stream);
@@ -175,8 +181,9 @@ TA_API int tree_attn_forward(int dtype, const void* q, const void* k_tree, const
 TA_API int tree_attn_mask_and_forward(int dtype, const int32_t* parents, const void* q,
                                       const void* k_tree, const void* v_tree,
                                       const void* k_prefix, const void* v_prefix,
-                                      const int64_t* prefix_offsets, const int32_t* node_offsets,
-                                      int32_t B, int32_t total_nodes, int32_t max_nodes,
+                                      const int64_t* prefix_offsets, const int64_t* prefix_lens,
+                                      const int32_t* node_offsets, int32_t B,
+                                      int32_t total_nodes, int32_t max_nodes,
                                       int64_t total_prefix, int64_t max_prefix, int32_t Hq,
                                       int32_t Hkv, int32_t D, float scale, uint64_t* mask,
                                       int32_t* depth, int32_t* tree_status, void* out,
@@ -223,6 +230,46 @@ TA_API int tree_verify_greedy(int logits_dtype, const void* logits, const int32_
                        int32_t* target_argmax, int32_t* accept_len, int32_t* accept_nodes,
                        int32_t* accept_tokens, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/*
+ * Commit of the accepted path to the KV cache (and rollback of the rest).
+ *
+ * Follows: inferensys "Tree Attention", Multi-Token Acceptance & Rollback (the
+ * accepted branch's entries stay in the cache, the rejected branches' are
+ * discarded) and Speculative KV Cache Reuse (the K/V rows the verification
+ * pass computed for the tree are reused, not recomputed).
+ *
+ *   dtype          TA_BF16 or TA_F32: element type of the four K/V buffers.
+ *   k_tree, v_tree [sum_N][Hkv][D]   the tree's K/V rows (as for
+ *                  tree_attn_forward).
+ *   node_offsets   int32 [B+1], as for tree_attn_build_mask.
+ *   accept_len     int32 [B], accept_nodes int32 [B][max_nodes]: the accepted
+ *                  paths, local node ids root first (tree_verify_greedy's
+ *                  outputs).
+ *   k_cache, v_cache [total_cache][Hkv][D] in/out: sequence b's cache slot is
+ *                  rows cache_offsets[b] .. cache_offsets[b+1]-1, of which the
+ *                  first cache_lens[b] are in use.
+ *   cache_offsets  int64 [B+1], non-decreasing slots within total_cache.
+ *   cache_lens     int64 [B] in/out.
+ *   B, total_nodes, max_nodes, Hkv, D, total_cache [host].
+ *   commit_status  out int32 [B], nullable.
+ * Effect per sequence b, with n = accept_len[b] and c = cache_lens[b] on
+ * entry: slot row c + t (t < n) of k_cache and v_cache receives the row of
+ * node accept_nodes[b][t] of k_tree and v_tree, and cache_lens[b] becomes
+ * c + n; no row of a rejected node is copied and no other cache row changes.
+ * Status TA_OK, or TA_ERR_INVALID_ARG when the offsets, lengths or node ids
+ * are out of range or the slot lacks room for n more rows; such a sequence is
+ * left untouched (cache rows and cache_lens).  The next step reads the cache
+ * with tree_attn_forward(..., prefix_offsets = cache_offsets,
+ * prefix_lens = cache_lens, ...).  Calls on one cache must be ordered on one
+ * stream (the lengths are read and written on the device).
+ */
+TA_API int tree_kv_commit(int dtype, const void* k_tree, const void* v_tree,
+                          const int32_t* node_offsets, const int32_t* accept_len,
+                          const int32_t* accept_nodes, int32_t B, int32_t total_nodes,
+                          int32_t max_nodes, int32_t Hkv, int32_t D, void* k_cache,
+                          void* v_cache, const int64_t* cache_offsets, int64_t* cache_lens,
+                          int64_t total_cache, int32_t* commit_status, void* stream);
 
 /* Static text for a status code; never NULL. */
 TA_API const char* tree_attn_status_string(int status);

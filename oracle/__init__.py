@@ -29,4 +29,5 @@ from .tree_attention import (  # noqa: F401
     tree_attention,
     target_argmax,
     verify_greedy,
+    kv_commit,
 )

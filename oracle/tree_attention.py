@@ -163,7 +163,7 @@ def path_causal_attention(q_path: np.ndarray, k_prefix: np.ndarray, v_prefix: np
 
 def tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, parents, node_offsets,
                    prefix_offsets, scale: float, nodes: Optional[Sequence[int]] = None,
-                   return_path_rows: bool = False):
+                   return_path_rows: bool = False, prefix_lens=None):
     """Tree attention output for every node (or for the global node ids given).
 
     q [sum_N][Hq][D]; k_tree, v_tree [sum_N][Hkv][D]; k_prefix, v_prefix
@@ -173,7 +173,9 @@ def tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, parents, node_offsets,
     last row is node i's result.  Returns (out [n][Hq][D], lse [n][Hq]) in
     float64 for the requested nodes (all nodes when ``nodes`` is None), plus,
     if asked, the per-node list of all path rows (the causal outputs of the
-    ancestors as seen from node i's sequence).
+    ancestors as seen from node i's sequence).  With ``prefix_lens`` the
+    prefix of sequence b is only the first prefix_lens[b] rows of its range
+    (a cache slot with room to grow).
     """
     q = _f64(q)
     kt, vt = _f64(k_tree), _f64(v_tree)
@@ -195,6 +197,8 @@ def tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, parents, node_offsets,
         b = int(seq_of[gi])
         n0 = int(node_offsets[b])
         p0, p1 = int(prefix_offsets[b]), int(prefix_offsets[b + 1])
+        if prefix_lens is not None:
+            p1 = p0 + int(prefix_lens[b])
         path = [n0 + j for j in root_path(parents[n0:int(node_offsets[b + 1])], gi - n0)]
         seq_rows = np.zeros((len(path), Hq, D))
         for g in range(Hkv):
@@ -255,3 +259,48 @@ def verify_greedy(logits, draft, parents, node_offsets, max_nodes: int):
             acc_nodes[b, k] = j
             acc_tok[b, k] = int(draft[lo + j])
     return pred, acc_len, acc_nodes, acc_tok
+
+
+# ---------------------------------------------------------------------------
+# Commit of the accepted path ([IS] Multi-Token Acceptance & Rollback,
+#                              Speculative KV Cache Reuse)
+# ---------------------------------------------------------------------------
+
+def kv_commit(k_tree, v_tree, node_offsets, accept_len, accept_nodes, k_cache, v_cache,
+              cache_offsets, cache_lens, max_nodes: int):
+    """Append each sequence's accepted path to its cache slot.
+
+    The accepted branch keeps its K/V entries, in root-to-leaf order, right
+    after the rows already in the sequence's cache; the rejected nodes' rows
+    are dropped.  Sequence b's slot is rows cache_offsets[b] ..
+    cache_offsets[b+1]-1 of k_cache/v_cache, the first cache_lens[b] in use.
+    Works on CPU torch tensors (any dtype; rows are copied, never converted).
+    Returns (k_cache', v_cache', cache_lens', status) as new objects; a
+    sequence whose offsets, lengths or node ids are out of range, or whose
+    slot has no room, is left as it was with status STATUS_INVALID_ARG.
+    """
+    kc, vc = k_cache.clone(), v_cache.clone()
+    node_offsets = np.asarray(node_offsets, dtype=np.int64)
+    accept_len = np.asarray(accept_len, dtype=np.int64)
+    accept_nodes = np.asarray(accept_nodes, dtype=np.int64)
+    cache_offsets = np.asarray(cache_offsets, dtype=np.int64)
+    lens = np.asarray(cache_lens, dtype=np.int64).copy()
+    B = len(node_offsets) - 1
+    total_nodes, total_cache = k_tree.shape[0], k_cache.shape[0]
+    status = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        n0, n1 = int(node_offsets[b]), int(node_offsets[b + 1])
+        c0, c1 = int(cache_offsets[b]), int(cache_offsets[b + 1])
+        n, c = int(accept_len[b]), int(lens[b])
+        nodes = [int(accept_nodes[b, t]) for t in range(max(0, min(n, max_nodes)))]
+        ok = (0 <= n0 <= n1 <= total_nodes and n1 - n0 <= max_nodes and
+              0 <= c0 <= c1 <= total_cache and c >= 0 and 0 <= n <= n1 - n0 and
+              c + n <= c1 - c0 and all(0 <= j < n1 - n0 for j in nodes))
+        if not ok:
+            status[b] = STATUS_INVALID_ARG
+            continue
+        for t, j in enumerate(nodes):
+            kc[c0 + c + t] = k_tree[n0 + j]
+            vc[c0 + c + t] = v_tree[n0 + j]
+        lens[b] = c + n
+    return kc, vc, lens, status

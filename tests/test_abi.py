@@ -24,9 +24,9 @@ def lib():
 def test_header_declares_the_three_calls():
     names = _declared_functions()
     for n in ("tree_attn_build_mask", "tree_attn_forward", "tree_verify_greedy",
-              "tree_attn_mask_and_forward"):
+              "tree_attn_mask_and_forward", "tree_kv_commit"):
         assert n in names
-    assert len(names) == 7, names
+    assert len(names) == 8, names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -44,12 +44,13 @@ def test_status_strings(lib):
 
 def _fwd(lib, **kw):
     args = dict(dtype=1, q=1 << 20, kt=1 << 20, vt=1 << 20, kp=1 << 20, vp=1 << 20, po=1 << 20,
-                no=1 << 20, mask=1 << 20, B=1, total=64, maxn=64, tp=4096, mp=4096, Hq=32, Hkv=8,
+                pl=None, no=1 << 20, mask=1 << 20, B=1, total=64, maxn=64, tp=4096, mp=4096, Hq=32,
+                Hkv=8,
                 D=128, scale=0.088, out=1 << 20, lse=None, ws=None, wsb=0, stream=None)
     args.update(kw)
     a = args
     return lib.tree_attn_forward(a["dtype"], a["q"], a["kt"], a["vt"], a["kp"], a["vp"], a["po"],
-                                 a["no"], a["mask"], a["B"], a["total"], a["maxn"], a["tp"],
+                                 a["pl"], a["no"], a["mask"], a["B"], a["total"], a["maxn"], a["tp"],
                                  a["mp"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["out"],
                                  a["lse"], a["ws"], a["wsb"], a["stream"])
 
@@ -99,13 +100,14 @@ def test_build_mask_and_verify_host_validation(lib):
 
 def _mfwd(lib, **kw):
     args = dict(dtype=1, par=1 << 20, q=1 << 20, kt=1 << 20, vt=1 << 20, kp=1 << 20, vp=1 << 20,
-                po=1 << 20, no=1 << 20, B=1, total=64, maxn=64, tp=4096, mp=4096, Hq=32, Hkv=8,
-                D=128, scale=0.088, mask=1 << 20, depth=None, status=None, out=1 << 20, lse=None,
+                po=1 << 20, pl=None, no=1 << 20, B=1, total=64, maxn=64, tp=4096, mp=4096, Hq=32,
+                Hkv=8, D=128, scale=0.088, mask=1 << 20, depth=None, status=None, out=1 << 20,
+                lse=None,
                 ws=None, wsb=0, stream=None)
     args.update(kw)
     a = args
     return lib.tree_attn_mask_and_forward(
-        a["dtype"], a["par"], a["q"], a["kt"], a["vt"], a["kp"], a["vp"], a["po"], a["no"],
+        a["dtype"], a["par"], a["q"], a["kt"], a["vt"], a["kp"], a["vp"], a["po"], a["pl"], a["no"],
         a["B"], a["total"], a["maxn"], a["tp"], a["mp"], a["Hq"], a["Hkv"], a["D"], a["scale"],
         a["mask"], a["depth"], a["status"], a["out"], a["lse"], a["ws"], a["wsb"], a["stream"])
 
@@ -120,3 +122,25 @@ def test_mask_and_forward_host_validation(lib):
     assert _mfwd(lib, ws=None, wsb=0) == 4         # split partials need a workspace
     assert _mfwd(lib, maxn=200, ws=None, wsb=0) == 4   # two-call path checks it too
     assert _mfwd(lib, total=0) == 0                # nothing to do, nothing launched
+
+
+def _commit(lib, **kw):
+    args = dict(dtype=1, kt=1 << 20, vt=1 << 20, no=1 << 20, al=1 << 20, an=1 << 20, B=2,
+                total=10, maxn=8, Hkv=8, D=128, kc=1 << 20, vc=1 << 20, co=1 << 20, cl=1 << 20,
+                tc=100, st=None, stream=None)
+    args.update(kw)
+    a = args
+    return lib.tree_kv_commit(a["dtype"], a["kt"], a["vt"], a["no"], a["al"], a["an"], a["B"],
+                              a["total"], a["maxn"], a["Hkv"], a["D"], a["kc"], a["vc"], a["co"],
+                              a["cl"], a["tc"], a["st"], a["stream"])
+
+
+def test_kv_commit_host_validation(lib):
+    assert _commit(lib, dtype=9) == 3
+    assert _commit(lib, B=0) == 1
+    assert _commit(lib, maxn=5000) == 3
+    assert _commit(lib, Hkv=0) == 1
+    assert _commit(lib, kt=None) == 1              # tree rows but no tree pointer
+    assert _commit(lib, kc=None) == 1              # cache rows but no cache pointer
+    assert _commit(lib, cl=None) == 1              # the lengths are required
+    assert _commit(lib, tc=-1) == 1

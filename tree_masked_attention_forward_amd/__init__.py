@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     build_mask,
     forward,
     forward_workspace_size,
+    kv_commit,
     load_library,
     mask_and_forward,
     mask_words,
@@ -35,3 +36,4 @@ tree_attn_build_mask = build_mask
 tree_attn_forward = forward
 tree_attn_mask_and_forward = mask_and_forward
 tree_verify_greedy = verify_greedy
+tree_kv_commit = kv_commit

@@ -59,11 +59,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tree_attn_forward_workspace_size.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32,
                                                      _i32, _i64, _i64]
     lib.tree_attn_forward.restype = ctypes.c_int
-    lib.tree_attn_forward.argtypes = [ctypes.c_int] + [_c_void_p] * 8 + [
+    lib.tree_attn_forward.argtypes = [ctypes.c_int] + [_c_void_p] * 9 + [
         _i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32, ctypes.c_float, _c_void_p, _c_void_p,
         _c_void_p, ctypes.c_size_t, _c_void_p]
     lib.tree_attn_mask_and_forward.restype = ctypes.c_int
-    lib.tree_attn_mask_and_forward.argtypes = [ctypes.c_int] + [_c_void_p] * 8 + [
+    lib.tree_attn_mask_and_forward.argtypes = [ctypes.c_int] + [_c_void_p] * 9 + [
         _i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32, ctypes.c_float] + [_c_void_p] * 6 + [
         ctypes.c_size_t, _c_void_p]
     lib.tree_verify_greedy_workspace_size.restype = ctypes.c_size_t
@@ -72,6 +72,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tree_verify_greedy.argtypes = [ctypes.c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                        _i32, _i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
                                        _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p]
+    lib.tree_kv_commit.restype = ctypes.c_int
+    lib.tree_kv_commit.argtypes = [ctypes.c_int] + [_c_void_p] * 5 + [_i32] * 5 + [
+        _c_void_p] * 4 + [_i64, _c_void_p, _c_void_p]
     if path is None:
         _lib = lib
     return lib
@@ -151,7 +154,7 @@ def forward_workspace_size(dtype: torch.dtype, B: int, total_nodes: int, max_nod
 
 
 def _forward_args(q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets, node_offsets,
-                  max_nodes, max_prefix, out, lse, return_lse, workspace):
+                  max_nodes, max_prefix, out, lse, return_lse, workspace, prefix_lens):
     """Checks shared by forward() and mask_and_forward(); allocates outputs and
     the (zero-filled) workspace when they are not given."""
     dev = _device_of(q)
@@ -175,6 +178,10 @@ def _forward_args(q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets, node_of
     B = node_offsets.numel() - 1
     if prefix_offsets.numel() != B + 1:
         raise ValueError("prefix_offsets and node_offsets must both hold B+1 entries")
+    if prefix_lens is not None:
+        _need(prefix_lens, "prefix_lens", torch.int64, dev, 1)
+        if prefix_lens.numel() != B:
+            raise ValueError("prefix_lens must hold B entries")
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", dtype, dev, 3)
@@ -200,17 +207,21 @@ def forward(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor,
             k_prefix: torch.Tensor, v_prefix: torch.Tensor, prefix_offsets: torch.Tensor,
             node_offsets: torch.Tensor, mask: torch.Tensor, max_nodes: int, max_prefix: int,
             scale: float, *, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-            return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
+            return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
+            prefix_lens: Optional[torch.Tensor] = None):
     """tree_attn_forward.  Returns out (and lse when asked or given).  A
-    workspace passed in must have been zero-filled before its first use."""
+    workspace passed in must have been zero-filled before its first use.
+    prefix_lens (int64 [B]) reads only the first prefix_lens[b] rows of each
+    prefix range (a cache slot)."""
     a = _forward_args(q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets, node_offsets,
-                      max_nodes, max_prefix, out, lse, return_lse, workspace)
+                      max_nodes, max_prefix, out, lse, return_lse, workspace, prefix_lens)
     _need(mask, "mask", torch.uint64, a["dev"], 2)
     if mask.shape != (a["total"], mask_words(max_nodes)):
         raise ValueError("mask must be [sum_N, ceil(max_nodes/64)]")
     _check("tree_attn_forward", load_library().tree_attn_forward(
         a["code"], _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_prefix), _ptr(v_prefix),
-        _ptr(prefix_offsets), _ptr(node_offsets), _ptr(mask), a["B"], a["total"], int(max_nodes),
+        _ptr(prefix_offsets), _ptr(prefix_lens), _ptr(node_offsets), _ptr(mask), a["B"],
+        a["total"], int(max_nodes),
         a["total_prefix"], int(max_prefix), a["Hq"], a["Hkv"], a["D"], float(scale),
         _ptr(a["out"]), _ptr(a["lse"]), _ptr(a["workspace"]), a["ws_len"], _stream(a["dev"])))
     return (a["out"], a["lse"]) if (return_lse or lse is not None) else a["out"]
@@ -223,11 +234,12 @@ def mask_and_forward(parents: torch.Tensor, q: torch.Tensor, k_tree: torch.Tenso
                      lse: Optional[torch.Tensor] = None, return_lse: bool = False,
                      mask: Optional[torch.Tensor] = None, depth: Optional[torch.Tensor] = None,
                      status: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None):
+                     workspace: Optional[torch.Tensor] = None,
+                     prefix_lens: Optional[torch.Tensor] = None):
     """tree_attn_mask_and_forward: the ancestor mask and the attention in one
     call.  Returns (out, [lse,] mask, depth, status)."""
     a = _forward_args(q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets, node_offsets,
-                      max_nodes, max_prefix, out, lse, return_lse, workspace)
+                      max_nodes, max_prefix, out, lse, return_lse, workspace, prefix_lens)
     dev, total, B = a["dev"], a["total"], a["B"]
     _need(parents, "parents", torch.int32, dev, 1)
     if parents.numel() != total:
@@ -244,7 +256,8 @@ def mask_and_forward(parents: torch.Tensor, q: torch.Tensor, k_tree: torch.Tenso
         raise ValueError(f"mask must be [{total}, {W}]")
     _check("tree_attn_mask_and_forward", load_library().tree_attn_mask_and_forward(
         a["code"], _ptr(parents), _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_prefix),
-        _ptr(v_prefix), _ptr(prefix_offsets), _ptr(node_offsets), B, total, int(max_nodes),
+        _ptr(v_prefix), _ptr(prefix_offsets), _ptr(prefix_lens), _ptr(node_offsets), B, total,
+        int(max_nodes),
         a["total_prefix"], int(max_prefix), a["Hq"], a["Hkv"], a["D"], float(scale), _ptr(mask),
         _ptr(depth), _ptr(status), _ptr(a["out"]), _ptr(a["lse"]), _ptr(a["workspace"]),
         a["ws_len"], _stream(dev)))
@@ -292,3 +305,44 @@ def verify_greedy(logits: torch.Tensor, draft_tokens: torch.Tensor, mask: torch.
         int(max_nodes), V, _ptr(target_argmax), _ptr(accept_len), _ptr(accept_nodes),
         _ptr(accept_tokens), _ptr(workspace), ws_len, _stream(dev)))
     return target_argmax, accept_len, accept_nodes, accept_tokens
+
+
+def kv_commit(k_tree: torch.Tensor, v_tree: torch.Tensor, node_offsets: torch.Tensor,
+              accept_len: torch.Tensor, accept_nodes: torch.Tensor, k_cache: torch.Tensor,
+              v_cache: torch.Tensor, cache_offsets: torch.Tensor, cache_lens: torch.Tensor, *,
+              status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """tree_kv_commit: append each sequence's accepted path to its cache slot
+    (k_cache/v_cache and cache_lens are updated in place).  Returns the
+    per-sequence status."""
+    dev = _device_of(k_tree)
+    dtype = k_tree.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("k_tree must be bfloat16 or float32")
+    for name, t in (("k_tree", k_tree), ("v_tree", v_tree), ("k_cache", k_cache),
+                    ("v_cache", v_cache)):
+        _need(t, name, dtype, dev, 3)
+    total, Hkv, D = k_tree.shape
+    if v_tree.shape != k_tree.shape:
+        raise ValueError("v_tree must have k_tree's shape")
+    if v_cache.shape != k_cache.shape or tuple(k_cache.shape[1:]) != (Hkv, D):
+        raise ValueError("k_cache/v_cache must be [total_cache, Hkv, D]")
+    _need(node_offsets, "node_offsets", torch.int32, dev, 1)
+    _need(accept_len, "accept_len", torch.int32, dev, 1)
+    _need(accept_nodes, "accept_nodes", torch.int32, dev, 2)
+    _need(cache_offsets, "cache_offsets", torch.int64, dev, 1)
+    _need(cache_lens, "cache_lens", torch.int64, dev, 1)
+    B = node_offsets.numel() - 1
+    max_nodes = accept_nodes.shape[1]
+    if accept_len.numel() != B or accept_nodes.shape[0] != B or cache_lens.numel() != B:
+        raise ValueError("accept_len, accept_nodes and cache_lens must have B rows")
+    if cache_offsets.numel() != B + 1:
+        raise ValueError("cache_offsets must hold B+1 entries")
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(status, "status", torch.int32, dev, 1)
+    code = TA_BF16 if dtype == torch.bfloat16 else TA_F32
+    _check("tree_kv_commit", load_library().tree_kv_commit(
+        code, _ptr(k_tree), _ptr(v_tree), _ptr(node_offsets), _ptr(accept_len),
+        _ptr(accept_nodes), B, total, int(max_nodes), Hkv, D, _ptr(k_cache), _ptr(v_cache),
+        _ptr(cache_offsets), _ptr(cache_lens), k_cache.shape[0], _ptr(status), _stream(dev)))
+    return status

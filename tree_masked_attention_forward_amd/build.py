@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtreeattn.so")
-SOURCES = ["api.cpp", "mask_build.hip", "attn_fwd.hip", "attn_fwd_f32.hip", "verify.hip"]
+SOURCES = ["api.cpp", "mask_build.hip", "attn_fwd.hip", "attn_fwd_f32.hip", "verify.hip",
+           "kv_commit.hip"]
 ARCH = os.environ.get("TREE_ATTN_ARCH", "gfx950")
 
 

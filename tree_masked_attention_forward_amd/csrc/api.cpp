@@ -101,7 +101,8 @@ namespace {
 // `empty` is set when there is nothing to compute (total_nodes == 0).
 int check_forward(int dtype, const void* q, const void* k_tree, const void* v_tree,
                   const void* k_prefix, const void* v_prefix, const int64_t* prefix_offsets,
-                  const int32_t* node_offsets, int32_t B, int32_t total_nodes, int32_t max_nodes,
+                  const int64_t* prefix_lens, const int32_t* node_offsets, int32_t B,
+                  int32_t total_nodes, int32_t max_nodes,
                   int64_t total_prefix, int64_t max_prefix, int32_t Hq, int32_t Hkv, int32_t D,
                   float scale, void* out, float* lse, void* workspace, ta::FwdArgs& a,
                   bool& empty) {
@@ -137,6 +138,7 @@ int check_forward(int dtype, const void* q, const void* k_tree, const void* v_tr
   a.k_prefix = k_prefix;
   a.v_prefix = v_prefix;
   a.prefix_offsets = prefix_offsets;
+  a.prefix_lens = prefix_lens;
   a.node_offsets = node_offsets;
   a.B = B;
   a.total_nodes = total_nodes;
@@ -173,16 +175,17 @@ extern "C" {
 
 int tree_attn_forward(int dtype, const void* q, const void* k_tree, const void* v_tree,
                       const void* k_prefix, const void* v_prefix,
-                      const int64_t* prefix_offsets, const int32_t* node_offsets,
-                      const uint64_t* mask, int32_t B, int32_t total_nodes, int32_t max_nodes,
+                      const int64_t* prefix_offsets, const int64_t* prefix_lens,
+                      const int32_t* node_offsets, const uint64_t* mask, int32_t B,
+                      int32_t total_nodes, int32_t max_nodes,
                       int64_t total_prefix, int64_t max_prefix, int32_t Hq, int32_t Hkv,
                       int32_t D, float scale, void* out, float* lse, void* workspace,
                       size_t workspace_bytes, void* stream) {
   ta::FwdArgs a;
   bool empty = false;
   const int st = check_forward(dtype, q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets,
-                               node_offsets, B, total_nodes, max_nodes, total_prefix, max_prefix,
-                               Hq, Hkv, D, scale, out, lse, workspace, a, empty);
+                               prefix_lens, node_offsets, B, total_nodes, max_nodes, total_prefix,
+                               max_prefix, Hq, Hkv, D, scale, out, lse, workspace, a, empty);
   if (st != TA_OK || empty) return st;
   if (!mask) return TA_ERR_INVALID_ARG;
   a.mask = mask;
@@ -192,7 +195,8 @@ int tree_attn_forward(int dtype, const void* q, const void* k_tree, const void* 
 int tree_attn_mask_and_forward(int dtype, const int32_t* parents, const void* q,
                                const void* k_tree, const void* v_tree, const void* k_prefix,
                                const void* v_prefix, const int64_t* prefix_offsets,
-                               const int32_t* node_offsets, int32_t B, int32_t total_nodes,
+                               const int64_t* prefix_lens, const int32_t* node_offsets,
+                               int32_t B, int32_t total_nodes,
                                int32_t max_nodes, int64_t total_prefix, int64_t max_prefix,
                                int32_t Hq, int32_t Hkv, int32_t D, float scale, uint64_t* mask,
                                int32_t* depth, int32_t* tree_status, void* out, float* lse,
@@ -200,8 +204,8 @@ int tree_attn_mask_and_forward(int dtype, const int32_t* parents, const void* q,
   ta::FwdArgs a;
   bool empty = false;
   const int st = check_forward(dtype, q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets,
-                               node_offsets, B, total_nodes, max_nodes, total_prefix, max_prefix,
-                               Hq, Hkv, D, scale, out, lse, workspace, a, empty);
+                               prefix_lens, node_offsets, B, total_nodes, max_nodes, total_prefix,
+                               max_prefix, Hq, Hkv, D, scale, out, lse, workspace, a, empty);
   if (st != TA_OK) return st;
   if (empty) {
     if (tree_status && B > 0)   // same as tree_attn_build_mask on zero nodes
@@ -257,6 +261,28 @@ int tree_verify_greedy(int logits_dtype, const void* logits, const int32_t* draf
                                       node_offsets, B, total_nodes, max_nodes, V, target_argmax,
                                       accept_len, accept_nodes, accept_tokens, workspace, p,
                                       static_cast<hipStream_t>(stream)));
+}
+
+int tree_kv_commit(int dtype, const void* k_tree, const void* v_tree,
+                   const int32_t* node_offsets, const int32_t* accept_len,
+                   const int32_t* accept_nodes, int32_t B, int32_t total_nodes,
+                   int32_t max_nodes, int32_t Hkv, int32_t D, void* k_cache, void* v_cache,
+                   const int64_t* cache_offsets, int64_t* cache_lens, int64_t total_cache,
+                   int32_t* commit_status, void* stream) {
+  if (dtype != TA_BF16 && dtype != TA_F32) return TA_ERR_UNSUPPORTED;
+  if (B <= 0 || total_nodes < 0 || max_nodes < 1 || Hkv <= 0 || D <= 0 || total_cache < 0)
+    return TA_ERR_INVALID_ARG;
+  if (max_nodes > TA_MAX_NODES) return TA_ERR_UNSUPPORTED;
+  if (!node_offsets || !accept_len || !accept_nodes || !cache_offsets || !cache_lens)
+    return TA_ERR_INVALID_ARG;
+  if (total_nodes > 0 && (!k_tree || !v_tree)) return TA_ERR_INVALID_ARG;
+  if (total_cache > 0 && (!k_cache || !v_cache)) return TA_ERR_INVALID_ARG;
+  const long long row_bytes = (long long)Hkv * D * (dtype == TA_BF16 ? 2 : 4);
+  if (row_bytes > (1LL << 30) || total_cache > (1LL << 40)) return TA_ERR_UNSUPPORTED;
+  return hip_status(ta::launch_kv_commit(k_tree, v_tree, node_offsets, accept_len, accept_nodes,
+                                         B, total_nodes, max_nodes, row_bytes, k_cache, v_cache,
+                                         cache_offsets, cache_lens, total_cache, commit_status,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -81,6 +81,7 @@ struct KParams {
   const uint16_t* k_prefix;
   const uint16_t* v_prefix;
   const int64_t* prefix_offsets;
+  const int64_t* prefix_lens;   // nullable: rows in use of each prefix slot
   const int32_t* node_offsets;
   const uint64_t* mask;      // ancestor rows (null when the kernel builds them)
   uint16_t* out;
@@ -120,9 +121,10 @@ __device__ inline bool decode_seq(const KParams& P, int b, Seq& s) {
   const int n0 = P.node_offsets[b];
   const int n1 = P.node_offsets[b + 1];
   const long long p0 = P.prefix_offsets[b];
-  const long long p1 = P.prefix_offsets[b + 1];
+  const long long pe = P.prefix_offsets[b + 1];
+  const long long p1 = P.prefix_lens ? p0 + P.prefix_lens[b] : pe;
   if (n0 < 0 || n1 <= n0 || n1 - n0 > P.max_nodes || n1 > P.total_nodes) return false;
-  if (p0 < 0 || p1 < p0 || p1 - p0 > P.max_prefix || p1 > P.total_prefix) return false;
+  if (p0 < 0 || p1 < p0 || p1 > pe || p1 - p0 > P.max_prefix || pe > P.total_prefix) return false;
   s.n0 = n0;
   s.nn = n1 - n0;
   s.p0 = p0;
@@ -1073,6 +1075,7 @@ hipError_t launch_forward_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t s
   kp.k_prefix = static_cast<const uint16_t*>(a.k_prefix);
   kp.v_prefix = static_cast<const uint16_t*>(a.v_prefix);
   kp.prefix_offsets = a.prefix_offsets;
+  kp.prefix_lens = a.prefix_lens;
   kp.node_offsets = a.node_offsets;
   kp.mask = a.mask;
   kp.out = static_cast<uint16_t*>(a.out);

@@ -25,6 +25,7 @@ struct F32Params {
   const float* k_prefix;
   const float* v_prefix;
   const int64_t* prefix_offsets;
+  const int64_t* prefix_lens;   // nullable: rows in use of each prefix slot
   const int32_t* node_offsets;
   const uint64_t* mask;
   float* out;
@@ -55,10 +56,11 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(F32Params P) {
   }
   const int b = lo;
   const int n0 = P.node_offsets[b], n1 = P.node_offsets[b + 1];
-  const long long p0 = P.prefix_offsets[b], p1 = P.prefix_offsets[b + 1];
+  const long long p0 = P.prefix_offsets[b], pe = P.prefix_offsets[b + 1];
+  const long long p1 = P.prefix_lens ? p0 + P.prefix_lens[b] : pe;
   if (n0 < 0 || n1 <= n0 || n1 - n0 > P.max_nodes || n1 > P.total_nodes) return;
   if (gnode < n0 || gnode >= n1) return;
-  if (p0 < 0 || p1 < p0 || p1 - p0 > P.max_prefix || p1 > P.total_prefix) return;
+  if (p0 < 0 || p1 < p0 || p1 > pe || p1 - p0 > P.max_prefix || pe > P.total_prefix) return;
   const int nn = n1 - n0;
   const int D = P.D;
   float qv[4], acc[4];
@@ -124,6 +126,7 @@ hipError_t launch_forward_f32(const FwdArgs& a, hipStream_t stream) {
   fp.k_prefix = static_cast<const float*>(a.k_prefix);
   fp.v_prefix = static_cast<const float*>(a.v_prefix);
   fp.prefix_offsets = a.prefix_offsets;
+  fp.prefix_lens = a.prefix_lens;
   fp.node_offsets = a.node_offsets;
   fp.mask = a.mask;
   fp.out = static_cast<float*>(a.out);

@@ -34,6 +34,7 @@ struct FwdArgs {
   const void* k_prefix;
   const void* v_prefix;
   const int64_t* prefix_offsets;
+  const int64_t* prefix_lens;   // nullable: rows in use of each prefix slot
   const int32_t* node_offsets;
   const uint64_t* mask;
   int B, total_nodes, max_nodes;
@@ -85,5 +86,13 @@ hipError_t launch_verify(bool bf16, const void* logits, const int32_t* draft,
                          int total_nodes, int max_nodes, int V, int32_t* target_argmax,
                          int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
                          void* workspace, const VerifyPlan& p, hipStream_t stream);
+
+// Appends each sequence's accepted path (rows of row_bytes bytes) to its
+// cache slot and advances cache_lens; see tree_kv_commit.
+hipError_t launch_kv_commit(const void* k_tree, const void* v_tree, const int32_t* node_offsets,
+                            const int32_t* accept_len, const int32_t* accept_nodes, int B,
+                            int total_nodes, int max_nodes, long long row_bytes, void* k_cache,
+                            void* v_cache, const int64_t* cache_offsets, int64_t* cache_lens,
+                            long long total_cache, int32_t* status, hipStream_t stream);
 
 }  // namespace ta
