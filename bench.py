@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--eager", action="store_true",
                    help="launch every call from Python instead of replaying captured HIP graphs")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra-calls", action="store_true",
+                   help="time only the step's calls (no standalone commit or next-token "
+                        "verifier), so that profiler averages per kernel name cover the step")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a plain 256 MiB device-to-device copy (counter calibration)")
@@ -199,11 +202,11 @@ def summarize_profiles(root):
 
 PROFILE_CMDS = {
     "prof_trace": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o run -- "
-                  "python -u bench.py --steps 50 --warmup 5 --no-cpu-baseline",
+                  "python -u bench.py --steps 50 --warmup 5 --no-cpu-baseline --no-extra-calls",
     "prof_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch -o run -- "
-                  "python -u bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+                  "python -u bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-extra-calls",
     "prof_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_write -o run -- "
-                  "python -u bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+                  "python -u bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-extra-calls",
     "prof_calib_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_calib_fetch -o run -- "
                         "python -u bench.py --calib-copy",
     "prof_calib_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_calib_write -o run -- "
@@ -413,6 +416,20 @@ def main():
     commit_status = torch.empty(B, dtype=torch.int32, device=dev)
     acc_len, acc_nodes = alen.clone(), anodes.clone()
 
+    # The verifier on next-token rows: the same logits read as the token after each
+    # node, plus one prefix row per sequence, and the bonus token.
+    root_rows = torch.randn((B, V), generator=torch.Generator().manual_seed(99)).to(
+        base["logits"].dtype).to(dev)
+    vws_next = torch.empty(max(ta.verify_workspace_size(sum_n + B, max_nodes, V), 16),
+                           dtype=torch.uint8, device=dev)
+    nx = [torch.empty_like(t) for t in (pred, alen, anodes, atok)] + [
+        torch.empty(B, dtype=torch.int32, device=dev)]
+
+    def do_verify_next(s):
+        ta.verify_greedy_next(s["logits"], root_rows, s["draft"], mask, s["noffs"], max_nodes,
+                              workspace=vws_next, target_argmax=nx[0], accept_len=nx[1],
+                              accept_nodes=nx[2], accept_tokens=nx[3], bonus_token=nx[4])
+
     def do_commit(s):
         ta.kv_commit(s["kt"], s["vt"], s["noffs"], acc_len, acc_nodes, k_cache, v_cache,
                      cache_offs, cache_lens, status=commit_status)
@@ -421,8 +438,11 @@ def main():
     t_mask, d_mask = event_time(do_mask, args.steps)
     t_fwd, d_fwd = event_time(fwd_fn, args.steps)
     t_ver, d_ver = event_time(do_verify, args.steps)
-    t_commit, d_commit = event_time(do_commit, args.steps)
-    if not bool((commit_status == 0).all()):
+    t_commit = t_vnext = d_commit = d_vnext = None
+    if not args.no_extra_calls:
+        t_commit, d_commit = event_time(do_commit, args.steps)
+        t_vnext, d_vnext = event_time(do_verify_next, args.steps)
+    if t_commit is not None and not bool((commit_status == 0).all()):
         raise SystemExit("tree_kv_commit reported a failure in the timing loop")
     print(f"[bench] per call us: mask {t_mask:.2f} forward {t_fwd:.2f} verify {t_ver:.2f}",
           file=sys.stderr, flush=True)
@@ -497,10 +517,12 @@ def main():
         "detail": {
             "us_per_call": {fwd_call: round(t_fwd, 3), "tree_verify_greedy": round(t_ver, 3),
                             "tree_attn_build_mask (standalone)": round(t_mask, 3),
-                            "tree_kv_commit (standalone)": round(t_commit, 3)},
+                            "tree_kv_commit (standalone)": t_commit and round(t_commit, 3),
+                            "tree_verify_greedy_next (standalone)": t_vnext and round(t_vnext, 3)},
             "us_per_call_spread": {fwd_call: d_fwd, "tree_verify_greedy": d_ver,
                                    "tree_attn_build_mask (standalone)": d_mask,
-                                   "tree_kv_commit (standalone)": d_commit},
+                                   "tree_kv_commit (standalone)": d_commit,
+                                   "tree_verify_greedy_next (standalone)": d_vnext},
             "commit": {"accepted_rows": int(acc_len.sum()),
                        "alg_bytes": int(acc_len.sum()) * Hkv * D * base["kt"].element_size() * 4},
             "forward": {"tree_tokens_per_s": round(sum_n / (t_fwd * 1e-6), 1),

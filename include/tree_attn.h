@@ -232,6 +232,42 @@ TA_API int tree_verify_greedy(int logits_dtype, const void* logits, const int32_
                        void* stream);
 
 /*
+ * Greedy tree verification on next-token rows: the same acceptance rule as
+ * tree_verify_greedy, with the target's outputs given as they come out of the
+ * verification pass, one row per position for the token that FOLLOWS it.
+ *
+ * Follows: inferensys "Tree Attention", comparison table (the target yields
+ * next-token logits at every node) and Multi-Token Acceptance & Rollback;
+ * premlal listing, verify_candidate_tree (argmax of the target, draft compared
+ * with prediction) and its final step, which counts one more token than the
+ * accepted ones: the target's own prediction after the accepted path.
+ *
+ *   logits         [sum_N][V]; row i: the target's distribution of the token
+ *                  after node i.
+ *   root_logits    [B][V]; row b: the distribution of the token after the
+ *                  prefix of sequence b (what the roots are checked against).
+ *   draft_tokens, mask, node_offsets, B, total_nodes, max_nodes, V,
+ *   accept_len, accept_nodes, accept_tokens: as for tree_verify_greedy.
+ *   target_argmax  out int32 [sum_N], nullable: argmax of each node's row.
+ *   bonus_token    out int32 [B]: argmax of the accepted leaf's row, or of the
+ *                  prefix row when nothing is accepted (the token the step
+ *                  emits after its accepted ones).
+ *   workspace      at least tree_verify_greedy_workspace_size(total_nodes + B,
+ *                  max_nodes, V) bytes.
+ * Node c matches iff draft_tokens[c] equals the argmax of its parent's row (of
+ * the prefix row for a root); ties and the longest-path rule are those of
+ * tree_verify_greedy.  Equivalent to tree_verify_greedy on the rows gathered
+ * so that row c is its parent's (the prefix's for a root).
+ */
+TA_API int tree_verify_greedy_next(int logits_dtype, const void* logits, const void* root_logits,
+                                   const int32_t* draft_tokens, const uint64_t* mask,
+                                   const int32_t* node_offsets, int32_t B, int32_t total_nodes,
+                                   int32_t max_nodes, int32_t V, int32_t* target_argmax,
+                                   int32_t* accept_len, int32_t* accept_nodes,
+                                   int32_t* accept_tokens, int32_t* bonus_token, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * Commit of the accepted path to the KV cache (and rollback of the rest).
  *
  * Follows: inferensys "Tree Attention", Multi-Token Acceptance & Rollback (the

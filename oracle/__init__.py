@@ -29,5 +29,6 @@ from .tree_attention import (  # noqa: F401
     tree_attention,
     target_argmax,
     verify_greedy,
+    verify_greedy_next,
     kv_commit,
 )

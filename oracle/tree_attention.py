@@ -261,6 +261,50 @@ def verify_greedy(logits, draft, parents, node_offsets, max_nodes: int):
     return pred, acc_len, acc_nodes, acc_tok
 
 
+def verify_greedy_next(logits, root_logits, draft, parents, node_offsets, max_nodes: int):
+    """Greedy acceptance on next-token rows, plus the bonus token.
+
+    Row i of ``logits`` is the target's distribution of the token that
+    follows node i; row b of ``root_logits`` that of the token after sequence
+    b's prefix.  A node's draft token must equal the prediction made where the
+    node's token is produced: at its parent (at the prefix for a root).  The
+    longest path of matching nodes from a root wins (lowest terminal index on
+    ties), and the step also emits the target's prediction after the accepted
+    leaf (after the prefix when nothing is accepted).  Returns (pred
+    [sum_N], accept_len [B], accept_nodes [B][max_nodes], accept_tokens
+    [B][max_nodes], bonus [B]).
+    """
+    pred = target_argmax(logits)
+    root_pred = target_argmax(root_logits)
+    draft = np.asarray(draft, dtype=np.int64)
+    parents = np.asarray(parents, dtype=np.int64)
+    node_offsets = np.asarray(node_offsets, dtype=np.int64)
+    B = len(node_offsets) - 1
+    acc_len = np.zeros(B, dtype=np.int32)
+    acc_nodes = np.full((B, max_nodes), -1, dtype=np.int32)
+    acc_tok = np.full((B, max_nodes), -1, dtype=np.int32)
+    bonus = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        lo, hi = int(node_offsets[b]), int(node_offsets[b + 1])
+        par = parents[lo:hi]
+
+        def expected(i):
+            return int(root_pred[b]) if par[i] < 0 else int(pred[lo + int(par[i])])
+
+        match = [bool(draft[lo + i] == expected(i)) for i in range(hi - lo)]
+        best, best_path = -1, []
+        for i in range(hi - lo):
+            path = root_path(par, i)
+            if all(match[j] for j in path) and len(path) > len(best_path):
+                best, best_path = i, path
+        acc_len[b] = len(best_path)
+        for k, j in enumerate(best_path):
+            acc_nodes[b, k] = j
+            acc_tok[b, k] = int(draft[lo + j])
+        bonus[b] = int(pred[lo + best]) if best_path else int(root_pred[b])
+    return pred, acc_len, acc_nodes, acc_tok, bonus
+
+
 # ---------------------------------------------------------------------------
 # Commit of the accepted path ([IS] Multi-Token Acceptance & Rollback,
 #                              Speculative KV Cache Reuse)

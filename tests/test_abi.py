@@ -24,9 +24,9 @@ def lib():
 def test_header_declares_the_three_calls():
     names = _declared_functions()
     for n in ("tree_attn_build_mask", "tree_attn_forward", "tree_verify_greedy",
-              "tree_attn_mask_and_forward", "tree_kv_commit"):
+              "tree_attn_mask_and_forward", "tree_kv_commit", "tree_verify_greedy_next"):
         assert n in names
-    assert len(names) == 8, names
+    assert len(names) == 9, names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -144,3 +144,19 @@ def test_kv_commit_host_validation(lib):
     assert _commit(lib, kc=None) == 1              # cache rows but no cache pointer
     assert _commit(lib, cl=None) == 1              # the lengths are required
     assert _commit(lib, tc=-1) == 1
+
+
+def test_verify_next_host_validation(lib):
+    v = lib.tree_verify_greedy_next
+    ok = [1, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 2, 64, 64, 1000, None, 1 << 20,
+          1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, None]
+    bad = list(ok); bad[0] = 5
+    assert v(*bad) == 3
+    bad = list(ok); bad[2] = None                  # the prefix rows are required
+    assert v(*bad) == 1
+    bad = list(ok); bad[14] = None                 # so is the bonus token
+    assert v(*bad) == 1
+    bad = list(ok); bad[16] = 8                    # workspace for sum_N + B rows
+    assert v(*bad) == 4
+    bad = list(ok); bad[8] = 5000
+    assert v(*bad) == 3

@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     mask_words,
     status_string,
     verify_greedy,
+    verify_greedy_next,
     verify_workspace_size,
 )
 
@@ -37,3 +38,4 @@ tree_attn_forward = forward
 tree_attn_mask_and_forward = mask_and_forward
 tree_verify_greedy = verify_greedy
 tree_kv_commit = kv_commit
+tree_verify_greedy_next = verify_greedy_next

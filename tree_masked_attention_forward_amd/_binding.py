@@ -72,6 +72,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tree_verify_greedy.argtypes = [ctypes.c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                        _i32, _i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
                                        _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p]
+    lib.tree_verify_greedy_next.restype = ctypes.c_int
+    lib.tree_verify_greedy_next.argtypes = [ctypes.c_int] + [_c_void_p] * 5 + [_i32] * 4 + [
+        _c_void_p] * 6 + [ctypes.c_size_t, _c_void_p]
     lib.tree_kv_commit.restype = ctypes.c_int
     lib.tree_kv_commit.argtypes = [ctypes.c_int] + [_c_void_p] * 5 + [_i32] * 5 + [
         _c_void_p] * 4 + [_i64, _c_void_p, _c_void_p]
@@ -305,6 +308,54 @@ def verify_greedy(logits: torch.Tensor, draft_tokens: torch.Tensor, mask: torch.
         int(max_nodes), V, _ptr(target_argmax), _ptr(accept_len), _ptr(accept_nodes),
         _ptr(accept_tokens), _ptr(workspace), ws_len, _stream(dev)))
     return target_argmax, accept_len, accept_nodes, accept_tokens
+
+
+def verify_greedy_next(logits: torch.Tensor, root_logits: torch.Tensor,
+                       draft_tokens: torch.Tensor, mask: torch.Tensor,
+                       node_offsets: torch.Tensor, max_nodes: int, *,
+                       workspace: Optional[torch.Tensor] = None,
+                       target_argmax: Optional[torch.Tensor] = None,
+                       accept_len: Optional[torch.Tensor] = None,
+                       accept_nodes: Optional[torch.Tensor] = None,
+                       accept_tokens: Optional[torch.Tensor] = None,
+                       bonus_token: Optional[torch.Tensor] = None):
+    """tree_verify_greedy_next (row i: the token after node i; root_logits row
+    b: the token after sequence b's prefix).  Returns (target_argmax,
+    accept_len, accept_nodes, accept_tokens, bonus_token)."""
+    dev = _device_of(logits)
+    if logits.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("logits must be bfloat16 or float32")
+    _need(logits, "logits", logits.dtype, dev, 2)
+    _need(root_logits, "root_logits", logits.dtype, dev, 2)
+    total, V = logits.shape
+    _need(draft_tokens, "draft_tokens", torch.int32, dev, 1)
+    _need(mask, "mask", torch.uint64, dev, 2)
+    _need(node_offsets, "node_offsets", torch.int32, dev, 1)
+    B = node_offsets.numel() - 1
+    if tuple(root_logits.shape) != (B, V):
+        raise ValueError("root_logits must be [B, V]")
+    if draft_tokens.numel() != total or mask.shape != (total, mask_words(max_nodes)):
+        raise ValueError("draft_tokens/mask do not match the logits rows")
+    if target_argmax is None:
+        target_argmax = torch.empty(total, dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if accept_nodes is None:
+        accept_nodes = torch.empty((B, max_nodes), dtype=torch.int32, device=dev)
+    if accept_tokens is None:
+        accept_tokens = torch.empty((B, max_nodes), dtype=torch.int32, device=dev)
+    if bonus_token is None:
+        bonus_token = torch.empty(B, dtype=torch.int32, device=dev)
+    ws_bytes = verify_workspace_size(total + B, max_nodes, V)
+    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws_len = workspace.numel() * workspace.element_size()
+    code = TA_BF16 if logits.dtype == torch.bfloat16 else TA_F32
+    _check("tree_verify_greedy_next", load_library().tree_verify_greedy_next(
+        code, _ptr(logits), _ptr(root_logits), _ptr(draft_tokens), _ptr(mask), _ptr(node_offsets),
+        B, total, int(max_nodes), V, _ptr(target_argmax), _ptr(accept_len), _ptr(accept_nodes),
+        _ptr(accept_tokens), _ptr(bonus_token), _ptr(workspace), ws_len, _stream(dev)))
+    return target_argmax, accept_len, accept_nodes, accept_tokens, bonus_token
 
 
 def kv_commit(k_tree: torch.Tensor, v_tree: torch.Tensor, node_offsets: torch.Tensor,

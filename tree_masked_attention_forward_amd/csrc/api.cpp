@@ -263,6 +263,30 @@ int tree_verify_greedy(int logits_dtype, const void* logits, const int32_t* draf
                                       static_cast<hipStream_t>(stream)));
 }
 
+int tree_verify_greedy_next(int logits_dtype, const void* logits, const void* root_logits,
+                            const int32_t* draft_tokens, const uint64_t* mask,
+                            const int32_t* node_offsets, int32_t B, int32_t total_nodes,
+                            int32_t max_nodes, int32_t V, int32_t* target_argmax,
+                            int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
+                            int32_t* bonus_token, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (logits_dtype != TA_BF16 && logits_dtype != TA_F32) return TA_ERR_UNSUPPORTED;
+  if (B <= 0 || total_nodes < 0 || max_nodes < 1 || V <= 0) return TA_ERR_INVALID_ARG;
+  if (max_nodes > TA_MAX_NODES) return TA_ERR_UNSUPPORTED;
+  if (!node_offsets || !accept_len || !accept_nodes || !accept_tokens || !bonus_token ||
+      !root_logits)
+    return TA_ERR_INVALID_ARG;
+  if (total_nodes > 0 && (!logits || !draft_tokens || !mask)) return TA_ERR_INVALID_ARG;
+  const ta::VerifyPlan p = ta::plan_verify(total_nodes + B, V);
+  if (!workspace || workspace_bytes < p.ws_bytes || misaligned16(workspace))
+    return TA_ERR_WORKSPACE;
+  return hip_status(ta::launch_verify(logits_dtype == TA_BF16, logits, draft_tokens, mask,
+                                      node_offsets, B, total_nodes, max_nodes, V, target_argmax,
+                                      accept_len, accept_nodes, accept_tokens, workspace, p,
+                                      static_cast<hipStream_t>(stream), root_logits,
+                                      bonus_token));
+}
+
 int tree_kv_commit(int dtype, const void* k_tree, const void* v_tree,
                    const int32_t* node_offsets, const int32_t* accept_len,
                    const int32_t* accept_nodes, int32_t B, int32_t total_nodes,

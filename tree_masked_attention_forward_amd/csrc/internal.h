@@ -85,7 +85,8 @@ hipError_t launch_verify(bool bf16, const void* logits, const int32_t* draft,
                          const uint64_t* mask, const int32_t* node_offsets, int B,
                          int total_nodes, int max_nodes, int V, int32_t* target_argmax,
                          int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
-                         void* workspace, const VerifyPlan& p, hipStream_t stream);
+                         void* workspace, const VerifyPlan& p, hipStream_t stream,
+                         const void* root_logits = nullptr, int32_t* bonus_token = nullptr);
 
 // Appends each sequence's accepted path (rows of row_bytes bytes) to its
 // cache slot and advances cache_lens; see tree_kv_commit.

@@ -20,6 +20,14 @@
 //       bits (the longest path), lowest index on ties.  The accepted path is
 //       the set bits of that node's mask in increasing order, which is root to
 //       leaf because parents precede children.
+//
+// Next-token rows (tree_verify_greedy_next): row i holds the target's
+// distribution of the token that follows node i, and one more row per
+// sequence that of the token after the prefix.  A node's draft token is then
+// checked against the prediction of its parent's row (a root's against the
+// prefix row); the parent is the highest set bit of the node's mask row below
+// the node itself.  The prediction after the accepted leaf (after the prefix
+// when nothing is accepted) is the bonus token the step emits on top.
 #include "internal.h"
 
 #include <algorithm>
@@ -54,11 +62,18 @@ __device__ inline void wave_best(float& bv, int& bi) {
 // (kUnroll * 256 * VEC elements per pass) at full memory-level parallelism.
 constexpr int kUnroll = 8;
 
+// Rows [0, rows1) come from `logits1`, the rest from `logits2`; partial
+// results go to ws[row][chunk] over both.
 template <bool BF16, int VEC>
-__global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const void* __restrict__ logits,
-                                                                  int V, int cpr, int chunk,
+__global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const void* __restrict__ logits1,
+                                                                  const void* __restrict__ logits2,
+                                                                  long long rows1, int V, int cpr,
+                                                                  int chunk,
                                                                   float2* __restrict__ ws) {
-  const long long row = blockIdx.x / cpr;
+  const long long out_row = blockIdx.x / cpr;
+  const bool first = out_row < rows1;
+  const void* logits = first ? logits1 : logits2;
+  const long long row = first ? out_row : out_row - rows1;
   const int c = blockIdx.x % cpr;
   const int lo = c * chunk;
   const int hi = min(V, lo + chunk);
@@ -131,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const void* __
         bv = sv[w];
         bi = si[w];
       }
-    ws[row * cpr + c] = make_float2(bv, __int_as_float(bi));
+    ws[out_row * cpr + c] = make_float2(bv, __int_as_float(bi));
   }
 }
 
@@ -157,16 +172,19 @@ __device__ inline void load_seq_regs(SeqRegs& r, const float2* ws, const int32_t
   }
 }
 
+template <bool NEXT>
 __global__ __launch_bounds__(kThreads) void path_select_kernel(
     const float2* __restrict__ ws, int cpr, const int32_t* __restrict__ draft,
     const uint64_t* __restrict__ mask, const int32_t* __restrict__ node_offsets,
     int total_nodes, int max_nodes, int W, int32_t* __restrict__ target_argmax,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
-    int32_t* __restrict__ accept_tokens) {
+    int32_t* __restrict__ accept_tokens, const float2* __restrict__ ws_root,
+    int32_t* __restrict__ bonus_token) {
   extern __shared__ uint64_t rows[];   // [nn][W] mask rows of the sequence
   __shared__ int32_t tgt[TA_MAX_NODES];
   __shared__ uint64_t match_w[(TA_MAX_NODES + 63) / 64];
   __shared__ unsigned long long red[kThreads / 64];
+  __shared__ int32_t root_pred;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -223,12 +241,37 @@ __global__ __launch_bounds__(kThreads) void path_select_kernel(
     const int pidx = p0 + tid;
     reduce_pass(pidx, pidx < pairs ? ws[(size_t)n0 * cpr + pidx] : make_float2(0.f, 0.f));
   }
+  if (NEXT && wave == 0) {
+    // The prefix row's chunks (cpr <= 64 of them) in the first wave.
+    float bv = kNegInf;
+    int bi = 0x7fffffff;
+    if (lane < cpr) {
+      const float2 x = ws_root[(size_t)b * cpr + lane];
+      bv = x.x;
+      bi = __float_as_int(x.y);
+    }
+    wave_best(bv, bi);
+    if (lane == 0) root_pred = bi;
+  }
   __syncthreads();
 
   // Match set: node i matches iff its draft token is the target's argmax.
   // Thread t, slot k holds node t + 256k, so wave w's ballot is word 4k + w.
+  auto expected = [&](int i) {
+    if constexpr (NEXT) {
+      // parent = highest ancestor index below i (parents precede children)
+      for (int w = i >> 6; w >= 0; --w) {
+        uint64_t mw = rows[i * W + w];
+        if (w == (i >> 6)) mw &= (1ull << (i & 63)) - 1ull;
+        if (mw) return tgt[64 * w + 63 - __builtin_clzll(mw)];
+      }
+      return root_pred;
+    } else {
+      return tgt[i];
+    }
+  };
   auto match_pass = [&](int i, int32_t d) {
-    const bool m = i < nn && d == tgt[i < nn ? i : 0];
+    const bool m = i < nn && d == expected(i < nn ? i : 0);
     const uint64_t bits = __ballot(m);
     if (lane == 0 && 64 * (i >> 6) < nn) match_w[i >> 6] = bits;
   };
@@ -302,7 +345,10 @@ __global__ __launch_bounds__(kThreads) void path_select_kernel(
       place(j, j < nn ? draft[n0 + j] : -1);
     }
   }
-  if (tid == 0) accept_len[b] = len;
+  if (tid == 0) {
+    accept_len[b] = len;
+    if (NEXT) bonus_token[b] = len > 0 ? tgt[best] : root_pred;
+  }
 }
 
 }  // namespace
@@ -325,42 +371,66 @@ VerifyPlan plan_verify(int total_nodes, int V) {
   return p;
 }
 
+namespace {
+
+hipError_t launch_argmax(bool bf16, const void* logits1, long long rows1,
+                         const void* logits2, long long rows2, int V, const VerifyPlan& p,
+                         float2* ws, hipStream_t stream) {
+  const long long rows = rows1 + rows2;
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)(rows * p.cpr));
+  const auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  const bool aligned = al(logits1) && (rows2 == 0 || al(logits2));
+  if (bf16) {
+    if (aligned && V % 8 == 0)
+      hipLaunchKernelGGL((argmax_partial_kernel<true, 8>), grid, dim3(kThreads), 0, stream,
+                         logits1, logits2, rows1, V, p.cpr, p.chunk, ws);
+    else
+      hipLaunchKernelGGL((argmax_partial_kernel<true, 1>), grid, dim3(kThreads), 0, stream,
+                         logits1, logits2, rows1, V, p.cpr, p.chunk, ws);
+  } else {
+    if (aligned && V % 4 == 0)
+      hipLaunchKernelGGL((argmax_partial_kernel<false, 4>), grid, dim3(kThreads), 0, stream,
+                         logits1, logits2, rows1, V, p.cpr, p.chunk, ws);
+    else
+      hipLaunchKernelGGL((argmax_partial_kernel<false, 1>), grid, dim3(kThreads), 0, stream,
+                         logits1, logits2, rows1, V, p.cpr, p.chunk, ws);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_verify(bool bf16, const void* logits, const int32_t* draft,
                          const uint64_t* mask, const int32_t* node_offsets, int B,
                          int total_nodes, int max_nodes, int V, int32_t* target_argmax,
                          int32_t* accept_len, int32_t* accept_nodes, int32_t* accept_tokens,
-                         void* workspace, const VerifyPlan& p, hipStream_t stream) {
+                         void* workspace, const VerifyPlan& p, hipStream_t stream,
+                         const void* root_logits, int32_t* bonus_token) {
   float2* ws = static_cast<float2*>(workspace);
+  float2* ws_root = ws + (size_t)total_nodes * p.cpr;
   const int W = (max_nodes + 63) / 64;
-  if (total_nodes > 0) {
-    const dim3 grid((unsigned)((long long)total_nodes * p.cpr));
-    const bool aligned = (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
-    if (bf16) {
-      if (aligned && V % 8 == 0)
-        hipLaunchKernelGGL((argmax_partial_kernel<true, 8>), grid, dim3(kThreads), 0, stream,
-                           logits, V, p.cpr, p.chunk, ws);
-      else
-        hipLaunchKernelGGL((argmax_partial_kernel<true, 1>), grid, dim3(kThreads), 0, stream,
-                           logits, V, p.cpr, p.chunk, ws);
-    } else {
-      if (aligned && V % 4 == 0)
-        hipLaunchKernelGGL((argmax_partial_kernel<false, 4>), grid, dim3(kThreads), 0, stream,
-                           logits, V, p.cpr, p.chunk, ws);
-      else
-        hipLaunchKernelGGL((argmax_partial_kernel<false, 1>), grid, dim3(kThreads), 0, stream,
-                           logits, V, p.cpr, p.chunk, ws);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  // One launch over the node rows and, for next-token rows, the prefix rows.
+  hipError_t e = launch_argmax(bf16, logits, total_nodes, root_logits, root_logits ? B : 0, V, p,
+                               ws, stream);
+  if (e != hipSuccess) return e;
   const size_t lds = (size_t)max_nodes * W * sizeof(uint64_t);
+  const void* kern = root_logits ? reinterpret_cast<const void*>(&path_select_kernel<true>)
+                                 : reinterpret_cast<const void*>(&path_select_kernel<false>);
   if (lds > 32 * 1024) {
-    hipError_t e = raise_dynamic_lds(reinterpret_cast<const void*>(&path_select_kernel), (int)lds);
+    e = raise_dynamic_lds(kern, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(path_select_kernel, dim3(B), dim3(kThreads), lds, stream, ws, p.cpr, draft,
-                     mask, node_offsets, total_nodes, max_nodes, W, target_argmax, accept_len,
-                     accept_nodes, accept_tokens);
+  if (root_logits)
+    hipLaunchKernelGGL(path_select_kernel<true>, dim3(B), dim3(kThreads), lds, stream, ws,
+                       p.cpr, draft, mask, node_offsets, total_nodes, max_nodes, W,
+                       target_argmax, accept_len, accept_nodes, accept_tokens, ws_root,
+                       bonus_token);
+  else
+    hipLaunchKernelGGL(path_select_kernel<false>, dim3(B), dim3(kThreads), lds, stream, ws,
+                       p.cpr, draft, mask, node_offsets, total_nodes, max_nodes, W,
+                       target_argmax, accept_len, accept_nodes, accept_tokens, nullptr,
+                       nullptr);
   return hipGetLastError();
 }
 
