@@ -368,8 +368,12 @@ struct LdsMap {
   static_assert(kBytes <= kLdsMax, "LDS budget");
 };
 
+// At most two waves per SIMD (eight waves per workgroup, and the LDS holds one
+// workgroup per CU): telling the compiler so lets it schedule for latency
+// instead of trying to fit more waves.
 template <int RG, int KG, int TPW, int NS, bool MR>
-__global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
+__global__ __launch_bounds__(RG * KG * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_bf16_kernel(KParams P) {
   static_assert(NS >= 3 && NS <= 4, "ring depth");
   constexpr int NW = RG * KG;
   constexpr int NT = NW * 64;
@@ -789,7 +793,9 @@ __global__ __launch_bounds__(RG * KG * 64) void fwd_bf16_kernel(KParams P) {
     for (int j = 0; j < TPW; ++j) {
       tl[j] = t_lo + (it * KG + kg) * TPW + j;
       ac[j] = group_active && tl[j] < t_hi;
-      if (ac[j]) sc[j] = qk(st + (kg * TPW + j) * kTileBytes);
+      // Unconditional, so the MFMA chains of the wave's tiles share one basic
+      // block (an idle tile's scores come from in-bounds rows and are dropped).
+      sc[j] = qk(st + (kg * TPW + j) * kTileBytes);
     }
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
