@@ -61,6 +61,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a plain 256 MiB device-to-device copy (counter calibration)")
+    p.add_argument("--summarize-configs", metavar="DIR",
+                   help="write profiles/tree_attn_forward_configs.md from the per-workload runs "
+                        "under DIR (see CONFIG_CMDS)")
     p.add_argument("--summarize-profiles", metavar="DIR",
                    help="write profiles/ summaries from rocprofv3 CSV output under DIR")
     return p.parse_args()
@@ -214,10 +217,62 @@ PROFILE_CMDS = {
 }
 
 
+# Per-workload runs: the bench line (per-call HIP-event times) and a kernel trace.
+CONFIG_NAMES = ("llama3_8b", "batched", "llama3_70b", "forest")
+CONFIG_CMDS = {
+    "bench": "python -u bench.py --config {name} --steps 30 --warmup 5 --no-cpu-baseline "
+             "> gpurun_out/cfg_{name}.json",
+    "trace": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/cfg_trace_{name} -o run -- "
+             "python -u bench.py --config {name} --steps 10 --warmup 2 --no-cpu-baseline "
+             "--no-extra-calls",
+}
+
+
+def summarize_configs(root):
+    """One table over the workloads: the forward call's device time (HIP events, p50
+    over graph replays, and the kernel-trace average of its kernels), its algorithmic
+    rate against the roof that bounds it, and the verifier's time."""
+    rows = []
+    for name in CONFIG_NAMES:
+        try:
+            with open(os.path.join(root, f"cfg_{name}.json")) as f:
+                line = json.loads(f.read().strip().splitlines()[-1])
+        except (OSError, ValueError, IndexError):
+            continue
+        d = line["detail"]
+        fwd_call = line["roofline"]["kernel"] if line["roofline"]["kernel"] != "tree_verify_greedy" \
+            else line["detail"]["roofline_other"]["kernel"]
+        fw = d["forward"]
+        r = line["roofline"] if line["roofline"]["kernel"] == fwd_call else d["roofline_other"]
+        stats = _read_csvs(os.path.join(root, f"cfg_trace_{name}"), "kernel_stats.csv")
+        fwd_ns = sum(float(x["AverageNs"]) for x in stats
+                     if "fwd_bf16_kernel" in x["Name"] or "merge_bf16_kernel" in x["Name"])
+        rows.append(f"| {name} | {line['config']['workload'].split(';')[0]} | "
+                    f"{d['us_per_call_spread'][fwd_call]['p50']:.1f} | {fwd_ns / 1e3:.1f} | "
+                    f"{r['achieved']} {r['unit']} | {r['bound']} | {r['frac']:.3f} | "
+                    f"{fw['t_roof_us']:.1f} | {d['us_per_call']['tree_verify_greedy']:.1f} |")
+    md = ["# Forward call on every workload (MI355X, one GPU)", "",
+          "Commands (repository root, MI355X box), for each workload name:", "",
+          "    " + CONFIG_CMDS["bench"], "    " + CONFIG_CMDS["trace"], "",
+          "Times in microseconds per call. `events p50`: median over graph replays of the call on",
+          "resident inputs (HIP events on the launch stream); `trace`: kernel-trace average of",
+          "the forward's kernels (split kernel + merge kernel where there is one). The rate and",
+          "fraction are the algorithmic bytes or flops per call over the events mean, against",
+          "8 TB/s HBM or 2.5 PFLOP/s dense bf16 MFMA, whichever bounds the workload.", "",
+          "| workload | shape | events p50 | trace | achieved | bound | roofline frac | roof | verify |",
+          "|---|---|---|---|---|---|---|---|---|"] + rows
+    with open(os.path.join(PROFILES, "tree_attn_forward_configs.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
 def main():
     args = parse()
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles)
+        return
+    if args.summarize_configs:
+        summarize_configs(args.summarize_configs)
         return
     if args.calib_copy:
         calib_copy()
