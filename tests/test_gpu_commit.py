@@ -131,3 +131,42 @@ def test_verify_commit_next_step_continues_the_tree(ta):
     ro, rl = oracle.tree_attention(c.q, c.k_tree, c.v_tree, c.k_prefix, c.v_prefix, c.parents,
                                    c.node_offsets, c.prefix_offsets, c.scale, nodes=leaf)
     check_attention(out, lse, ro, rl, fp32=False, what="next step after commit")
+
+
+def test_commit_replayed_from_a_graph_appends_each_time(ta):
+    """The commit keeps its lengths on the device, so a captured graph can
+    replay it: each replay appends the accepted path once more, after the
+    rows the previous replays appended."""
+    rng = np.random.default_rng(40)
+    trees = [synthetic.random_tree(rng, 20, 1, 5, 3).tolist() for _ in range(2)]
+    c = synthetic.make_case("gcommit", prefix_lens=[10, 3], trees=trees, Hq=8, Hkv=8, D=128,
+                            seed=40)
+    reps = 4
+    kc, vc, offs, L = _slotted_cache(c, [reps * 8, reps * 8], 41, torch.bfloat16)
+    acc = np.zeros(2, dtype=np.int32)
+    nodes = np.full((2, 20), -1, dtype=np.int32)
+    for b in range(2):
+        n0, n1 = int(c.node_offsets[b]), int(c.node_offsets[b + 1])
+        path = oracle.root_path(c.parents[n0:n1], int(rng.integers(n1 - n0)))
+        nodes[b, :len(path)] = path
+        acc[b] = len(path)
+    d = torch.device("cuda")
+    args = [c.k_tree.to(d), c.v_tree.to(d), torch.from_numpy(c.node_offsets).to(d),
+            torch.from_numpy(acc).to(d), torch.from_numpy(nodes).to(d)]
+    kc_d, vc_d = kc.to(d), vc.to(d)
+    offs_d, lens_d = torch.from_numpy(offs).to(d), torch.from_numpy(L).to(d)
+    status = torch.empty(2, dtype=torch.int32, device=d)
+    ta.kv_commit(*args, kc_d, vc_d, offs_d, lens_d, status=status)   # eager once
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ta.kv_commit(*args, kc_d, vc_d, offs_d, lens_d, status=status)
+    ref_k, ref_v, ref_len = kc, vc, L
+    for _ in range(reps):   # the eager call, then reps - 1 replays
+        ref_k, ref_v, ref_len, st = oracle.kv_commit(c.k_tree, c.v_tree, c.node_offsets, acc,
+                                                     nodes, ref_k, ref_v, offs, ref_len, 20)
+    for _ in range(reps - 1):
+        g.replay()
+        torch.cuda.synchronize()
+    assert status.cpu().tolist() == [0, 0]
+    assert lens_d.cpu().tolist() == ref_len.tolist() == (L + reps * acc).tolist()
+    assert torch.equal(kc_d.cpu(), ref_k) and torch.equal(vc_d.cpu(), ref_v)

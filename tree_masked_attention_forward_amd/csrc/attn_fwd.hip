@@ -43,7 +43,16 @@
 // sum (fp32) in the workspace, in the MFMA register layout so every store is
 // coalesced, and the splits are combined by log-sum-exp: by merge workgroups
 // at the end of the same grid when there are few groups (see
-// merge_in_kernel), else by a separate merge kernel.
+// merge_in_kernel; items then run head-major, so a group's splits share an
+// XCD), else by a separate merge kernel.
+//
+// Mask bits: a tree tile's 32-bit mask half per lane rides in the stage, or,
+// for trees of up to 128 nodes (MR), each lane keeps its node's whole row in
+// registers.  With MR the kernel can also build those rows itself from the
+// parent array (tree_attn_mask_and_forward: the node and its parent chain,
+// the same relation as the separate mask builder) while its first tiles load.
+// A sequence's prefix is the range prefix_offsets[b] .. [b+1], or the first
+// prefix_lens[b] rows of it when the prefix is a cache slot.
 #include "internal.h"
 
 #include <math.h>
