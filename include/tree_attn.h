@@ -21,8 +21,11 @@
  *
  * Conventions shared by every call:
  *   - Array arguments are DEVICE pointers unless marked [host].  Every buffer is
- *     allocated and owned by the caller; the library allocates nothing, keeps
- *     no state between calls, and never synchronises the stream.
+ *     allocated and owned by the caller; the library allocates nothing and
+ *     never synchronises the stream.  Its only state between calls is a
+ *     record, per device, of the kernels whose dynamic-LDS limit it has raised
+ *     and of the device's compute-unit count (so later launches make no such
+ *     runtime call and can be captured in a HIP graph).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     All work is enqueued on it; the call returns before the work finishes.
  *   - Return value: TA_OK, or an error code for anything the host can check

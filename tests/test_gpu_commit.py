@@ -170,3 +170,21 @@ def test_commit_replayed_from_a_graph_appends_each_time(ta):
     assert status.cpu().tolist() == [0, 0]
     assert lens_d.cpu().tolist() == ref_len.tolist() == (L + reps * acc).tolist()
     assert torch.equal(kc_d.cpu(), ref_k) and torch.equal(vc_d.cpu(), ref_v)
+
+
+def test_fp32_forward_reads_only_the_rows_in_use_of_each_slot(ta):
+    rng = np.random.default_rng(50)
+    trees = [synthetic.random_tree(rng, n, 1, 5, 3).tolist() for n in (6, 19)]
+    c = synthetic.make_case("slot32", prefix_lens=[40, 0], trees=trees, Hq=6, Hkv=2, D=72,
+                            dtype=torch.float32, seed=50)
+    kc, vc, offs, L = _slotted_cache(c, [9, 4], 51, torch.float32)
+    ro, rl = oracle.tree_attention(c.q, c.k_tree, c.v_tree, c.k_prefix, c.v_prefix, c.parents,
+                                   c.node_offsets, c.prefix_offsets, c.scale)
+    dc = DevCase(c)
+    mask, _, _ = ta.build_mask(dc.parents, dc.node_offsets, dc.max_nodes)
+    d = torch.device("cuda")
+    out, lse = ta.forward(dc.q, dc.k_tree, dc.v_tree, kc.to(d), vc.to(d),
+                          torch.from_numpy(offs).to(d), dc.node_offsets, mask, dc.max_nodes,
+                          int(L.max()), c.scale, return_lse=True,
+                          prefix_lens=torch.from_numpy(L).to(d))
+    check_attention(out, lse, ro, rl, fp32=True, what="fp32 slotted prefix")
