@@ -631,10 +631,14 @@ void fwd_bf16_kernel(KParams P) {
     return sacc;
   };
 
-  // Mask, online softmax and O^T += V^T P^T for one tile whose scores are in
-  // sacc and whose V rows start at vb.
-  auto softmax_pv = [&](f32x16_t sacc, const unsigned char* vb, int tile, uint32_t mbits) {
-    if (tile >= Lt) {
+  // Masking of one tile's scores: an idle tile (beyond the split, or an idle
+  // row group) is all -inf; a tree tile keeps the row node's ancestors; the
+  // prefix's partial last tile drops the keys past the prefix.
+  auto mask_tile = [&](f32x16_t& sacc, int tile, uint32_t mbits, bool active) {
+    if (!active) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[v] = kNegInf;
+    } else if (tile >= Lt) {
       const uint32_t bits = row_ok ? mbits : 0u;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -648,11 +652,20 @@ void fwd_bf16_kernel(KParams P) {
         if (tile * kKT + key >= L) sacc[v] = kNegInf;
       }
     }
-    float mt = sacc[0];
+  };
+
+  // Online softmax and O^T += V^T P^T over the wave's TPW tiles of a stage,
+  // taken as one block of keys: one max, one lazy-reference decision and at
+  // most one rescale per stage, and the exponentials of one tile can overlap
+  // the PV MFMAs of the other.
+  auto softmax_pv = [&](f32x16_t (&sc)[TPW], const unsigned char* const (&vb)[TPW]) {
+    float mt = sc[0][0];
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mt = fmaxf(mt, sacc[v]);
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sc[j][v]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    // Lazy running max: the reference moves only when the tile's max exceeds
+    // Lazy running max: the reference moves only when the block's max exceeds
     // it by more than kLazyLog2 (log2 units), so after the first tiles the
     // output is almost never rescaled; probabilities stay below 2^kLazyLog2
     // and numerator and denominator share the reference, so the result is
@@ -664,51 +677,54 @@ void fwd_bf16_kernel(KParams P) {
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
     const float alpha = move ? fast_exp2((m_old - m_use) * c2) : 1.f;
     const float mc = m_use * c2;
-    float ps = 0.f;
-    f32x16_t p;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      p[v] = fast_exp2(fmaf(sacc[v], c2, -mc));
-      ps += p[v];
-    }
-    l_run = fmaf(l_run, alpha, ps);
     if (__ballot(move)) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[e][v] *= alpha;
     }
-    // Two 16-key steps x four 32-dim blocks; one address add per dim block,
-    // the key offsets are immediates.
-    bf16x8_t pb[2];
+    float ps = 0.f;
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      f32x8_t pf;
+    for (int j = 0; j < TPW; ++j) {
+      f32x16_t p;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pf[j] = p[8 * cc + j];
-      pb[cc] = __builtin_convertvector(pf, bf16x8_t);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const unsigned char* ve = vb + voff[e];
+      for (int v = 0; v < 16; ++v) {
+        p[v] = fast_exp2(fmaf(sc[j][v], c2, -mc));
+        ps += p[v];
+      }
+      // Two 16-key steps x four 32-dim blocks; one address add per dim block,
+      // the key offsets are immediates.
+      bf16x8_t pb[2];
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        // slots 0-3: keys 16cc+4hh+0..3, slots 4-7: keys 16cc+8+4hh+0..3
-        const i16x4_t lo = lds_read_tr16(ve + 16 * cc * kRow);
-        const i16x4_t hi = lds_read_tr16(ve + (16 * cc + 8) * kRow);
-        const i16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb[cc],
-                                                          oacc[e], 0, 0, 0);
+        f32x8_t pf;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) pf[q] = p[8 * cc + q];
+        pb[cc] = __builtin_convertvector(pf, bf16x8_t);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned char* ve = vb[j] + voff[e];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          // slots 0-3: keys 16cc+4hh+0..3, slots 4-7: keys 16cc+8+4hh+0..3
+          const i16x4_t lo = lds_read_tr16(ve + 16 * cc * kRow);
+          const i16x4_t hi = lds_read_tr16(ve + (16 * cc + 8) * kRow);
+          const i16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                            pb[cc], oacc[e], 0, 0, 0);
+        }
       }
     }
+    l_run = fmaf(l_run, alpha, ps);
   };
 
   // Pipeline: stage it is computed while stages it+1 .. it+NS-2 are in
   // flight; stage it+NS-1 goes to slot (it-1) % NS, which every wave finished
   // reading before the barrier of stage it.  Each wave takes TPW consecutive
-  // tiles per stage: all their scores first, then softmax + PV of each, in
-  // one basic block, so the scheduler can fill the MFMA chains of one tile
-  // with the VALU work of the other.
+  // tiles per stage: all their scores first, then one softmax over them and
+  // the PV of each, in one basic block, so the scheduler can fill the MFMA
+  // chains of one tile with the VALU work of the other.
   // The query (and mask) loads precede stage 0, so the first stage wait
   // retires them.
   uint32_t mw[4] = {0u, 0u, 0u, 0u};   // MR: this lane's mask row, 32 nodes per dword
@@ -806,20 +822,23 @@ void fwd_bf16_kernel(KParams P) {
       // block (an idle tile's scores come from in-bounds rows and are dropped).
       sc[j] = qk(st + (kg * TPW + j) * kTileBytes);
     }
+    bool any = false;
+    const unsigned char* vbs[TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
-      if (ac[j]) {
-        uint32_t mbits;
-        if constexpr (MR) {
-          const int d = tl[j] - Lt;   // uniform; only tree tiles (d >= 0) use the bits
-          mbits = d <= 0 ? mw[0] : d == 1 ? mw[1] : d == 2 ? mw[2] : mw[3];
-        } else {
-          mbits = *reinterpret_cast<const uint32_t*>(st + kMaskOff + (wave * TPW + j) * 256 +
-                                                     lane * 4);
-        }
-        softmax_pv(sc[j], st + (kg * TPW + j) * kTileBytes + kTileKV, tl[j], mbits);
+      any = any || ac[j];
+      uint32_t mbits;
+      if constexpr (MR) {
+        const int d = tl[j] - Lt;   // uniform; only tree tiles (d >= 0) use the bits
+        mbits = d <= 0 ? mw[0] : d == 1 ? mw[1] : d == 2 ? mw[2] : mw[3];
+      } else {
+        mbits = *reinterpret_cast<const uint32_t*>(st + kMaskOff + (wave * TPW + j) * 256 +
+                                                   lane * 4);
       }
+      mask_tile(sc[j], tl[j], mbits, ac[j]);
+      vbs[j] = st + (kg * TPW + j) * kTileBytes + kTileKV;
     }
+    if (any) softmax_pv(sc, vbs);
   }
   if (MR && P.build && g == 0 && s == 0) {
     // One writer per node: the workgroups of KV head 0 and split 0, the lane
