@@ -188,3 +188,21 @@ def test_fp32_forward_reads_only_the_rows_in_use_of_each_slot(ta):
                           int(L.max()), c.scale, return_lse=True,
                           prefix_lens=torch.from_numpy(L).to(d))
     check_attention(out, lse, ro, rl, fp32=True, what="fp32 slotted prefix")
+
+
+def test_commit_longest_path_at_the_node_limit(ta):
+    """A 1024-node chain accepted whole: every source index slot is used."""
+    n = 1024
+    c = synthetic.make_case("chain", prefix_lens=[5], trees=[[-1] + list(range(n - 1))], Hq=2,
+                            Hkv=2, D=16, dtype=torch.float32, seed=60)
+    kc, vc, offs, L = _slotted_cache(c, [n + 3], 61, torch.float32)
+    acc = np.array([n], dtype=np.int32)
+    nodes = np.arange(n, dtype=np.int32)[None, :]
+    ref = oracle.kv_commit(c.k_tree, c.v_tree, c.node_offsets, acc, nodes, kc, vc, offs, L, n)
+    d = torch.device("cuda")
+    kc_d, vc_d, lens_d = kc.to(d), vc.to(d), torch.from_numpy(L).to(d)
+    st = ta.kv_commit(c.k_tree.to(d), c.v_tree.to(d), torch.from_numpy(c.node_offsets).to(d),
+                      torch.from_numpy(acc).to(d), torch.from_numpy(nodes).to(d), kc_d, vc_d,
+                      torch.from_numpy(offs).to(d), lens_d)
+    assert st.cpu().tolist() == [0] and lens_d.cpu().tolist() == ref[2].tolist() == [5 + n]
+    assert torch.equal(kc_d.cpu(), ref[0]) and torch.equal(vc_d.cpu(), ref[1])

@@ -103,3 +103,17 @@ def test_verify_next_equals_same_row_verifier_on_gathered_rows(ta):
     np.testing.assert_array_equal(alen.cpu().numpy(), ref[1])
     np.testing.assert_array_equal(anodes.cpu().numpy(), ref[2])
     np.testing.assert_array_equal(atok.cpu().numpy(), ref[3])
+
+
+def test_verify_next_at_the_node_limit(ta):
+    """A 1024-node chain and a 1024-node forest (16 mask words per row): the
+    parent search walks down through every word."""
+    rng = np.random.default_rng(70)
+    trees = [[-1] + list(range(1023)), synthetic.random_tree(rng, 1024, 5, 40, 3).tolist()]
+    V = 300
+    c = synthetic.make_case("nbig", prefix_lens=[0, 0], trees=trees, Hq=1, Hkv=1, D=8,
+                            dtype=torch.float32, seed=70, vocab=V)
+    root_logits = torch.randn((2, V), generator=torch.Generator().manual_seed(71))
+    draft = _draft_following(c, root_logits, rng, 0.995)
+    _, _, ref = _run(ta, c, root_logits, draft)
+    print(f"[verify next] accept_len={ref[1].tolist()}", flush=True)
