@@ -61,6 +61,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a plain 256 MiB device-to-device copy (counter calibration)")
+    p.add_argument("--summarize-mfma", metavar="DIR",
+                   help="write profiles/tree_attn_forward_mfma.md from the MfmaUtil runs under DIR "
+                        "(see MFMA_CMD)")
     p.add_argument("--summarize-configs", metavar="DIR",
                    help="write profiles/tree_attn_forward_configs.md from the per-workload runs "
                         "under DIR (see CONFIG_CMDS)")
@@ -266,6 +269,53 @@ def summarize_configs(root):
     print("\n".join(md))
 
 
+MFMA_CMD = ("rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 -f csv -d gpurun_out/mfma_{name} "
+            "-o run -- python -u bench.py --config {name} --steps 10 --warmup 2 --no-cpu-baseline "
+            "--no-extra-calls")
+
+
+def summarize_mfma(root):
+    """MFMA evidence for the forward kernel: the share of cycles the matrix units are
+    busy (rocprofv3's MfmaUtil: SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs) and
+    the MFMA work executed (SQ_INSTS_VALU_MFMA_MOPS_BF16, 512 flops per unit) against the
+    algorithmic flops (taken from the per-workload bench line in the same directory)."""
+    lines = ["# MFMA use of the forward kernel (rocprofv3 counters)", "",
+             "Command (repository root, MI355X box), per workload name:", "",
+             "    " + MFMA_CMD, "",
+             "`MfmaUtil`: mean over the dispatches of the split kernel of the cycles its matrix",
+             "units are busy, as a share of the cycles the GPU is active times the SIMD count.",
+             "`executed`: MFMA flops the kernel issued (MOPS x 512); `algorithmic`: the dense",
+             "prefix and visible tree pairs only; the excess is padding keys and masked tree keys.", "",
+             "| workload | kernel | dispatches | MfmaUtil % | executed GFLOP | algorithmic GFLOP |",
+             "|---|---|---|---|---|---|"]
+    for name in CONFIG_NAMES:
+        acc = {}
+        for r in _read_csvs(os.path.join(root, f"mfma_{name}"), "counter_collection.csv"):
+            if "fwd_bf16_kernel" not in r["Kernel_Name"]:
+                continue
+            short = r["Kernel_Name"].replace("ta::(anonymous namespace)::", "").replace(
+                "void ", "").split("(")[0]
+            acc.setdefault((short, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+        if not acc:
+            continue
+        alg = None
+        try:
+            with open(os.path.join(root, f"cfg_{name}.json")) as f:
+                alg = json.loads(f.read().strip().splitlines()[-1])["detail"]["forward"]["alg_flops"]
+        except (OSError, ValueError, IndexError, KeyError):
+            pass
+        for kname in sorted({k for k, _ in acc}):
+            util = acc.get((kname, "MfmaUtil"), [])
+            mops = acc.get((kname, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), [])
+            u = sum(util) / len(util) if util else float("nan")
+            ex = sum(mops) / len(mops) * 512 / 1e9 if mops else float("nan")
+            lines.append(f"| {name} | `{kname}` | {len(util)} | {u:.1f} | {ex:.2f} | "
+                         f"{'' if alg is None else f'{alg / 1e9:.2f}'} |")
+    with open(os.path.join(PROFILES, "tree_attn_forward_mfma.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
     if args.summarize_profiles:
@@ -273,6 +323,9 @@ def main():
         return
     if args.summarize_configs:
         summarize_configs(args.summarize_configs)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
         return
     if args.calib_copy:
         calib_copy()
