@@ -38,7 +38,8 @@
  *   - Tensors are contiguous, row-major in the layouts given, 16-byte aligned.
  *   - sum_N = total_nodes = node_offsets[B]; sum_L = total_prefix =
  *     prefix_offsets[B]; W = ceil(max_nodes / 64) mask words per node.
- *   - Limits: 1 <= max_nodes <= TA_MAX_NODES; bf16 attention needs D == 128;
+ *   - Limits: 1 <= max_nodes <= TA_MAX_NODES (4096 nodes per sequence, W <= 64
+ *     mask words per row); bf16 attention needs D == 128;
  *     fp32 attention needs 1 <= D <= 256; Hq % Hkv == 0.
  */
 #ifndef TREE_ATTN_H
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define TA_MAX_NODES 1024
+#define TA_MAX_NODES 4096
 
 #if defined(__GNUC__) || defined(__clang__)
 #define TA_API __attribute__((visibility("default")))
@@ -92,6 +93,9 @@ typedef enum { TA_F32 = 0, TA_BF16 = 1 } ta_dtype;
  *          its offsets are decreasing, exceed max_nodes or total_nodes (then
  *          its rows are not written).
  * The mask is computed once per verification step and reused by every layer.
+ * Up to 1024 nodes one workgroup per sequence builds the rows in LDS by
+ * pointer jumping; larger trees are split over workgroups of 64 rows, each
+ * walking its rows' parent chains (time grows with the tree's depth).
  */
 TA_API int tree_attn_build_mask(const int32_t* parents, const int32_t* node_offsets, int32_t B,
                          int32_t total_nodes, int32_t max_nodes, uint64_t* mask,

@@ -61,7 +61,7 @@ def test_forward_host_validation(lib):
     assert _fwd(lib, Hq=30, Hkv=8) == 1            # Hq % Hkv != 0
     assert _fwd(lib, D=64) == 3                    # bf16 path needs D == 128
     assert _fwd(lib, dtype=0, D=300) == 3          # fp32 path: D <= 256
-    assert _fwd(lib, maxn=2000) == 3               # above TA_MAX_NODES
+    assert _fwd(lib, maxn=5000) == 3               # above TA_MAX_NODES
     assert _fwd(lib, q=None) == 1
     assert _fwd(lib, kp=None) == 1                 # prefix rows but no prefix pointer
     assert _fwd(lib, q=(1 << 20) + 2) == 1         # misaligned bf16 pointer
@@ -83,7 +83,7 @@ def test_workspace_queries_are_pure_host(lib):
 
 def test_build_mask_and_verify_host_validation(lib):
     assert lib.tree_attn_build_mask(1 << 20, 1 << 20, 0, 5, 5, 1 << 20, None, None, None) == 1
-    assert lib.tree_attn_build_mask(1 << 20, 1 << 20, 1, 5, 4096, 1 << 20, None, None, None) == 3
+    assert lib.tree_attn_build_mask(1 << 20, 1 << 20, 1, 5, 4097, 1 << 20, None, None, None) == 3
     assert lib.tree_attn_build_mask(None, 1 << 20, 1, 5, 5, 1 << 20, None, None, None) == 1
     v = lib.tree_verify_greedy
     ok = [1, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1, 64, 64, 1000, None, 1 << 20, 1 << 20,
@@ -115,7 +115,7 @@ def _mfwd(lib, **kw):
 def test_mask_and_forward_host_validation(lib):
     assert _mfwd(lib, dtype=7) == 3
     assert _mfwd(lib, Hq=30, Hkv=8) == 1
-    assert _mfwd(lib, maxn=2000) == 3
+    assert _mfwd(lib, maxn=5000) == 3
     assert _mfwd(lib, q=None) == 1
     assert _mfwd(lib, par=None) == 1               # parents are required
     assert _mfwd(lib, mask=None) == 1              # the mask is an output here

@@ -24,7 +24,7 @@ TA_ERR_WORKSPACE = 4
 TA_ERR_HIP = 5
 TA_F32 = 0
 TA_BF16 = 1
-TA_MAX_NODES = 1024
+TA_MAX_NODES = 4096
 
 _c_void_p = ctypes.c_void_p
 _i32 = ctypes.c_int32

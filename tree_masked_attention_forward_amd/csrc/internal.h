@@ -10,6 +10,12 @@
 
 namespace ta {
 
+// Trees of up to this many nodes per sequence have their mask rows built and
+// scanned in LDS (max_nodes * W * 8 bytes, 128 KiB here); larger ones, up to
+// TA_MAX_NODES, take kernels that keep only per-node scalars in LDS and read
+// the rows from global memory.
+constexpr int kLdsTreeMaxNodes = 1024;
+
 // Work decomposition of one tree_attn_forward call on the bf16 MFMA path.
 // Derived from host scalars only, so the workspace query and the call agree.
 struct FwdPlan {

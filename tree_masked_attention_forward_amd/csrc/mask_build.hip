@@ -17,13 +17,24 @@
 // its owner is extending it is still a subset of that node's ancestors, and
 // J is double buffered, so the covered distance never falls behind J.  The
 // depth of i is |R(i)| - 1.
+//
+// Trees above 1024 nodes (up to TA_MAX_NODES): the rows no longer fit in LDS.
+// build_mask_large_kernel spreads a sequence over several workgroups; each
+// keeps the whole parent array in LDS (4 bytes per node), validates it, and
+// writes the rows of its own block of nodes straight to global memory.  Lane
+// (row i, word w) follows the parent chain of i, whose indices fall strictly
+// (parents precede children), and sets the bits of the ancestors inside word
+// w, stopping as soon as the chain drops below the word.  A row's depth is
+// the popcount summed over its lanes, minus one.  The walk costs depth + 1
+// LDS steps for the lane of the root's word: fast for bushy trees, linear in
+// N for a long chain.
 #include "internal.h"
 
 namespace ta {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerThread = TA_MAX_NODES / kThreads;
+constexpr int kPerThread = kLdsTreeMaxNodes / kThreads;
 
 __device__ inline uint64_t lds_load(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -124,12 +135,82 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
   if (tid == 0 && status) status[b] = 0;
 }
 
+constexpr int kLargeThreads = 1024;
+constexpr int kLargeRows = 64;   // node rows per workgroup
+
+// Grid B x nblk workgroups, nblk row blocks per sequence.  Wp = W rounded up to a power of two (32 or 64 here):
+// Wp consecutive lanes hold one row, so a wave covers 64 / Wp rows per pass.
+__global__ __launch_bounds__(kLargeThreads) void build_mask_large_kernel(
+    const int32_t* __restrict__ parents, const int32_t* __restrict__ node_offsets,
+    int total_nodes, int max_nodes, int W, int Wp, int nblk, uint64_t* __restrict__ mask,
+    int32_t* __restrict__ depth, int32_t* __restrict__ status) {
+  __shared__ int32_t par[TA_MAX_NODES];
+  const int b = blockIdx.x / nblk;
+  const int blk = blockIdx.x % nblk;
+  const int r0 = blk * kLargeRows;
+  const int tid = threadIdx.x;
+  const int n0 = node_offsets[b];
+  const int n1 = node_offsets[b + 1];
+  const int n = n1 - n0;
+  if (n0 < 0 || n < 0 || n > max_nodes || n1 > total_nodes || max_nodes > TA_MAX_NODES) {
+    if (blk == 0 && tid == 0 && status) status[b] = 1;  // TA_ERR_INVALID_ARG
+    return;
+  }
+  // Every workgroup checks the whole parent array, so all of them agree on
+  // whether the tree is valid.
+  int bad = 0;
+  for (int i = tid; i < n; i += kLargeThreads) {
+    const int p = parents[n0 + i];
+    bad |= (p < -1 || p >= i);
+    par[i] = p;
+  }
+  bad = __syncthreads_or(bad);
+  const int r1 = min(n, r0 + kLargeRows);
+  if (bad) {
+    for (int idx = tid; idx < (r1 - r0) * W; idx += kLargeThreads)
+      mask[(size_t)(n0 + r0) * W + idx] = 0ull;
+    if (depth)
+      for (int i = r0 + tid; i < r1; i += kLargeThreads) depth[n0 + i] = -1;
+    if (blk == 0 && tid == 0 && status) status[b] = 2;  // TA_ERR_INVALID_TREE
+    return;
+  }
+  const int w = tid & (Wp - 1);
+  const int rows_per_pass = kLargeThreads / Wp;
+  // Uniform trip count: the row lanes of one wave reduce together below.
+  for (int base = r0; base < r1; base += rows_per_pass) {
+    const int i = base + tid / Wp;
+    uint64_t word = 0ull;
+    if (i < r1 && w < W) {
+      const int lo = 64 * w;
+      int x = i;
+      while (x >= lo) {   // ends: x falls strictly along the chain, down to -1
+        if (x < lo + 64) word |= 1ull << (x - lo);
+        x = par[x];
+      }
+      mask[(size_t)(n0 + i) * W + w] = word;
+    }
+    int c = __popcll(word);
+    for (int o = Wp >> 1; o > 0; o >>= 1) c += __shfl_xor(c, o);
+    if (depth && i < r1 && w == 0) depth[n0 + i] = c - 1;
+  }
+  if (blk == 0 && tid == 0 && status) status[b] = 0;
+}
+
 }  // namespace
 
 hipError_t launch_build_mask(const int32_t* parents, const int32_t* node_offsets, int B,
                              int total_nodes, int max_nodes, uint64_t* mask, int32_t* depth,
                              int32_t* status, hipStream_t stream) {
   const int W = (max_nodes + 63) / 64;
+  if (max_nodes > kLdsTreeMaxNodes) {
+    int Wp = 1;
+    while (Wp < W) Wp <<= 1;
+    const int nblk = (max_nodes + kLargeRows - 1) / kLargeRows;
+    hipLaunchKernelGGL(build_mask_large_kernel, dim3((unsigned)((long long)B * nblk)),
+                       dim3(kLargeThreads), 0, stream, parents, node_offsets, total_nodes,
+                       max_nodes, W, Wp, nblk, mask, depth, status);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)max_nodes * W * sizeof(uint64_t) + 2 * (size_t)max_nodes * sizeof(int32_t);
   if (lds > 64 * 1024) {
     hipError_t e = raise_dynamic_lds(reinterpret_cast<const void*>(&build_mask_kernel), (int)lds);

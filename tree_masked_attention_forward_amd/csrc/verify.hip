@@ -181,8 +181,8 @@ __global__ __launch_bounds__(kThreads) void path_select_kernel(
     int32_t* __restrict__ accept_tokens, const float2* __restrict__ ws_root,
     int32_t* __restrict__ bonus_token) {
   extern __shared__ uint64_t rows[];   // [nn][W] mask rows of the sequence
-  __shared__ int32_t tgt[TA_MAX_NODES];
-  __shared__ uint64_t match_w[(TA_MAX_NODES + 63) / 64];
+  __shared__ int32_t tgt[kLdsTreeMaxNodes];
+  __shared__ uint64_t match_w[(kLdsTreeMaxNodes + 63) / 64];
   __shared__ unsigned long long red[kThreads / 64];
   __shared__ int32_t root_pred;
   const int b = blockIdx.x;
@@ -351,6 +351,177 @@ __global__ __launch_bounds__(kThreads) void path_select_kernel(
   }
 }
 
+// Trees above 1024 nodes (up to TA_MAX_NODES): the mask rows (W <= 64 words
+// each) stay in global memory and are read a whole row per Wp lanes, Wp = W
+// rounded up to a power of two.  The steps and the tie rules are those of
+// path_select_kernel: per-node argmax from the chunk results; for next-token
+// rows each node's parent (the highest set bit of its row below itself) into
+// LDS; the match set by ballots; then one more pass over the rows for the
+// accepted test and the path length; the best row's bits, placed by a prefix
+// sum of word popcounts, give the path.
+constexpr int kBigThreads = 1024;
+
+template <bool NEXT>
+__global__ __launch_bounds__(kBigThreads) void path_select_large_kernel(
+    const float2* __restrict__ ws, int cpr, const int32_t* __restrict__ draft,
+    const uint64_t* __restrict__ mask, const int32_t* __restrict__ node_offsets,
+    int total_nodes, int max_nodes, int W, int Wp, int32_t* __restrict__ target_argmax,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
+    int32_t* __restrict__ accept_tokens, const float2* __restrict__ ws_root,
+    int32_t* __restrict__ bonus_token) {
+  __shared__ int32_t tgt[TA_MAX_NODES];
+  __shared__ int32_t par[NEXT ? TA_MAX_NODES : 1];
+  __shared__ uint64_t match_w[TA_MAX_NODES / 64];
+  __shared__ unsigned long long red[kBigThreads / 64];
+  __shared__ int32_t root_pred;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n0 = node_offsets[b];
+  const int n1 = node_offsets[b + 1];
+  int nn = n1 - n0;
+  if (n0 < 0 || nn < 0 || nn > max_nodes || n1 > total_nodes || max_nodes > TA_MAX_NODES)
+    nn = 0;   // nothing accepted
+
+  // Target argmax per node: a node's cpr chunk results sit in cpr
+  // consecutive lanes (cpr a power of two <= 64); ties -> lowest index.
+  const int pairs = nn * cpr;
+  for (int p0 = 0; p0 < pairs; p0 += kBigThreads) {
+    const int pidx = p0 + tid;
+    float bv = kNegInf;
+    int bi = 0x7fffffff;
+    if (pidx < pairs) {
+      const float2 x = ws[(size_t)n0 * cpr + pidx];
+      bv = x.x;
+      bi = __float_as_int(x.y);
+    }
+    for (int o = cpr >> 1; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (pidx < pairs && (pidx & (cpr - 1)) == 0) {
+      tgt[pidx / cpr] = bi;
+      if (target_argmax) target_argmax[n0 + pidx / cpr] = bi;
+    }
+  }
+  if (NEXT && wave == 0) {
+    float bv = kNegInf;
+    int bi = 0x7fffffff;
+    if (lane < cpr) {
+      const float2 x = ws_root[(size_t)b * cpr + lane];
+      bv = x.x;
+      bi = __float_as_int(x.y);
+    }
+    wave_best(bv, bi);
+    if (lane == 0) root_pred = bi;
+  }
+
+  const int w = tid & (Wp - 1);
+  const int rows_per_pass = kBigThreads / Wp;
+  // Word w of row i, with the bits at or above `lim` cleared.
+  auto row_word = [&](int i, int lim) -> uint64_t {
+    if (i >= nn || w >= W || 64 * w >= lim) return 0ull;
+    uint64_t mw = mask[(size_t)(n0 + i) * W + w];
+    if (lim - 64 * w < 64) mw &= (1ull << (lim - 64 * w)) - 1ull;
+    return mw;
+  };
+  if constexpr (NEXT) {
+    // Parent of i: the highest ancestor below i.
+    for (int base = 0; base < nn; base += rows_per_pass) {
+      const int i = base + tid / Wp;
+      const uint64_t mw = row_word(i, i);
+      int hi = mw ? 64 * w + 63 - __builtin_clzll(mw) : -1;
+      for (int o = Wp >> 1; o > 0; o >>= 1) hi = max(hi, __shfl_xor(hi, o));
+      if (i < nn && w == 0) par[i] = hi;
+    }
+  }
+  __syncthreads();
+
+  // Match set: node i matches iff its draft token is the prediction it is
+  // checked against; wave w's ballot over nodes base + 64w .. is one word.
+  for (int base = 0; base < nn; base += kBigThreads) {
+    const int i = base + tid;
+    bool m = false;
+    if (i < nn) {
+      int e;
+      if constexpr (NEXT) e = par[i] >= 0 ? tgt[par[i]] : root_pred;
+      else e = tgt[i];
+      m = draft[n0 + i] == e;
+    }
+    const uint64_t bits = __ballot(m);
+    if (lane == 0 && base + 64 * wave < nn) match_w[(base >> 6) + wave] = bits;
+  }
+  __syncthreads();
+
+  // Accepted iff the row (cut at nn) lies inside the match set; the longest
+  // accepted path wins, lowest index on ties.
+  unsigned long long key = 0ull;
+  for (int base = 0; base < nn; base += rows_per_pass) {
+    const int i = base + tid / Wp;
+    const uint64_t mw = row_word(i, nn);
+    int badw = (mw & ~(mw ? match_w[w] : 0ull)) != 0ull;
+    int len = __popcll(mw);
+    for (int o = Wp >> 1; o > 0; o >>= 1) {
+      badw |= __shfl_xor(badw, o);
+      len += __shfl_xor(len, o);
+    }
+    if (i < nn && w == 0 && !badw && len > 0) {
+      const unsigned long long k = ((unsigned long long)len << 32) | (0xffffffffu - (uint32_t)i);
+      key = k > key ? k : key;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long ok2 = __shfl_xor(key, o);
+    key = ok2 > key ? ok2 : key;
+  }
+  if (lane == 0) red[wave] = key;
+  __syncthreads();
+  key = red[0];
+  for (int k = 1; k < kBigThreads / 64; ++k) key = red[k] > key ? red[k] : key;
+  const int len = (int)(key >> 32);
+  const int best = (int)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+
+  int32_t* an = accept_nodes + (size_t)b * max_nodes;
+  int32_t* at = accept_tokens + (size_t)b * max_nodes;
+  for (int pos = len + tid; pos < max_nodes; pos += kBigThreads) {
+    an[pos] = -1;
+    at[pos] = -1;
+  }
+  if (len > 0 && wave == 0) {
+    // Lane k holds word k of the best row (W <= 64); its bits go after the
+    // popcounts of the lower words.
+    uint64_t mw = 0ull;
+    if (lane < W && 64 * lane < nn) {
+      mw = mask[(size_t)(n0 + best) * W + lane];
+      if (nn - 64 * lane < 64) mw &= (1ull << (nn - 64 * lane)) - 1ull;
+    }
+    const int c = __popcll(mw);
+    int incl = c;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    int pos = incl - c;
+    while (mw) {
+      const int j = 64 * lane + __builtin_ctzll(mw);
+      an[pos] = j;
+      at[pos] = draft[n0 + j];
+      ++pos;
+      mw &= mw - 1ull;
+    }
+  }
+  if (tid == 0) {
+    accept_len[b] = len;
+    if (NEXT) bonus_token[b] = len > 0 ? tgt[best] : root_pred;
+  }
+}
+
 }  // namespace
 
 VerifyPlan plan_verify(int total_nodes, int V) {
@@ -413,6 +584,21 @@ hipError_t launch_verify(bool bf16, const void* logits, const int32_t* draft,
   hipError_t e = launch_argmax(bf16, logits, total_nodes, root_logits, root_logits ? B : 0, V, p,
                                ws, stream);
   if (e != hipSuccess) return e;
+  if (max_nodes > kLdsTreeMaxNodes) {
+    int Wp = 1;
+    while (Wp < W) Wp <<= 1;
+    if (root_logits)
+      hipLaunchKernelGGL(path_select_large_kernel<true>, dim3(B), dim3(kBigThreads), 0, stream,
+                         ws, p.cpr, draft, mask, node_offsets, total_nodes, max_nodes, W, Wp,
+                         target_argmax, accept_len, accept_nodes, accept_tokens, ws_root,
+                         bonus_token);
+    else
+      hipLaunchKernelGGL(path_select_large_kernel<false>, dim3(B), dim3(kBigThreads), 0, stream,
+                         ws, p.cpr, draft, mask, node_offsets, total_nodes, max_nodes, W, Wp,
+                         target_argmax, accept_len, accept_nodes, accept_tokens, nullptr,
+                         nullptr);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)max_nodes * W * sizeof(uint64_t);
   const void* kern = root_logits ? reinterpret_cast<const void*>(&path_select_kernel<true>)
                                  : reinterpret_cast<const void*>(&path_select_kernel<false>);
