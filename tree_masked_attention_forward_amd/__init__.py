@@ -3,7 +3,7 @@
 The computation lives in ``libtreeattn.so`` (hand-written HIP kernels behind
 the C ABI of ``include/tree_attn.h``); this package is its Python binding.
 Importing the package loads the library and raises ImportError when it has not
-been built (``python -m tree_masked_attention_forward_amd.build``).
+been built (``python tree_masked_attention_forward_amd/build.py``).
 """
 from ._binding import (  # noqa: F401
     LIBRARY_PATH,

@@ -48,7 +48,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     p = path or LIBRARY_PATH
     if not os.path.exists(p):
         raise ImportError(f"{p} is missing: build it with "
-                          "`python -m tree_masked_attention_forward_amd.build`")
+                          "`python tree_masked_attention_forward_amd/build.py`")
     lib = ctypes.CDLL(p)
     lib.tree_attn_status_string.restype = ctypes.c_char_p
     lib.tree_attn_status_string.argtypes = [ctypes.c_int]

@@ -1,6 +1,6 @@
 """Build libtreeattn.so in-tree with hipcc for gfx950.
 
-    python -m tree_masked_attention_forward_amd.build
+    python tree_masked_attention_forward_amd/build.py
 
 Each source is compiled to an object file in parallel, then linked into
 ``tree_masked_attention_forward_amd/libtreeattn.so``.  Packed-fp32 VALU
