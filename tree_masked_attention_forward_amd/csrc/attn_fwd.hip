@@ -634,22 +634,25 @@ void fwd_bf16_kernel(KParams P) {
   // Masking of one tile's scores: an idle tile (beyond the split, or an idle
   // row group) is all -inf; a tree tile keeps the row node's ancestors; the
   // prefix's partial last tile drops the keys past the prefix.
+  // One uniform branch that edits the scores in place: full prefix tiles (all
+  // but a few) skip it, and no per-case copies of the scores are made.
   auto mask_tile = [&](f32x16_t& sacc, int tile, uint32_t mbits, bool active) {
-    if (!active) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[v] = kNegInf;
-    } else if (tile >= Lt) {
-      const uint32_t bits = row_ok ? mbits : 0u;
+    const bool tree = tile >= Lt;
+    const bool tail = !tree && (tile + 1) * kKT > L;
+    if (!active || tree || tail) {
+      // Bit k of keep: key k of the tile stays visible.
+      uint32_t keep;
+      if (!active)
+        keep = 0u;
+      else if (tree)
+        keep = row_ok ? mbits : 0u;
+      else
+        keep = (1u << (L - tile * kKT)) - 1u;   // 1 <= L - 32*tile <= 31 keys left
+      const uint32_t kh = keep >> (4 * hh);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int key = 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (!((bits >> key) & 1u)) sacc[v] = kNegInf;
-      }
-    } else if ((tile + 1) * kKT > L) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (tile * kKT + key >= L) sacc[v] = kNegInf;
+        const int key = 8 * (v >> 2) + (v & 3);
+        sacc[v] = (kh & (1u << key)) ? sacc[v] : kNegInf;
       }
     }
   };
