@@ -137,6 +137,29 @@ def test_forward_many_sequences_full_check(ta):
     check_attention(out, lse, *_oracle_attn(c), fp32=False, what="16 ragged sequences")
 
 
+def test_forward_ragged_pieces_longest_first_full_check(ta):
+    """Strongly ragged prefixes (17 to 2100 keys) over 16 sequences x 8 KV heads:
+    long sequences are cut into several equal pieces that workgroups take
+    longest first, short ones stay whole.  Every node, both forward entry
+    points (mask given, mask built in the kernel), against the oracle.
+    (Prefixes of only a few keys give outputs near 4 in size, whose bf16
+    rounding alone takes 0.008 of the 0.01 max-abs bar; the L = 0 shapes
+    above cover them.)"""
+    rng = np.random.default_rng(33)
+    lens = [2100, 40, 1500, 90, 900, 33, 1200, 64, 2000, 130, 700, 300, 1800, 17, 1100, 400]
+    trees = [synthetic.random_tree(rng, 64, 1, 6, 4).tolist() for _ in range(16)]
+    c = synthetic.make_case("pieces", prefix_lens=lens, trees=trees, Hq=32, Hkv=8, D=128, seed=33)
+    dc, mask = _check_mask(ta, c)
+    out, lse = gpu_forward(ta, dc, mask)
+    check_attention(out, lse, *_oracle_attn(c), fp32=False, what="ragged pieces")
+    fo, fl, fm, fd, fs = ta.mask_and_forward(dc.parents, dc.q, dc.k_tree, dc.v_tree, dc.k_prefix,
+                                             dc.v_prefix, dc.prefix_offsets, dc.node_offsets,
+                                             dc.max_nodes, dc.max_prefix, c.scale,
+                                             return_lse=True)
+    assert torch.equal(fo, out) and torch.equal(fl, lse)
+    assert torch.equal(fm, mask) and int(fs.abs().sum()) == 0
+
+
 def test_forward_llama3_8b_full_check(ta):
     """The benchmarked workload (one 8B-shaped layer, N=64, L=4096), every
     node and head, in the same launch configuration the benchmark times."""

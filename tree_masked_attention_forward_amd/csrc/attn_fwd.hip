@@ -113,8 +113,10 @@ struct KParams {
   int merge_wpg;              // merge workgroups per group (in-kernel merge)
   long long groups;           // B * Hkv * R (sequence, KV head, row tile) groups
   int head_major;             // item order: (b, g, s, r) if set, else (b, s, g, r)
+  int piece;                  // > 0: a sequence takes ceil(T / piece) splits (ragged batches)
+  int lpt;                    // workgroups take the pieces longest first (see lpt_piece)
   int total_nodes, max_nodes;
-  int Hq, Hkv, G, W;
+  int B, Hq, Hkv, G, W;
   int rows_wg, R, S, tmax;
   float scale, scale_log2;
 };
@@ -156,7 +158,8 @@ __device__ inline bool row_tile_range(const KParams& P, const Seq& sq, int r, Ra
   g.n_hi = (row0 + g.rows_here - 1) / P.G;
   g.Lt = (sq.L + kKT - 1) / kKT;
   g.T = g.Lt + (g.n_hi + kKT) / kKT;
-  int sb = (int)(((long long)P.S * g.T + P.tmax - 1) / P.tmax);
+  const int sb = P.piece > 0 ? (g.T + P.piece - 1) / P.piece
+                             : (int)(((long long)P.S * g.T + P.tmax - 1) / P.tmax);
   g.Sb = max(1, min(sb, min(P.S, g.T)));
   return true;
 }
@@ -170,6 +173,45 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline long long item_index(const KParams& P, int b, int g, int s, int r) {
   return P.head_major ? (((long long)b * P.Hkv + g) * P.S + s) * P.R + r
                       : (((long long)b * P.S + s) * P.Hkv + g) * P.R + r;
+}
+
+// Longest-piece-first order for ragged batches (one row tile, B <= 64).
+// Sequences are cut into pieces of about `piece` tiles; the pieces of all
+// (sequence, split, KV head) units are ordered by length, longest first (ties:
+// lower sequence, then split, then head), and workgroup k takes piece k.
+// Workgroup ids are dealt round-robin over the XCDs and each XCD starts its
+// workgroups in id order, so every XCD gets an equal share of the work and
+// starts its longest pieces first.  Every wave computes the same answer from
+// the offsets (lane b holds sequence b).  A sequence whose offsets do not
+// decode keeps one piece per KV head, ordered last, so its workgroups still
+// report it.  Returns false when k is past the last piece.
+__device__ inline bool lpt_piece(const KParams& P, long long k, int& b, int& g, int& s) {
+  const int lane = threadIdx.x & 63;
+  int key = 0, cnt = 0;   // piece length (tiles) and pieces of sequence `lane`
+  if (lane < P.B) {
+    Seq sq;
+    Range rg;
+    if (decode_seq(P, lane, sq) && row_tile_range(P, sq, 0, rg)) {
+      key = (rg.T + rg.Sb - 1) / rg.Sb;
+      cnt = rg.Sb * P.Hkv;
+    } else {
+      cnt = P.Hkv;
+    }
+  }
+  // Pieces of the sequences ahead of this one in the order.
+  long long off = 0;
+  for (int j = 0; j < P.B; ++j) {
+    const int kj = __builtin_amdgcn_readlane(key, j);
+    const int cj = __builtin_amdgcn_readlane(cnt, j);
+    if (kj > key || (kj == key && j < lane)) off += cj;
+  }
+  const unsigned long long hit = __ballot(lane < P.B && k >= off && k < off + cnt);
+  if (!hit) return false;
+  b = __builtin_ctzll(hit);
+  const long long idx = k - __shfl(off, b);
+  s = (int)(idx / P.Hkv);
+  g = (int)(idx % P.Hkv);
+  return true;
 }
 
 // Hardware id of the XCD this wave runs on (HW_REG_XCC_ID, bits 3:0).
@@ -410,12 +452,18 @@ void fwd_bf16_kernel(KParams P) {
   // Workgroup ids are dealt round-robin over the 8 XCDs; remap so that
   // consecutive items (same sequence and KV head, same key split, different
   // row tiles) run on one XCD.
+  int g, s, b, r;
+  long long item;
+  if (P.lpt) {
+    if (!lpt_piece(P, blockIdx.x, b, g, s)) return;
+    r = 0;
+    item = item_index(P, b, g, s, 0);
+  } else {
   const long long nb = P.n_split_blocks;
-  const long long item = (long long)(blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
+  item = (long long)(blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
   if (item >= P.n_items) return;
-  const int r = (int)(item % P.R);
+  r = (int)(item % P.R);
   long long t = item / P.R;
-  int g, s, b;
   if (P.head_major) {
     s = (int)(t % P.S);
     t /= P.S;
@@ -426,6 +474,7 @@ void fwd_bf16_kernel(KParams P) {
     t /= P.Hkv;
     s = (int)(t % P.S);
     b = (int)(t / P.S);
+  }
   }
 
   Seq sq;
@@ -1045,6 +1094,12 @@ constexpr long long kMaxMergeBlocks = 128;
 // Bytes of group counters at the start of a workspace that holds partials.
 constexpr size_t kCounterBytes = 2048;
 
+// Pieces per CU for ragged batches (see plan_forward_bf16).
+#ifndef TA_ITEMS_PER_CU
+#define TA_ITEMS_PER_CU 1
+#endif
+constexpr long long kItemsPerCU = TA_ITEMS_PER_CU;
+
 int pow2_ceil(int x) {
   int p = 1;
   while (p < x) p <<= 1;
@@ -1073,13 +1128,28 @@ FwdPlan plan_forward_bf16(int B, int total_nodes, int max_nodes, int Hq, int Hkv
   p.rows_wg = 32 * p.rg;
   p.R = (int)((rows_max + p.rows_wg - 1) / p.rows_wg);
   p.tmax = (int)((max_prefix + kKT - 1) / kKT + (max_nodes + kKT - 1) / kKT);
-  // Splits: aim for one full round of workgroups (256 CUs); twice that when
-  // prefix lengths are ragged so short and long sequences balance out.  Keep
-  // at least two iterations per split.
+  // Splits.  Equal prefix lengths: aim for one full round of workgroups
+  // (MI355X's 256 CUs), every sequence split alike.  Ragged prefix lengths:
+  // cut every sequence into pieces of about the same number of tiles, sized
+  // so the whole workload makes about kItemsPerCU pieces per CU; with one row
+  // tile and at most 64 sequences the workgroups then take the pieces
+  // longest first (lpt_piece), which balances the XCDs and keeps the long
+  // pieces from starting last.  Keep at least two iterations per split.
   const long long units = (long long)B * Hkv * p.R;
   const bool ragged = max_prefix * B > total_prefix + total_prefix / 4;
-  const long long target = ragged ? 512 : 256;
-  long long S = (target + units - 1) / units;
+  long long S;
+  p.piece = 0;
+  if (ragged) {
+    const long long tiles = (total_prefix + (long long)B * (kKT - 1)) / kKT +
+                            (long long)B * ((max_nodes + kKT - 1) / kKT);   // all sequences
+    const long long pieces = 256LL * kItemsPerCU;
+    const long long piece = std::max<long long>(
+        2 * p.kg, (tiles * Hkv * p.R + pieces - 1) / pieces);
+    p.piece = (int)std::min<long long>(piece, p.tmax);
+    S = (p.tmax + p.piece - 1) / p.piece;
+  } else {
+    S = (256 + units - 1) / units;
+  }
   S = std::min<long long>(S, std::max(1, p.tmax / (2 * p.kg)));
   p.S = (int)std::max<long long>(1, S);
   p.n_items = units * p.S;
@@ -1093,6 +1163,7 @@ FwdPlan plan_forward_bf16(int B, int total_nodes, int max_nodes, int Hq, int Hkv
   p.merge_in_kernel = p.S > 1 && p.S < 128 && p.groups * p.merge_wpg <= kMaxMergeBlocks &&
                       ((long long)B * Hkv) % 8 == 0 &&
                       p.groups * 2 * sizeof(unsigned long long) <= kCounterBytes;
+  p.lpt = p.piece > 0 && p.R == 1 && B <= 64 && !p.merge_in_kernel;
   p.ws_bytes = 0;
   if (p.S > 1) {
     // [group counters | O partials | max and sum partials].  The counter
@@ -1143,6 +1214,10 @@ hipError_t launch_forward_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t s
     }
   }
   kp.merge_wpg = p.merge_wpg;
+  kp.piece = p.piece;
+  // The in-kernel merge needs its own item placement; lpt never comes with it.
+  kp.lpt = p.lpt && !kp.head_major ? 1 : 0;
+  kp.B = a.B;
   kp.groups = p.groups;
   kp.total_prefix = a.total_prefix;
   kp.max_prefix = a.max_prefix;

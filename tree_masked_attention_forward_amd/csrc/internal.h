@@ -30,6 +30,8 @@ struct FwdPlan {
   long long groups;    // B * Hkv * R (sequence, KV head, row tile) groups
   int merge_wpg;       // merge workgroups per group when the merge runs in-kernel
   bool merge_in_kernel;  // splits merged by trailing workgroups of the same grid
+  int piece;           // > 0: ragged batch, a sequence takes ceil(tiles / piece) splits
+  bool lpt;            // split workgroups take the pieces longest first
   size_t ws_bytes;     // partial (O, m, l) storage [+ counters]; 0 when S == 1
 };
 
