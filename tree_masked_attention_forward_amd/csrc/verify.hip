@@ -86,20 +86,23 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const void* __
     const int first = lo + threadIdx.x * VEC;
     if (first < hi) bi = first;
     for (int base = lo; base < hi; base += kThreads * VEC * kUnroll) {
+      // Every load is issued (no branch around it), so they retire in order
+      // and each compare waits only for its own load.  Past the chunk's end a
+      // lane reads the chunk's last full vector again instead: those values
+      // are copies of elements of this chunk under higher indices, so they
+      // never change the maximum nor become the lowest index holding it.
+      // (Vector rows hold a multiple of VEC elements, so hi - VEC >= lo.)
       u32x4_t u[kUnroll];
 #pragma unroll
       for (int k = 0; k < kUnroll; ++k) {
         const int e = base + (k * kThreads + threadIdx.x) * VEC;
-        if (e < hi) {
-          if (BF16)
-            u[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
-                static_cast<const uint16_t*>(logits) + row * V + e));
-          else
-            u[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
-                static_cast<const float*>(logits) + row * V + e));
-        } else {
-          u[k] = u32x4_t{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};   // -inf, never taken
-        }
+        const int ec = e < hi ? e : hi - VEC;
+        if (BF16)
+          u[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+              static_cast<const uint16_t*>(logits) + row * V + ec));
+        else
+          u[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+              static_cast<const float*>(logits) + row * V + ec));
       }
 #pragma unroll
       for (int k = 0; k < kUnroll; ++k) {
