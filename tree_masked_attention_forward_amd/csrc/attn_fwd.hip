@@ -1017,12 +1017,11 @@ void fwd_bf16_kernel(KParams P) {
 }
 
 // Separate merge kernel: one workgroup per (sequence, KV head, row tile, row
-// group, 32-dim block), wave j = 8-dim slice.
+// group); wave j takes the 8-dim slice j of each of the four 32-dim blocks, so
+// every thread has four partial loads per split in flight.
 template <int RG>
 __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
   long long t = blockIdx.x;
-  const int e = (int)(t % 4);
-  t /= 4;
   const int rg = (int)(t % RG);
   t /= RG;
   const int r = (int)(t % P.R);
@@ -1037,18 +1036,19 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
   const long long split_stride = item_index(P, b, g, 1, r) - item0;
 
   // The partial slots do not depend on the offsets: issue the loads of the
-  // first kMaxS splits before decoding the sequence, so both round trips
+  // first kPre splits before decoding the sequence, so both round trips
   // overlap.  Slots past this row tile's split count are never written by
   // this call and are ignored below.
-  constexpr int kMaxS = 16;
-  float2 ml[kMaxS];
-  u32x2_t h[kMaxS];
+  constexpr int kPre = 8;
+  float2 ml[kPre];
+  u32x2_t h[kPre][4];
 #pragma unroll
-  for (int k = 0; k < kMaxS; ++k) {
+  for (int k = 0; k < kPre; ++k) {
     if (k < P.S) {
       const long long it = item0 + k * split_stride;
       ml[k] = P.ws_ml[(size_t)it * P.rows_wg + rl];
-      h[k] = P.ws_o[(((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[k][e] = P.ws_o[(((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane];
     }
   }
 
@@ -1060,16 +1060,21 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
   const float c2 = P.scale_log2;
   const int Sb = rgn.Sb;
 
-  MergeAcc ma;
+  MergeAcc ma[4];
 #pragma unroll
-  for (int k = 0; k < kMaxS; ++k)
-    if (k < Sb) ma.add(ml[k], h[k], c2);
-  for (int s = kMaxS; s < Sb; ++s) {
+  for (int k = 0; k < kPre; ++k)
+    if (k < Sb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ma[e].add(ml[k], h[k][e], c2);
+  for (int s = kPre; s < Sb; ++s) {
     const long long it = item0 + s * split_stride;
-    ma.add(P.ws_ml[(size_t)it * P.rows_wg + rl],
-           P.ws_o[(((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane], c2);
+    const float2 m_l = P.ws_ml[(size_t)it * P.rows_wg + rl];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      ma[e].add(m_l, P.ws_o[(((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane], c2);
   }
-  store_merged(P, sq, g, r, rl, e, j, hh, ma);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) store_merged(P, sq, g, r, rl, e, j, hh, ma[e]);
 }
 
 template <int RG, int KG, int TPW, int NS, bool MR>
@@ -1237,7 +1242,7 @@ hipError_t launch_forward_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t s
   kp.n_split_blocks = (p.n_items + 7) / 8 * 8;
   const long long grid = kp.n_split_blocks + merge_blocks;
   const long long merge_grid =
-      (p.S > 1 && merge_blocks == 0) ? (long long)a.B * a.Hkv * p.R * p.rg * 4 : 0;
+      (p.S > 1 && merge_blocks == 0) ? (long long)a.B * a.Hkv * p.R * p.rg : 0;
   switch (p.rg * 16 + p.kg) {
     // A three-stage ring measured as fast as four on every shape here.  With
     // MR the mask rows (at most 128 nodes) sit in registers.
