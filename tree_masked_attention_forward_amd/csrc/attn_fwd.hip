@@ -310,8 +310,9 @@ __device__ inline void store_merged(const KParams& P, const Seq& sq, int g, int 
 // split count, checks that every split ran on its own XCD, and merges
 // RG*16/NW (row group, 32-dim block, 8-dim slice) units, one per wave.  If
 // the XCD check fails (workgroups not dealt as assumed) it writes NaN instead
-// of a possibly stale result.  The last merge workgroup of a group returns
-// the group's counters to zero for the next call.  The wait is bounded
+// of a possibly stale result.  Each merge workgroup counts itself done right
+// after its poll succeeds, and the last one of a group returns the group's
+// counters to zero for the next call.  The wait is bounded
 // (about 0.3 s), so counters that were not zero at entry cannot hang a call:
 // a merge workgroup that times out writes NaN and zeroes the counters, so
 // the next call starts clean.
@@ -355,6 +356,13 @@ __device__ void merge_in_kernel(const KParams& P, long long m) {
   __syncthreads();
   const bool coherent =
       !timed_out && seen_word == (unsigned long long)rgn.Sb * arrival_word(xcc_id());
+  // Every merge workgroup counts itself done as soon as it has seen its group
+  // complete (its round trip then overlaps the partial loads below); once all
+  // of a group's merge workgroups have, nothing reads the group's counters in
+  // this call, so the last of them returns them to zero.
+  unsigned long long done = 0ull;
+  if (tid == 0 && !timed_out)
+    done = __hip_atomic_fetch_add(word + 1, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   const int rg = unit >> 4;
   const int e = (unit >> 2) & 3;
@@ -366,17 +374,38 @@ __device__ void merge_in_kernel(const KParams& P, long long m) {
   if (rl < rgn.rows_here) {
     MergeAcc ma;
     if (coherent) {
-      for (int s = 0; s < rgn.Sb; ++s) {
-        const long long it = item0 + s * split_stride;
-        // agent-scope loads skip the CU's L1 and read this XCD's L2
-        const unsigned long long ml = __hip_atomic_load(
+      // Agent-scope loads skip the CU's L1 and read this XCD's L2.  The first
+      // kBatch splits are all requested before any is used (slots past the
+      // split count re-read split 0 and are ignored), so the merge waits on
+      // one L2 round trip instead of one per split.
+      auto load_ml = [&](long long it) {
+        return __hip_atomic_load(
             reinterpret_cast<const unsigned long long*>(P.ws_ml + (size_t)it * P.rows_wg + rl),
             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned long long o = __hip_atomic_load(
+      };
+      auto load_o = [&](long long it) {
+        return __hip_atomic_load(
             reinterpret_cast<const unsigned long long*>(
                 P.ws_o + (((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane),
             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ma.add(__builtin_bit_cast(float2, ml), __builtin_bit_cast(u32x2_t, o), P.scale_log2);
+      };
+      constexpr int kBatch = 16;
+      unsigned long long mlv[kBatch], ov[kBatch];
+#pragma unroll
+      for (int s = 0; s < kBatch; ++s) {
+        const long long it = item0 + (s < rgn.Sb ? s : 0) * split_stride;
+        mlv[s] = load_ml(it);
+        ov[s] = load_o(it);
+      }
+#pragma unroll
+      for (int s = 0; s < kBatch; ++s)
+        if (s < rgn.Sb)
+          ma.add(__builtin_bit_cast(float2, mlv[s]), __builtin_bit_cast(u32x2_t, ov[s]),
+                 P.scale_log2);
+      for (int s = kBatch; s < rgn.Sb; ++s) {
+        const long long it = item0 + s * split_stride;
+        ma.add(__builtin_bit_cast(float2, load_ml(it)), __builtin_bit_cast(u32x2_t, load_o(it)),
+               P.scale_log2);
       }
     } else {
       ma.M = __builtin_nanf("");
@@ -385,11 +414,7 @@ __device__ void merge_in_kernel(const KParams& P, long long m) {
     }
     store_merged(P, sq, g, r, rl, e, j, hh, ma);
   }
-  __syncthreads();
   if (tid == 0) {
-    const unsigned long long done =
-        timed_out ? 0ull
-                  : __hip_atomic_fetch_add(word + 1, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (timed_out || done + 1 == (unsigned long long)P.merge_wpg) {
       __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(word + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
