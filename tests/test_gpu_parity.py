@@ -160,6 +160,31 @@ def test_forward_ragged_pieces_longest_first_full_check(ta):
     assert torch.equal(fm, mask) and int(fs.abs().sum()) == 0
 
 
+def test_forward_ragged_pieces_bad_offsets_reported(ta):
+    """Longest-first pieces with one sequence whose node count exceeds
+    max_nodes: that sequence reports TA_ERR_INVALID_ARG from the kernel and
+    every other sequence still meets the oracle."""
+    rng = np.random.default_rng(41)
+    lens = [1900, 60, 1300, 250, 700, 1600, 90, 1100, 40, 2000, 500, 150, 1200, 75, 800, 330]
+    ns = [40] * 16
+    ns[5] = 64                                   # over max_nodes below
+    trees = [synthetic.random_tree(rng, n, 1, 6, 4).tolist() for n in ns]
+    c = synthetic.make_case("badpieces", prefix_lens=lens, trees=trees, Hq=32, Hkv=8, D=128,
+                            seed=41)
+    dc = DevCase(c)
+    max_nodes = 48
+    out, lse, _, _, status = ta.mask_and_forward(
+        dc.parents, dc.q, dc.k_tree, dc.v_tree, dc.k_prefix, dc.v_prefix, dc.prefix_offsets,
+        dc.node_offsets, max_nodes, dc.max_prefix, c.scale, return_lse=True)
+    st = status.cpu().numpy()
+    assert st[5] == ta.TA_ERR_INVALID_ARG and (np.delete(st, 5) == 0).all(), st
+    no = c.node_offsets
+    rows = np.r_[np.arange(no[0], no[5]), np.arange(no[6], no[16])]
+    ro, rl = _oracle_attn(c, nodes=rows)
+    check_attention(out[torch.from_numpy(rows).cuda()], lse[torch.from_numpy(rows).cuda()],
+                    ro, rl, fp32=False, what="pieces with a bad sequence")
+
+
 def test_forward_llama3_8b_full_check(ta):
     """The benchmarked workload (one 8B-shaped layer, N=64, L=4096), every
     node and head, in the same launch configuration the benchmark times."""
