@@ -22,7 +22,10 @@
 // the tile range in balanced pieces (the tree tiles ride with the last prefix
 // tiles).  Each XCD runs a contiguous run of item ids: the row tiles that
 // share a KV chunk read it once from HBM and once from that XCD's L2, and the
-// XCD streams whole key rows (all KV heads) of one key range.
+// XCD streams whole key rows (all KV heads) of one key range.  Ragged batches
+// (one row tile, at most 64 sequences) instead cut every sequence into pieces
+// of about equal length that workgroups take longest first, so the XCDs get
+// equal shares (lpt_piece).
 //
 // Per 32-key tile and wave:
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T
