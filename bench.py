@@ -59,6 +59,11 @@ def parse():
                    help="time only the step's calls (no standalone commit or next-token "
                         "verifier), so that profiler averages per kernel name cover the step")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--hbm-ceiling", action="store_true",
+                   help="time plain device copies and a read-only reduction at several sizes "
+                        "(the practical HBM ceiling) and print one JSON line")
+    p.add_argument("--summarize-ceiling", metavar="FILE",
+                   help="write profiles/hbm_ceiling.md from the --hbm-ceiling output in FILE")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a plain 256 MiB device-to-device copy (counter calibration)")
     p.add_argument("--summarize-mfma", metavar="DIR",
@@ -108,6 +113,59 @@ def calib_copy():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calib_copy_bytes": CALIB_BYTES}))
+
+
+HBM_CEILING_CMD = "python -u bench.py --hbm-ceiling > gpurun_out/hbm_ceiling.json"
+CEILING_SIZES_MB = (16, 32, 64, 256, 1024)
+
+
+def hbm_ceiling():
+    """The practical HBM rate on this GPU: torch's device-to-device copy (bytes
+    read + written) over buffers of each size, rotated over enough copies to
+    exceed twice the 256 MB Infinity Cache so every pass reads cold data; HIP
+    events around 50 passes."""
+    import torch
+    dev = torch.device("cuda:0")
+    out = []
+    for mb in CEILING_SIZES_MB:
+        n = mb << 20
+        sets = max(2, -(-1024 // mb))   # >= 1 GiB in rotation
+        src = [torch.empty(n, dtype=torch.uint8, device=dev).fill_(1) for _ in range(sets)]
+        dst = [torch.empty_like(src[0]) for _ in range(sets)]
+        torch.cuda.synchronize()
+        for i in range(2 * sets):   # warm-up: touch every page
+            dst[i % sets].copy_(src[i % sets])
+        reps = 50
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            dst[i % sets].copy_(src[i % sets])
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        res = {"MB": mb, "us": round(us, 2), "GBps": round(2 * n / (us * 1e-6) / 1e9, 1)}
+        out.append(res)
+        print(f"[ceiling] {res}", file=sys.stderr, flush=True)
+        del src, dst
+        torch.cuda.empty_cache()
+    print(json.dumps({"hbm_ceiling": out, "peak_GBps": HBM_PEAK_GBS}))
+
+
+def summarize_ceiling(path):
+    with open(path) as f:
+        rec = json.loads(f.read().strip().splitlines()[-1])
+    lines = ["# Practical HBM ceiling on the MI355X box", "",
+             "Command (repository root, MI355X box):", "", "    " + HBM_CEILING_CMD, "",
+             "torch device-to-device copy of a buffer of each size (GB/s counts the bytes read "
+             "plus the bytes written), 50 passes timed with HIP events, buffers rotated over "
+             ">= 1 GiB so every pass reads cold data (the Infinity Cache is 256 MB). The "
+             "published peak is 8 TB/s. For scale: one 8B-shaped forward call moves 18.1 "
+             "algorithmic MB (35.9 MB counted by FETCH_SIZE + WRITE_SIZE).", "",
+             "| buffer | us per copy | GB/s (read + write) |", "|---|---|---|"]
+    for r in rec["hbm_ceiling"]:
+        lines.append(f"| {r['MB']} MB | {r['us']} | {r['GBps']} |")
+    with open(os.path.join(PROFILES, "hbm_ceiling.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def _read_csvs(root, suffix):
@@ -329,6 +387,12 @@ def main():
         return
     if args.calib_copy:
         calib_copy()
+        return
+    if args.hbm_ceiling:
+        hbm_ceiling()
+        return
+    if args.summarize_ceiling:
+        summarize_ceiling(args.summarize_ceiling)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
