@@ -179,8 +179,9 @@ TA_API int tree_attn_forward(int dtype, const void* q, const void* k_tree, const
  *   parents        int32 [sum_N], as for tree_attn_build_mask.
  *   mask           out uint64 [sum_N][W], W = ceil(max_nodes / 64).
  *   depth          out int32 [sum_N], nullable.
- *   tree_status    out int32 [B], nullable: 0 ok, 1 offsets out of range,
- *                  2 invalid parent (that sequence's rows are all zero).
+ *   tree_status    out int32 [B], nullable: 0 ok (also for a sequence without
+ *                  nodes), 1 offsets out of range, 2 invalid parent (that
+ *                  sequence's rows are all zero).
  *   everything else as for tree_attn_forward (workspace: the same size query,
  *                  the same zero-filled requirement).
  * Returns the first non-OK status of the checks of either call.

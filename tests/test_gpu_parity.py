@@ -185,6 +185,26 @@ def test_forward_ragged_pieces_bad_offsets_reported(ta):
                     ro, rl, fp32=False, what="pieces with a bad sequence")
 
 
+def test_forward_ragged_pieces_with_empty_sequences(ta):
+    """Longest-first pieces with two sequences that have no nodes: both
+    report status 0 like the mask builder, and every node meets the oracle."""
+    rng = np.random.default_rng(43)
+    lens = [1800, 70, 1200, 300, 900, 1500, 60, 1000, 45, 2000, 450, 120, 1300, 80, 700, 350]
+    ns = [48] * 16
+    ns[3] = ns[11] = 0
+    trees = [synthetic.random_tree(rng, n, 1, 6, 4).tolist() if n else [] for n in ns]
+    c = synthetic.make_case("emptypieces", prefix_lens=lens, trees=trees, Hq=32, Hkv=8, D=128,
+                            seed=43)
+    dc = DevCase(c)
+    out, lse, mask, _, status = ta.mask_and_forward(
+        dc.parents, dc.q, dc.k_tree, dc.v_tree, dc.k_prefix, dc.v_prefix, dc.prefix_offsets,
+        dc.node_offsets, dc.max_nodes, dc.max_prefix, c.scale, return_lse=True)
+    assert int(status.abs().sum()) == 0, status.cpu().tolist()
+    rm, _, _ = oracle.build_mask(c.parents, c.node_offsets, dc.max_nodes)
+    np.testing.assert_array_equal(mask.cpu().numpy(), rm)
+    check_attention(out, lse, *_oracle_attn(c), fp32=False, what="pieces with empty sequences")
+
+
 def test_forward_llama3_8b_full_check(ta):
     """The benchmarked workload (one 8B-shaped layer, N=64, L=4096), every
     node and head, in the same launch configuration the benchmark times."""

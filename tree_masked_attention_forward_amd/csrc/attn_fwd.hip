@@ -507,8 +507,13 @@ void fwd_bf16_kernel(KParams P) {
 
   Seq sq;
   if (!decode_seq(P, b, sq)) {
-    if (P.build && P.status_out && g == 0 && s == 0 && r == 0 && tid == 0)
-      P.status_out[b] = TA_ERR_INVALID_ARG;
+    // A sequence without nodes is valid (nothing to compute or write), as the
+    // mask builder has it; any other offset that does not decode is reported.
+    if (P.build && P.status_out && g == 0 && s == 0 && r == 0 && tid == 0) {
+      const int n0 = P.node_offsets[b];
+      const int n1 = P.node_offsets[b + 1];
+      P.status_out[b] = (n0 >= 0 && n1 == n0 && n1 <= P.total_nodes) ? 0 : TA_ERR_INVALID_ARG;
+    }
     return;
   }
   Range rgn;
