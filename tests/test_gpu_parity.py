@@ -205,6 +205,24 @@ def test_forward_ragged_pieces_with_empty_sequences(ta):
     check_attention(out, lse, *_oracle_attn(c), fp32=False, what="pieces with empty sequences")
 
 
+def test_forward_ragged_many_sequences_piece_splits(ta):
+    """80 ragged sequences (more than the longest-first order takes): pieces
+    of about equal length with the standard item order, every node against
+    the oracle, both forward entry points."""
+    rng = np.random.default_rng(47)
+    lens = [int(x) for x in rng.integers(20, 400, 80)]
+    lens[7] = 1500
+    trees = [synthetic.random_tree(rng, int(n), 1, 4, 3).tolist() for n in rng.integers(1, 9, 80)]
+    c = synthetic.make_case("ragged80", prefix_lens=lens, trees=trees, Hq=4, Hkv=1, D=128, seed=47)
+    dc, mask = _check_mask(ta, c)
+    out, lse = gpu_forward(ta, dc, mask)
+    check_attention(out, lse, *_oracle_attn(c), fp32=False, what="80 ragged sequences")
+    fo, fl, _, _, fs = ta.mask_and_forward(dc.parents, dc.q, dc.k_tree, dc.v_tree, dc.k_prefix,
+                                           dc.v_prefix, dc.prefix_offsets, dc.node_offsets,
+                                           dc.max_nodes, dc.max_prefix, c.scale, return_lse=True)
+    assert torch.equal(fo, out) and torch.equal(fl, lse) and int(fs.abs().sum()) == 0
+
+
 def test_forward_llama3_8b_full_check(ta):
     """The benchmarked workload (one 8B-shaped layer, N=64, L=4096), every
     node and head, in the same launch configuration the benchmark times."""
