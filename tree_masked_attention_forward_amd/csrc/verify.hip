@@ -44,16 +44,41 @@ __device__ inline bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// One step of the wave reduction with a DPP lane move inside each row of 16
+// lanes (CTRL: a DPP control code whose pairing covers the row).
+template <int CTRL>
+__device__ inline void best_dpp(float& bv, int& bi) {
+  const float ov = __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xf, 0xf, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, bi, CTRL, 0xf, 0xf, false);
+  if (better(ov, oi, bv, bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
+// Best (value, index) of the wave, in every lane.  "Larger value, then lower
+// index" is a strict order, so any pairing gives the same winner: lane moves
+// within each row of 16 (quad swaps by 1 and 2, then the 8- and 16-lane
+// mirrors), then the four rows' winners read as uniform values.
 __device__ inline void wave_best(float& bv, int& bi) {
+  best_dpp<0xB1>(bv, bi);    // quad_perm [1,0,3,2]
+  best_dpp<0x4E>(bv, bi);    // quad_perm [2,3,0,1]
+  best_dpp<0x141>(bv, bi);   // row_half_mirror
+  best_dpp<0x140>(bv, bi);   // row_mirror
+  float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+  int i = __builtin_amdgcn_readlane(bi, 0);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(bv, o);
-    const int oi = __shfl_xor(bi, o);
-    if (better(ov, oi, bv, bi)) {
-      bv = ov;
-      bi = oi;
+  for (int row = 1; row < 4; ++row) {
+    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * row));
+    const int ri = __builtin_amdgcn_readlane(bi, 16 * row);
+    if (better(rv, ri, v, i)) {
+      v = rv;
+      i = ri;
     }
   }
+  bv = v;
+  bi = i;
 }
 
 // VEC: elements per 16-byte load (8 for bf16, 4 for fp32), or 1 for scalar
@@ -151,6 +176,32 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const void* __
       }
     ws[out_row * cpr + c] = make_float2(bv, __int_as_float(bi));
   }
+}
+
+// One step of a wave's 64-bit maximum with a DPP lane move inside each row.
+template <int CTRL>
+__device__ inline unsigned long long max_dpp(unsigned long long x) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (uint32_t)x, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (uint32_t)(x >> 32), CTRL, 0xf, 0xf, false);
+  const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+  return o > x ? o : x;
+}
+
+// Maximum over the wave, in every lane: the same pairings as wave_best.
+__device__ inline unsigned long long wave_max_u64(unsigned long long x) {
+  x = max_dpp<0xB1>(x);
+  x = max_dpp<0x4E>(x);
+  x = max_dpp<0x141>(x);
+  x = max_dpp<0x140>(x);
+  unsigned long long m = 0ull;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) {
+    const unsigned long long r =
+        ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(x >> 32), 16 * row) << 32) |
+        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 16 * row);
+    m = r > m ? r : m;
+  }
+  return m;
 }
 
 // Inputs of one sequence that path_select_kernel keeps in registers: slot k
@@ -306,11 +357,7 @@ __global__ __launch_bounds__(kThreads) void path_select_kernel(
       key = k > key ? k : key;
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const unsigned long long ok2 = __shfl_xor(key, o);
-    key = ok2 > key ? ok2 : key;
-  }
+  key = wave_max_u64(key);
   if (lane == 0) red[wave] = key;
   __syncthreads();
   key = red[0];
@@ -478,11 +525,7 @@ __global__ __launch_bounds__(kBigThreads) void path_select_large_kernel(
       key = k > key ? k : key;
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const unsigned long long ok2 = __shfl_xor(key, o);
-    key = ok2 > key ? ok2 : key;
-  }
+  key = wave_max_u64(key);
   if (lane == 0) red[wave] = key;
   __syncthreads();
   key = red[0];
