@@ -169,6 +169,23 @@ __device__ inline bool row_tile_range(const KParams& P, const Seq& sq, int r, Ra
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lanes l and l^32 hold the two halves of one query row.  v_permlane32_swap
+// exchanges the wave's two 32-lane halves in the VALU (no LDS round trip), so
+// each lane sees both values of its row.
+__device__ inline float2 row_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float row_max(float x) {
+  const float2 h = row_halves(x);
+  return fmaxf(h.x, h.y);
+}
+__device__ inline float row_sum(float x) {
+  const float2 h = row_halves(x);
+  return h.x + h.y;
+}
+
 // Grid item of (sequence b, KV head g, split s, row tile r).  Split-major
 // order (b, s, g, r) lets one XCD stream whole key rows of a key range; the
 // in-kernel merge uses head-major order (b, g, s, r) so that every split of a
@@ -749,7 +766,7 @@ void fwd_bf16_kernel(KParams P) {
     for (int j = 0; j < TPW; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sc[j][v]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = row_max(mt);
     // Lazy running max: the reference moves only when the block's max exceeds
     // it by more than kLazyLog2 (log2 units), so after the first tiles the
     // output is almost never rescaled; probabilities stay below 2^kLazyLog2
@@ -994,7 +1011,7 @@ void fwd_bf16_kernel(KParams P) {
 
   // No wave leaves early from here on: with the in-kernel merge every wave
   // takes part in the arrival barrier below.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = row_sum(l_run);
   if (!(group_active && row_ok)) keep_lo = keep_hi = false;
   // Accumulator v of oacc[e] holds dim 32e + 8*(v/4) + 4*hh + v%4 of this row.
   if (rgn.Sb == 1) {
