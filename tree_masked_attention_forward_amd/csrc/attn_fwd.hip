@@ -31,7 +31,8 @@
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T
 //     held in registers for the whole kernel): each lane holds 16 keys of ONE
 //     query row and lane^32 holds the other 16, so the row max is one
-//     cross-lane step and the output rescale is one factor per lane;
+//     cross-lane step (v_permlane32_swap) and the output rescale is one
+//     factor per lane;
 //   * online softmax in fp32 in the log2 domain (scale*log2(e) folded into one
 //     FMA before v_exp_f32); the running max is lazy (it moves only when a
 //     tile exceeds it by 2^8), so the 64-register rescale of O is rare;
