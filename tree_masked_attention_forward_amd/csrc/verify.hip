@@ -57,6 +57,26 @@ __device__ inline void best_dpp(float& bv, int& bi) {
   }
 }
 
+// Best (value, index) over aligned segments of cpr lanes (cpr a power of two,
+// at most 64), in every lane of the segment: a butterfly over lane ^ o; the
+// swaps by 1 and 2 are DPP quad moves, wider ones LDS permutes.
+__device__ inline void seg_best(float& bv, int& bi, int cpr) {
+  for (int o = cpr >> 1; o > 0; o >>= 1) {
+    if (o == 1) {
+      best_dpp<0xB1>(bv, bi);   // quad_perm [1,0,3,2] = lane ^ 1
+    } else if (o == 2) {
+      best_dpp<0x4E>(bv, bi);   // quad_perm [2,3,0,1] = lane ^ 2
+    } else {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+  }
+}
+
 // Best (value, index) of the wave, in every lane.  "Larger value, then lower
 // index" is a strict order, so any pairing gives the same winner: lane moves
 // within each row of 16 (quad swaps by 1 and 2, then the 8- and 16-lane
@@ -274,14 +294,7 @@ __global__ __launch_bounds__(kThreads) void path_select_kernel(
       bv = x.x;
       bi = __float_as_int(x.y);
     }
-    for (int o = cpr >> 1; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    seg_best(bv, bi, cpr);
     if (pidx < pairs && (pidx & (cpr - 1)) == 0) {
       const int i = pidx / cpr;
       tgt[i] = bi;
@@ -446,14 +459,7 @@ __global__ __launch_bounds__(kBigThreads) void path_select_large_kernel(
       bv = x.x;
       bi = __float_as_int(x.y);
     }
-    for (int o = cpr >> 1; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    seg_best(bv, bi, cpr);
     if (pidx < pairs && (pidx & (cpr - 1)) == 0) {
       tgt[pidx / cpr] = bi;
       if (target_argmax) target_argmax[n0 + pidx / cpr] = bi;
