@@ -722,12 +722,16 @@ void fwd_bf16_kernel(KParams P) {
     f32x16_t sacc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+    // All eight K fragments are requested before the MFMA chain starts, so
+    // the chain waits for the LDS once instead of before every MFMA.
+    u32x4_t kf[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(kb + koff[i]);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv), qf[i],
+    for (int i = 0; i < 8; ++i) kf[i] = *reinterpret_cast<const u32x4_t*>(kb + koff[i]);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[i]), qf[i],
                                                      sacc, 0, 0, 0);
-    }
     return sacc;
   };
 
