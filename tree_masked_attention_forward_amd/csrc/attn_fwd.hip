@@ -972,17 +972,35 @@ void fwd_bf16_kernel(KParams P) {
     // other two to its partner with its running max and sum, and both
     // combine and store half of the rows' dims.  Layout [rg][kg][v][lane].
     static_assert(KG == 2, "key groups are merged in pairs");
-    float* xo = reinterpret_cast<float*>(lds);
-    float* xm = xo + RG * 2 * 32 * 64;
+    // Each lane's 32 values sit in one row of 9 float4 (32 values and 4
+    // pad floats): 16-byte accesses, and consecutive lanes start on distinct
+    // banks.
+    constexpr int kRowF4 = 9;
+    f32x4_t* xo = reinterpret_cast<f32x4_t*>(lds);
+    float* xm = reinterpret_cast<float*>(xo + RG * 2 * 64 * kRowF4);
     float* xl = xm + RG * 2 * 64;
     const int mine = rg * 2 + kg;
     const int other = rg * 2 + (kg ^ 1);
+    // Register arrays are only ever indexed with constants (a runtime index
+    // would move them to scratch memory), hence the per-key-group branches.
+    auto put4 = [&](int e2, int q, const f32x16_t& src) {
+      xo[(mine * 64 + lane) * kRowF4 + 4 * e2 + q] =
+          f32x4_t{src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3]};
+    };
     if (group_active) {
+      if (kg == 0) {
 #pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2)
+        for (int q = 0; q < 4; ++q) {
+          put4(0, q, oacc[2]);
+          put4(1, q, oacc[3]);
+        }
+      } else {
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          xo[(mine * 32 + 16 * e2 + v) * 64 + lane] = kg == 0 ? oacc[2 + e2][v] : oacc[e2][v];
+        for (int q = 0; q < 4; ++q) {
+          put4(0, q, oacc[0]);
+          put4(1, q, oacc[1]);
+        }
+      }
       xm[mine * 64 + lane] = m_run;
       xl[mine * 64 + lane] = l_run;
     }
@@ -993,20 +1011,25 @@ void fwd_bf16_kernel(KParams P) {
     const float mu = (mm == kNegInf) ? 0.f : mm;
     const float a0 = fast_exp2((m_run - mu) * c2);
     const float a1 = fast_exp2((m1 - mu) * c2);
+    auto get4 = [&](int e2, int q, f32x16_t& dst) {
+      const f32x4_t t = xo[(other * 64 + lane) * kRowF4 + 4 * e2 + q];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) dst[4 * q + x] = dst[4 * q + x] * a0 + t[x] * a1;
+    };
     if (!group_active) {
       // idle row group: nothing to combine (its outputs are never written)
     } else if (kg == 0) {
 #pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          oacc[e2][v] = oacc[e2][v] * a0 + xo[(other * 32 + 16 * e2 + v) * 64 + lane] * a1;
+      for (int q = 0; q < 4; ++q) {
+        get4(0, q, oacc[0]);
+        get4(1, q, oacc[1]);
+      }
     } else {
 #pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          oacc[2 + e2][v] = oacc[2 + e2][v] * a0 + xo[(other * 32 + 16 * e2 + v) * 64 + lane] * a1;
+      for (int q = 0; q < 4; ++q) {
+        get4(0, q, oacc[2]);
+        get4(1, q, oacc[3]);
+      }
     }
     l_run = l_run * a0 + l1 * a1;
     m_run = mm;
