@@ -78,9 +78,12 @@ def parse():
 
 
 def src_hash(*names):
+    """Hash of the named kernel sources and of the build script (which holds
+    their compile flags): a change to either means a different kernel."""
     h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "tree_masked_attention_forward_amd", "csrc", n), "rb") as f:
+    pkg = os.path.join(ROOT, "tree_masked_attention_forward_amd")
+    for path in [os.path.join(pkg, "csrc", n) for n in names] + [os.path.join(pkg, "build.py")]:
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
