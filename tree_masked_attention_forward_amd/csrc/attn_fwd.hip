@@ -358,16 +358,13 @@ __device__ void merge_in_kernel(const KParams& P, long long m) {
   __shared__ unsigned long long seen_word;
   __shared__ int timed_out;
   if (tid == 0) {
-    // Poll with an atomic add of zero, written out because the compiler turns
-    // an idempotent read-modify-write into a plain load, which could keep
-    // reading a stale copy of the counter.
+    // Poll with a relaxed agent-scope atomic load (coherent with the splits'
+    // agent-scope adds, never a cached copy); it returns sooner than an
+    // atomic add of zero would.
     unsigned long long seen = 0;
     int n = 0;
     for (; n < kSpinMax; ++n) {
-      asm volatile("global_atomic_add_x2 %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)"
-                   : "=v"(seen)
-                   : "v"(word), "v"(0ull)
-                   : "memory");
+      seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if ((seen & 255) == (unsigned long long)rgn.Sb) break;
       __builtin_amdgcn_s_sleep(4);
     }
