@@ -149,7 +149,7 @@ TA_API size_t tree_attn_forward_workspace_size(int dtype, int32_t B, int32_t tot
  *                  largest size needed) serves calls of any shapes.  A
  *                  workspace whose counters are not zero does not hang a
  *                  call: the affected outputs are written as NaN after a
- *                  bounded wait (about 0.3 s) and the counters are zeroed for
+ *                  bounded wait (2^18 polls, under a second) and the counters are zeroed for
  *                  the next call.  Calls sharing one workspace must be ordered
  *                  on one stream.
  */

@@ -334,7 +334,7 @@ __device__ inline void store_merged(const KParams& P, const Seq& sq, int g, int 
 // of a possibly stale result.  Each merge workgroup counts itself done right
 // after its poll succeeds, and the last one of a group returns the group's
 // counters to zero for the next call.  The wait is bounded
-// (about 0.3 s), so counters that were not zero at entry cannot hang a call:
+// (2^18 polls, under a second), so counters that were not zero at entry cannot hang a call:
 // a merge workgroup that times out writes NaN and zeroes the counters, so
 // the next call starts clean.
 constexpr int kSpinMax = 1 << 18;
