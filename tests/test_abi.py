@@ -144,6 +144,16 @@ def test_kv_commit_host_validation(lib):
     assert _commit(lib, kc=None) == 1              # cache rows but no cache pointer
     assert _commit(lib, cl=None) == 1              # the lengths are required
     assert _commit(lib, tc=-1) == 1
+    # A tree buffer inside a cache buffer is refused before any HIP call; each
+    # case overlaps exactly one (tree, cache) pair.  (No case here passes the
+    # checks: that would launch a kernel on made-up addresses.)
+    row = 8 * 128 * 2
+    far = dict(kt=1 << 30, vt=(1 << 30) + (1 << 24), kc=1 << 32, vc=(1 << 32) + (1 << 28))
+    for tree, cache, at in (("kt", "kc", 0), ("vt", "vc", 99), ("kt", "vc", 50),
+                            ("vt", "kc", -9)):
+        kw = dict(far)
+        kw[tree] = far[cache] + at * row   # 10 tree rows starting at cache row `at`
+        assert _commit(lib, **kw) == 1, (tree, cache, at)
 
 
 def test_verify_next_host_validation(lib):

@@ -60,21 +60,50 @@ def test_in_kernel_merge_reuses_one_workspace():
 def test_in_kernel_merge_with_nonzero_workspace_fails_loudly_then_recovers():
     """Counters left non-zero (a workspace that was never zero-filled) must not
     hang the call: after the bounded wait the outputs that the in-kernel merge
-    writes are NaN, never a plausible wrong value, and the counters are zeroed
-    so the next call on that workspace is right again."""
+    writes are NaN, never a plausible wrong value, the merge status word says
+    so, and the counters are reset so the next call on that workspace is right
+    again (status 0)."""
     ta = lib()
     c = config_case("llama3_8b")
     dc, mask, n = _setup(ta, c)
     clean = torch.zeros(n, dtype=torch.uint8, device="cuda")
     ref_o, ref_l = _forward(ta, dc, mask, clean)
     ref_o, ref_l = ref_o.clone(), ref_l.clone()
+    assert ta.merge_status(clean) == 0
     dirty = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
+    dirty[:4].zero_()                       # the status word alone starts clean
     o, l = _forward(ta, dc, mask, dirty)
     torch.cuda.synchronize()
+    st = ta.merge_status(dirty, clear=True)
+    print(f"merge status after the dirty call: {st}", flush=True)
+    assert st & (ta.TA_MERGE_TIMEOUT | ta.TA_MERGE_STALE), st
+    assert not st & ta.TA_MERGE_PLACEMENT, st
     bad = ~torch.isfinite(o.float()).all(dim=-1)
+    assert bool(bad.any()), "a failed merge must not look like a result"
     assert torch.equal(o[~bad], ref_o[~bad]), "finite outputs must be the right ones"
     o, l = _forward(ta, dc, mask, dirty)
     assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+    assert ta.merge_status(dirty) == 0
+
+
+def test_in_kernel_merge_status_stays_zero_over_many_calls():
+    """Clean calls, also alternating two inputs on one workspace, never set a
+    status bit (the epoch tags of consecutive calls differ, and each call sees
+    only its own arrivals)."""
+    ta = lib()
+    ca = config_case("llama3_8b")
+    cb = synthetic.make_config_case("llama3_8b", with_logits=False, seed=7)
+    da, ma, n = _setup(ta, ca)
+    db, mb, _ = _setup(ta, cb)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    oa, _ = _forward(ta, da, ma, ws)
+    oa = oa.clone()
+    ob, _ = _forward(ta, db, mb, ws)
+    ob = ob.clone()
+    for rep in range(20):
+        o, _ = _forward(ta, da if rep % 2 else db, ma if rep % 2 else mb, ws)
+        assert torch.equal(o, oa if rep % 2 else ob), rep
+    assert ta.merge_status(ws) == 0
 
 
 def test_workspace_shared_across_shapes():

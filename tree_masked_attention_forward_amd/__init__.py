@@ -15,6 +15,9 @@ from ._binding import (  # noqa: F401
     TA_ERR_WORKSPACE,
     TA_F32,
     TA_MAX_NODES,
+    TA_MERGE_PLACEMENT,
+    TA_MERGE_STALE,
+    TA_MERGE_TIMEOUT,
     TA_OK,
     TreeAttnError,
     build_mask,
@@ -24,6 +27,7 @@ from ._binding import (  # noqa: F401
     load_library,
     mask_and_forward,
     mask_words,
+    merge_status,
     status_string,
     verify_greedy,
     verify_greedy_next,

@@ -25,6 +25,9 @@ TA_ERR_HIP = 5
 TA_F32 = 0
 TA_BF16 = 1
 TA_MAX_NODES = 4096
+TA_MERGE_PLACEMENT = 1
+TA_MERGE_TIMEOUT = 2
+TA_MERGE_STALE = 4
 
 _c_void_p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -154,6 +157,18 @@ def forward_workspace_size(dtype: torch.dtype, B: int, total_nodes: int, max_nod
     code = TA_BF16 if dtype == torch.bfloat16 else TA_F32
     return int(load_library().tree_attn_forward_workspace_size(
         code, B, total_nodes, max_nodes, Hq, Hkv, D, total_prefix, max_prefix))
+
+
+def merge_status(workspace: torch.Tensor, clear: bool = False) -> int:
+    """The merge status word of a forward workspace (the uint32 at byte 0; bits
+    TA_MERGE_*), read after synchronising the current stream; with clear=True
+    it is zeroed afterwards."""
+    word = workspace.view(torch.uint8)[:4]
+    torch.cuda.current_stream(workspace.device).synchronize()
+    value = int.from_bytes(bytes(word.cpu().tolist()), "little")
+    if clear:
+        word.zero_()
+    return value
 
 
 def _forward_args(q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets, node_offsets,

@@ -53,6 +53,13 @@ constexpr int kMaxF32HeadDim = 256;
 
 bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
 
+// Whether the byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void* a, unsigned long long na, const void* b, unsigned long long nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a);
+  const uintptr_t y = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? TA_OK : TA_ERR_HIP; }
 
 }  // namespace
@@ -303,6 +310,18 @@ int tree_kv_commit(int dtype, const void* k_tree, const void* v_tree,
   if (total_cache > 0 && (!k_cache || !v_cache)) return TA_ERR_INVALID_ARG;
   const long long row_bytes = (long long)Hkv * D * (dtype == TA_BF16 ? 2 : 4);
   if (row_bytes > (1LL << 30) || total_cache > (1LL << 40)) return TA_ERR_UNSUPPORTED;
+  // The rows are copied in parallel, so a tree buffer inside a cache buffer
+  // (draft K/V appended after the prefix in the same allocation) could be
+  // overwritten before it is read: such calls are refused.
+  if (total_nodes > 0 && total_cache > 0) {
+    const unsigned long long tree_len = (unsigned long long)total_nodes * row_bytes;
+    const unsigned long long cache_len = (unsigned long long)total_cache * row_bytes;
+    const void* trees[2] = {k_tree, v_tree};
+    const void* caches[2] = {k_cache, v_cache};
+    for (const void* t : trees)
+      for (const void* c : caches)
+        if (overlaps(t, tree_len, c, cache_len)) return TA_ERR_INVALID_ARG;
+  }
   return hip_status(ta::launch_kv_commit(k_tree, v_tree, node_offsets, accept_len, accept_nodes,
                                          B, total_nodes, max_nodes, row_bytes, k_cache, v_cache,
                                          cache_offsets, cache_lens, total_cache, commit_status,

@@ -76,6 +76,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;                       // head size of the MFMA path
 constexpr int kKT = 32;                       // keys per tile
@@ -86,6 +87,11 @@ constexpr int kLdsMax = 160 * 1024;           // LDS per workgroup on gfx950
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazyLog2 = 8.f;              // running-max slack: probabilities stay <= 256
+// Split partials are stored in fp16 scaled by a power of two per row, chosen
+// so that the row's largest possible value lies in [2^kPartialExp, 2^(kPartialExp+1)):
+// 11 significant bits (rounding error at most 2^-11 of the value) and a
+// factor of four below fp16's largest finite value.
+constexpr int kPartialExp = 13;
 
 struct KParams {
   const uint16_t* q;
@@ -106,12 +112,14 @@ struct KParams {
   int32_t* depth_out;
   int32_t* status_out;
   int build;
-  u32x2_t* ws_o;   // [n_items][RG][16][64] 4 x bf16: O / l in register layout
-  float2* ws_ml;   // [n_items][rows_wg]   (running max in score units, sum)
-  // In-kernel merge: per (sequence, KV head, row tile) group, the number of
-  // splits that have stored their partial and the number of merge workgroups
-  // done; null when a separate merge kernel combines the splits.
+  u32x2_t* ws_o;   // [n_items][RG][16][64] 4 x fp16: 2^k O / l in register layout
+  float2* ws_ml;   // [n_items][rows_wg]   running max (score units), sum carrying k
+  // In-kernel merge: per (sequence, KV head, row tile) group, four words
+  // (arrivals, arrival tags, epoch, merge workgroups done; see
+  // merge_in_kernel), and the call status word; null when a separate merge
+  // kernel combines the splits.
   unsigned long long* cnt;
+  unsigned int* merge_status;
   long long total_prefix, max_prefix, n_items;
   long long n_split_blocks;   // workgroups [0, n_split_blocks) run splits
   int merge_wpg;              // merge workgroups per group (in-kernel merge)
@@ -238,16 +246,50 @@ __device__ inline bool lpt_piece(const KParams& P, long long k, int& b, int& g, 
 // Hardware id of the XCD this wave runs on (HW_REG_XCC_ID, bits 3:0).
 __device__ inline int xcc_id() { return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & 15; }
 
-// Arrival word of one group: bits 0..7 count the splits that stored their
-// partial, and 7 bits per XCD (from bit 8) count them per XCD, so the merge
-// can check that every split ran on its own XCD.
-__device__ inline unsigned long long arrival_word(int xcc) {
-  return 1ull + (1ull << (8 + 7 * xcc));
+// Counter block of the in-kernel merge at the start of the workspace: the
+// call status word (uint32 at byte 0), then from byte kGroupBase four 64-bit
+// words per (sequence, KV head, row tile) group: arrivals, epoch, merge
+// workgroups done, unused.
+constexpr int kGroupBase = 64;
+constexpr int kGroupBytes = 32;
+
+// Arrival word of one split: bits 0..5 count the splits that stored their
+// partial, 6 bits per XCD (from bit 6) count them per XCD, so the merge can
+// check that every split ran on its own XCD, and bits 54..63 add up the
+// splits' tags (2E + 1 for the group's epoch E, modulo 2^10), so arrivals of
+// another call never complete this call's sum.  At most 32 splits per group.
+__device__ inline unsigned long long arrival_word(int xcc, unsigned long long epoch) {
+  return 1ull + (1ull << (6 + 6 * xcc)) + (((2ull * epoch + 1ull) & 1023ull) << 54);
+}
+
+// Sum of the arrival words of `sb` splits on XCD `xcc` in epoch `epoch`.
+__device__ inline unsigned long long group_complete(int sb, int xcc, unsigned long long epoch) {
+  const unsigned long long n = (unsigned long long)sb;
+  return n + (n << (6 + 6 * xcc)) + (((n * (2ull * epoch + 1ull)) & 1023ull) << 54);
+}
+
+__device__ inline unsigned long long load_agent(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Stored partial of one row (split epilogue): 4 x fp16 per 8 bytes, each the
+// normalised value times 2^k, and the row's running max m and sum l, whose
+// low 8 mantissa bits hold k + 128 (a relative change of l below 2^-15).
+__device__ inline f32x4_t unpack_f16x4(u32x2_t v) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x4_t, v), f32x4_t);
+}
+__device__ inline float partial_sum(float2 m_l) {
+  return __uint_as_float(__float_as_uint(m_l.y) & ~255u);
+}
+// 2^-k, the factor that undoes the row's scale.
+__device__ inline float partial_unscale(float2 m_l) {
+  const int k = (int)(__float_as_uint(m_l.y) & 255u) - 128;
+  return __uint_as_float((uint32_t)(127 - k) << 23);
 }
 
 // Log-sum-exp merge of the splits of one (sequence, KV head, row tile, row
 // group, 32-dim block e, 8-dim slice j): split s left its normalised output
-// O_s (bf16), its running max m_s and sum l_s; with M = max_s m_s and
+// O_s, its running max m_s and sum l_s; with M = max_s m_s and
 // w_s = l_s * exp(scale*(m_s - M)),
 //   out = sum_s w_s O_s / sum_s w_s,  lse = scale*M + log(sum_s w_s).
 // Splits that saw no visible key carry m = -inf and weigh nothing.  Lane
@@ -257,13 +299,12 @@ struct MergeAcc {
   float lsum = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   __device__ void add(float2 m_l, u32x2_t hv, float c2) {
-    const f32x4_t o = {__uint_as_float(hv[0] << 16), __uint_as_float(hv[0] & 0xffff0000u),
-                       __uint_as_float(hv[1] << 16), __uint_as_float(hv[1] & 0xffff0000u)};
+    const float l = partial_sum(m_l);
     const float m_new = fmaxf(M, m_l.x);
     const float mu = (m_new == kNegInf) ? 0.f : m_new;
     const float a = fast_exp2((M - mu) * c2);
-    const float w = fast_exp2((m_l.x - mu) * c2) * m_l.y;
-    acc = acc * a + w * o;
+    const float w = fast_exp2((m_l.x - mu) * c2) * l;
+    acc = acc * a + (w * partial_unscale(m_l)) * unpack_f16x4(hv);
     lsum = lsum * a + w;
     M = m_new;
   }
@@ -324,20 +365,31 @@ __device__ inline void store_merged(const KParams& P, const Seq& sq, int g, int 
 // 8 XCDs round-robin by id, and the item order puts all splits of a
 // (sequence, KV head) on one XCD; merge workgroup m also runs on XCD m % 8 and
 // takes groups of that XCD.  Partials then stay in that XCD's L2, which is
-// coherent for all its CUs, so no L2 write-back or invalidate is needed: a
-// split stores its partial, waits for the stores to be acknowledged, and
-// adds its arrival word (count + per-XCD count) to the group's counter; the
-// merge workgroup polls the counter until the count reaches the group's
-// split count, checks that every split ran on its own XCD, and merges
-// RG*16/NW (row group, 32-dim block, 8-dim slice) units, one per wave.  If
-// the XCD check fails (workgroups not dealt as assumed) it writes NaN instead
-// of a possibly stale result.  Each merge workgroup counts itself done right
-// after its poll succeeds, and the last one of a group returns the group's
-// counters to zero for the next call.  The wait is bounded
-// (2^18 polls, under a second), so counters that were not zero at entry cannot hang a call:
-// a merge workgroup that times out writes NaN and zeroes the counters, so
-// the next call starts clean.
+// coherent for all its CUs, so no L2 write-back or invalidate is needed.
+//
+// Protocol.  Every workgroup of a group reads the group's epoch E at its
+// start; E only changes once all of them have read it (below).  A split
+// stores its partial, waits for the stores to be acknowledged, and adds its
+// arrival word (count, per-XCD count, tag of E) to the group's arrivals.  A
+// merge workgroup polls the arrivals until the count reaches the group's
+// split count Sb; the partials are this call's and coherent in its L2 iff the
+// arrivals then equal group_complete(Sb, its XCD, E): every split ran on its
+// own XCD and every arrival carries this epoch's tag.  Then it merges RG*16/NW
+// (row group, 32-dim block, 8-dim slice) units, one per wave, and counts
+// itself done; the last one of a group returns arrivals and done count to
+// zero and advances E, so the next call's tags differ from this call's.
+// When the check fails it writes NaN instead of a possibly stale result and
+// sets a bit in the call status word (kMergeStatus*, the caller's way to
+// tell).  The wait is bounded (2^18 polls, under a second), so counters that
+// were not zero at entry cannot hang a call: a merge workgroup that times out
+// writes NaN, zeroes the group's words and advances E itself.  A split of a
+// timed-out call that arrives after that reset carries the old tag, so the
+// next call fails its check loudly instead of merging its stale partial, and
+// that call's last merge workgroup zeroes the words again.
 constexpr int kSpinMax = 1 << 18;
+constexpr unsigned kMergeStatusPlacement = TA_MERGE_PLACEMENT;
+constexpr unsigned kMergeStatusTimeout = TA_MERGE_TIMEOUT;
+constexpr unsigned kMergeStatusStale = TA_MERGE_STALE;
 
 template <int RG, int NW>
 __device__ void merge_in_kernel(const KParams& P, long long m) {
@@ -354,33 +406,52 @@ __device__ void merge_in_kernel(const KParams& P, long long m) {
   Seq sq;
   Range rgn;
   if (!decode_seq(P, b, sq) || !row_tile_range(P, sq, r, rgn) || rgn.Sb <= 1) return;
-  unsigned long long* word = P.cnt + 2 * gi;
-  __shared__ unsigned long long seen_word;
+  // arrivals, epoch, done
+  unsigned long long* word = P.cnt + (kGroupBase + kGroupBytes * gi) / 8;
+  __shared__ unsigned long long seen_word, seen_epoch;
   __shared__ int timed_out;
   if (tid == 0) {
-    // Poll with a relaxed agent-scope atomic load (coherent with the splits'
-    // agent-scope adds, never a cached copy); it returns sooner than an
+    // Poll with relaxed agent-scope atomic loads (coherent with the splits'
+    // agent-scope adds, never a cached copy); they return sooner than an
     // atomic add of zero would.
+    const unsigned long long ep = load_agent(word + 1);
     unsigned long long seen = 0;
     int n = 0;
     for (; n < kSpinMax; ++n) {
-      seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((seen & 255) == (unsigned long long)rgn.Sb) break;
+      seen = load_agent(word);
+      if ((seen & 63) == (unsigned long long)rgn.Sb) break;
       __builtin_amdgcn_s_sleep(4);
     }
     seen_word = seen;
+    seen_epoch = ep;
     timed_out = n == kSpinMax;
   }
   __syncthreads();
-  const bool coherent =
-      !timed_out && seen_word == (unsigned long long)rgn.Sb * arrival_word(xcc_id());
+  const int xcc = xcc_id();
+  const bool coherent = !timed_out && seen_word == group_complete(rgn.Sb, xcc, seen_epoch);
   // Every merge workgroup counts itself done as soon as it has seen its group
   // complete (its round trip then overlaps the partial loads below); once all
-  // of a group's merge workgroups have, nothing reads the group's counters in
-  // this call, so the last of them returns them to zero.
+  // of a group's merge workgroups have, nothing reads the group's words in
+  // this call, so the last of them resets them for the next call.
   unsigned long long done = 0ull;
-  if (tid == 0 && !timed_out)
-    done = __hip_atomic_fetch_add(word + 1, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    if (!timed_out)
+      done = __hip_atomic_fetch_add(word + 2, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!coherent) {
+      // Which check failed: a count beyond the splits' own (per XCD) means
+      // another call's arrivals; a count on another XCD, a placement failure.
+      // Placement: the per-XCD counts account for every arrival but not all
+      // on this XCD.  Otherwise the words hold arrivals of another call.
+      int per_xcd = 0;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) per_xcd += (int)((seen_word >> (6 + 6 * x)) & 63ull);
+      const bool all_here = (int)((seen_word >> (6 + 6 * xcc)) & 63ull) == rgn.Sb;
+      const unsigned bits = timed_out ? kMergeStatusTimeout
+                            : (per_xcd == rgn.Sb && !all_here) ? kMergeStatusPlacement
+                                                               : kMergeStatusStale;
+      __hip_atomic_fetch_or(P.merge_status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 
   const int rg = unit >> 4;
   const int e = (unit >> 2) & 3;
@@ -397,15 +468,12 @@ __device__ void merge_in_kernel(const KParams& P, long long m) {
       // split count re-read split 0 and are ignored), so the merge waits on
       // one L2 round trip instead of one per split.
       auto load_ml = [&](long long it) {
-        return __hip_atomic_load(
-            reinterpret_cast<const unsigned long long*>(P.ws_ml + (size_t)it * P.rows_wg + rl),
-            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return load_agent(
+            reinterpret_cast<const unsigned long long*>(P.ws_ml + (size_t)it * P.rows_wg + rl));
       };
       auto load_o = [&](long long it) {
-        return __hip_atomic_load(
-            reinterpret_cast<const unsigned long long*>(
-                P.ws_o + (((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane),
-            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return load_agent(reinterpret_cast<const unsigned long long*>(
+            P.ws_o + (((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane));
       };
       constexpr int kBatch = 16;
       unsigned long long mlv[kBatch], ov[kBatch];
@@ -435,7 +503,9 @@ __device__ void merge_in_kernel(const KParams& P, long long m) {
   if (tid == 0) {
     if (timed_out || done + 1 == (unsigned long long)P.merge_wpg) {
       __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(word + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(word + 2, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(word + 1, seen_epoch + 1ull, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -534,6 +604,14 @@ void fwd_bf16_kernel(KParams P) {
   Range rgn;
   if (!row_tile_range(P, sq, r, rgn)) return;
   if (s >= rgn.Sb) return;
+  // In-kernel merge: this group's words, and its epoch, read now so that the
+  // arrival after the key loop does not wait for it.
+  unsigned long long* grp_word = nullptr;
+  unsigned long long epoch = 0ull;
+  if (P.cnt && rgn.Sb > 1) {
+    grp_word = P.cnt + (kGroupBase + kGroupBytes * (((long long)b * P.Hkv + g) * P.R + r)) / 8;
+    epoch = load_agent(grp_word + 1);
+  }
   const int t_lo = (int)((long long)s * rgn.T / rgn.Sb);
   const int t_hi = (int)((long long)(s + 1) * rgn.T / rgn.Sb);
   const int L = sq.L;
@@ -959,10 +1037,29 @@ void fwd_bf16_kernel(KParams P) {
     if (r == 0 && tid == 0 && P.status_out)
       P.status_out[b] = tree_bad ? TA_ERR_INVALID_TREE : 0;
   }
+  // Split partials: this lane's largest |O| (un-normalised), for the scale
+  // of its row's stored partial (see the partial stores below).
+  float mx = 0.f;
+  if (rgn.Sb > 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, fabsf(oacc[e][v]));
+  }
   __syncthreads();
 
   // Dim blocks (32 dims each) this wave combines and stores.
   bool keep_lo = true, keep_hi = true;
+  // Split partials: a bound on the row's normalised |O| (no smaller than any
+  // of its values), from which the row's scale is taken.
+  auto ratio = [&](float mxl, float ll) {
+    const float lr = row_sum(ll);
+    return lr > 0.f ? row_max(mxl) * __builtin_amdgcn_rcpf(lr) : 0.f;
+  };
+  float bound = 0.f;
+  if constexpr (KG == 1) {
+    if (rgn.Sb > 1) bound = ratio(mx, l_run);
+  }
   if constexpr (KG > 1) {
     // The two key groups of a row group swap halves through LDS (the stage
     // buffers are free now): wave kg keeps dim blocks 2kg, 2kg+1, hands the
@@ -976,6 +1073,7 @@ void fwd_bf16_kernel(KParams P) {
     f32x4_t* xo = reinterpret_cast<f32x4_t*>(lds);
     float* xm = reinterpret_cast<float*>(xo + RG * 2 * 64 * kRowF4);
     float* xl = xm + RG * 2 * 64;
+    float* xx = xl + RG * 2 * 64;
     const int mine = rg * 2 + kg;
     const int other = rg * 2 + (kg ^ 1);
     // Register arrays are only ever indexed with constants (a runtime index
@@ -1000,10 +1098,14 @@ void fwd_bf16_kernel(KParams P) {
       }
       xm[mine * 64 + lane] = m_run;
       xl[mine * 64 + lane] = l_run;
+      xx[mine * 64 + lane] = mx;
     }
     __syncthreads();
     const float m1 = xm[other * 64 + lane];
     const float l1 = xl[other * 64 + lane];
+    // The combined row is a convex combination of the two key groups'
+    // normalised rows, so the larger of their bounds bounds it.
+    if (rgn.Sb > 1) bound = fmaxf(ratio(mx, l_run), ratio(xx[other * 64 + lane], l1));
     const float mm = fmaxf(m_run, m1);
     const float mu = (mm == kNegInf) ? 0.f : mm;
     const float a0 = fast_exp2((m_run - mu) * c2);
@@ -1057,11 +1159,18 @@ void fwd_bf16_kernel(KParams P) {
     if (P.lse && hh == 0 && keep_lo)
       P.lse[(size_t)(sq.n0 + node) * P.Hq + head] = m_run * P.scale + logf(l_tot);
   } else {
-    // Normalised partial O in bf16 (the merge reweights by l), lane-major so
-    // each store instruction writes 512 contiguous bytes.  Streaming stores:
-    // the partials are read once (by the merge), so they should not sit dirty
-    // in L2 when this kernel ends.
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // Normalised partial O (the merge reweights by l), lane-major so each
+    // store instruction writes 512 contiguous bytes, in fp16 times 2^k, the
+    // row's scale: k puts the row's bound in [2^kPartialExp, 2^(kPartialExp+1)),
+    // so no value overflows and each keeps 11 significant bits (a split over a
+    // few keys averages a few value rows, up to ~4 in size, where a bf16
+    // rounding would already cost 0.0078).  k + 128 rides in the low 8 bits
+    // of the stored sum.  Streaming stores: the partials are read once (by
+    // the merge), so they should not sit dirty in L2 when this kernel ends.
+    const int eb = (int)((__float_as_uint(bound) >> 23) & 255u);
+    const int k = min(126, max(-126, 127 + kPartialExp - eb));
+    const float inv =
+        l_tot > 0.f ? __uint_as_float((uint32_t)(127 + k) << 23) / l_tot : 0.f;
     auto put = [&](u32x2_t* p, u32x2_t v) { __builtin_nontemporal_store(v, p); };
     u32x2_t* wo = P.ws_o + ((size_t)item * RG + rg) * 16 * 64 + lane;
 #pragma unroll
@@ -1072,20 +1181,24 @@ void fwd_bf16_kernel(KParams P) {
         f32x4_t f;
 #pragma unroll
         for (int x = 0; x < 4; ++x) f[x] = oacc[e][4 * j + x] * inv;
-        put(&wo[(4 * e + j) * 64], __builtin_bit_cast(u32x2_t, __builtin_convertvector(f, bf16x4_t)));
+        put(&wo[(4 * e + j) * 64], __builtin_bit_cast(u32x2_t, __builtin_convertvector(f, f16x4_t)));
       }
     }
-    if (hh == 0 && keep_lo)
+    if (hh == 0 && keep_lo) {
+      const float l_k = __uint_as_float((__float_as_uint(l_tot) & ~255u) | (uint32_t)(k + 128));
       put(reinterpret_cast<u32x2_t*>(P.ws_ml + (size_t)item * P.rows_wg + rg * 32 + l32),
-          __builtin_bit_cast(u32x2_t, make_float2(m_run, l_tot)));
-    if (P.cnt) {
+          __builtin_bit_cast(u32x2_t, make_float2(m_run, l_k)));
+    }
+    if (grp_word) {
       // Arrival: every thread's partial is in this XCD's L2 (its stores are
       // acknowledged) before the group's counter moves.
       __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
       __syncthreads();
+      // The epoch was requested before the key loop; the empty asm keeps the
+      // compiler from computing the tag (and so waiting for the load) there.
+      asm volatile("" : "+v"(epoch));
       if (tid == 0)
-        __hip_atomic_fetch_add(P.cnt + 2 * (((size_t)b * P.Hkv + g) * P.R + r),
-                               arrival_word(xcc_id()), __ATOMIC_RELAXED,
+        __hip_atomic_fetch_add(grp_word, arrival_word(xcc_id(), epoch), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -1117,13 +1230,16 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
   constexpr int kPre = 8;
   float2 ml[kPre];
   u32x2_t h[kPre][4];
+  auto oslot = [&](long long it, int e) {
+    return (((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane;
+  };
 #pragma unroll
   for (int k = 0; k < kPre; ++k) {
     if (k < P.S) {
       const long long it = item0 + k * split_stride;
       ml[k] = P.ws_ml[(size_t)it * P.rows_wg + rl];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) h[k][e] = P.ws_o[(((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane];
+      for (int e = 0; e < 4; ++e) h[k][e] = P.ws_o[oslot(it, e)];
     }
   }
 
@@ -1145,8 +1261,7 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
     const long long it = item0 + s * split_stride;
     const float2 m_l = P.ws_ml[(size_t)it * P.rows_wg + rl];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      ma[e].add(m_l, P.ws_o[(((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane], c2);
+    for (int e = 0; e < 4; ++e) ma[e].add(m_l, P.ws_o[oslot(it, e)], c2);
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) store_merged(P, sq, g, r, rl, e, j, hh, ma[e]);
@@ -1171,7 +1286,8 @@ hipError_t launch_shape(const KParams& kp, long long grid, long long merge_grid,
 // Largest in-kernel merge grid: half of MI355X's 256 CUs (checked against the
 // device's CU count at launch).
 constexpr long long kMaxMergeBlocks = 128;
-// Bytes of group counters at the start of a workspace that holds partials.
+// Bytes of the counter block at the start of a workspace that holds partials
+// (status word and per-group words of the in-kernel merge).
 constexpr size_t kCounterBytes = 2048;
 
 // Pieces per CU for ragged batches (see plan_forward_bf16); measured on the
@@ -1239,16 +1355,18 @@ FwdPlan plan_forward_bf16(int B, int total_nodes, int max_nodes, int Hq, int Hkv
   // always find room to run.
   // Each XCD must hold whole (sequence, KV head) blocks of items, and the
   // arrival word counts at most 127 splits per XCD.
-  p.merge_in_kernel = p.S > 1 && p.S < 128 && p.groups * p.merge_wpg <= kMaxMergeBlocks &&
+  p.merge_in_kernel = p.S > 1 && p.S <= 32 && p.groups * p.merge_wpg <= kMaxMergeBlocks &&
                       ((long long)B * Hkv) % 8 == 0 &&
-                      p.groups * 2 * sizeof(unsigned long long) <= kCounterBytes;
+                      kGroupBase + p.groups * kGroupBytes <= (long long)kCounterBytes;
   p.lpt = p.piece > 0 && p.R == 1 && B <= 64 && !p.merge_in_kernel;
   p.ws_bytes = 0;
   if (p.S > 1) {
-    // [group counters | O partials | max and sum partials].  The counter
-    // block leads every workspace that holds partials, whichever merge runs,
-    // so a buffer shared by calls of different shapes never has partials
-    // written over the counters (which every call leaves at zero).
+    // [counter block | O partials | max and sum partials].
+    // The counter block (status word, per-group words) leads every
+    // workspace that holds partials, whichever merge runs, so a buffer
+    // shared by calls of different shapes never has partials written over
+    // the counters (every completed call leaves the arrival and done words
+    // at zero; an epoch word is only ever compared with itself).
     p.ws_bytes = kCounterBytes + (size_t)p.n_items * p.rows_wg * (kD * 2 + 8);
   }
   return p;
@@ -1288,6 +1406,7 @@ hipError_t launch_forward_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t s
     // MI355X (256 CUs); elsewhere the separate merge kernel runs.
     if (p.merge_in_kernel && device_cu_count() == 256) {
       kp.cnt = reinterpret_cast<unsigned long long*>(ws);
+      kp.merge_status = reinterpret_cast<unsigned int*>(ws);
       merge_blocks = p.groups * p.merge_wpg;
       kp.head_major = 1;
     }
