@@ -182,6 +182,40 @@ TA_API int tree_attn_forward(int dtype, const void* q, const void* k_tree, const
                       size_t workspace_bytes, void* stream);
 
 /*
+ * tree_attn_forward without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and errors as
+ * tree_attn_forward, minus workspace and workspace_bytes, plus merge_status.
+ *
+ * The split partials and merge counters live in a static device array of
+ * TA_NOALLOC_MAX_WORKSPACE bytes (64 MiB) that the library holds on every GPU
+ * it runs on until the process ends; the call allocates nothing.  A call that
+ * would need more scratch than that (tree_attn_forward_workspace_size above
+ * the limit) returns TA_ERR_WORKSPACE and enqueues nothing; the 8B-shaped
+ * layer (B=1, Hq=32, Hkv=8, L=4096, N=64) needs 8.25 MiB, the 32-sequence
+ * batch of up to 8192 keys each 33 MiB.  The first call on a device also
+ * enqueues a small kernel that zeroes the array's counter block.
+ *
+ * All calls on one GPU share that GPU's array, which keeps the last call's
+ * contents: calls that may overlap on one GPU (different streams without
+ * ordering, different host threads) race and must not be made; ordered calls
+ * are safe.
+ *
+ *   merge_status   uint32 [1], device, nullable: the in-kernel merge ORs its
+ *                  failure bits (TA_MERGE_*) into it, as into the workspace's
+ *                  status word of tree_attn_forward (zero it before the call).
+ */
+#define TA_NOALLOC_MAX_WORKSPACE (64u << 20)
+TA_API int tree_attn_forward_noalloc(int dtype, const void* q, const void* k_tree,
+                                     const void* v_tree, const void* k_prefix,
+                                     const void* v_prefix, const int64_t* prefix_offsets,
+                                     const int64_t* prefix_lens, const int32_t* node_offsets,
+                                     const uint64_t* mask, int32_t B, int32_t total_nodes,
+                                     int32_t max_nodes, int64_t total_prefix, int64_t max_prefix,
+                                     int32_t Hq, int32_t Hkv, int32_t D, float scale, void* out,
+                                     float* lse, uint32_t* merge_status, void* stream);
+
+/*
  * Ancestor mask and tree attention in one call: the same results as
  * tree_attn_build_mask(parents, node_offsets, B, total_nodes, max_nodes, mask,
  * depth, tree_status) followed by tree_attn_forward(..., mask, ...) with the

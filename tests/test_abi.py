@@ -24,9 +24,10 @@ def lib():
 def test_header_declares_the_three_calls():
     names = _declared_functions()
     for n in ("tree_attn_build_mask", "tree_attn_forward", "tree_verify_greedy",
-              "tree_attn_mask_and_forward", "tree_kv_commit", "tree_verify_greedy_next"):
+              "tree_attn_mask_and_forward", "tree_kv_commit", "tree_verify_greedy_next",
+              "tree_attn_forward_noalloc"):
         assert n in names
-    assert len(names) == 9, names
+    assert len(names) == 10, names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -170,3 +171,32 @@ def test_verify_next_host_validation(lib):
     assert v(*bad) == 4
     bad = list(ok); bad[8] = 5000
     assert v(*bad) == 3
+
+
+def _noalloc(lib, **kw):
+    args = dict(dtype=1, q=1 << 20, kt=1 << 20, vt=1 << 20, kp=1 << 20, vp=1 << 20, po=1 << 20,
+                pl=None, no=1 << 20, mask=1 << 20, B=1, total=64, maxn=64, tp=4096, mp=4096, Hq=32,
+                Hkv=8, D=128, scale=0.088, out=1 << 20, lse=None, st=None, stream=None)
+    args.update(kw)
+    a = args
+    return lib.tree_attn_forward_noalloc(a["dtype"], a["q"], a["kt"], a["vt"], a["kp"], a["vp"],
+                                         a["po"], a["pl"], a["no"], a["mask"], a["B"], a["total"],
+                                         a["maxn"], a["tp"], a["mp"], a["Hq"], a["Hkv"], a["D"],
+                                         a["scale"], a["out"], a["lse"], a["st"], a["stream"])
+
+
+def test_forward_noalloc_host_validation(lib):
+    """The same host checks as tree_attn_forward, and a shape whose scratch
+    exceeds the static array is refused before any HIP call."""
+    assert _noalloc(lib, dtype=7) == 3
+    assert _noalloc(lib, B=0) == 1
+    assert _noalloc(lib, D=64) == 3
+    assert _noalloc(lib, mask=None) == 1
+    assert _noalloc(lib, total=0) == 0                 # nothing to do, nothing launched
+    # 64 ragged sequences (262144 keys, the longest 65536) x 8 KV heads: each is cut into
+    # key splits whose partials need far more than 64 MiB
+    big = dict(B=64, total=64 * 64, tp=64 * 4096, mp=65536)
+    need = lib.tree_attn_forward_workspace_size(1, big["B"], big["total"], 64, 32, 8, 128,
+                                                big["tp"], big["mp"])
+    assert need > 64 << 20, need
+    assert _noalloc(lib, **big) == 4

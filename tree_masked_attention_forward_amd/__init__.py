@@ -18,10 +18,12 @@ from ._binding import (  # noqa: F401
     TA_MERGE_PLACEMENT,
     TA_MERGE_STALE,
     TA_MERGE_TIMEOUT,
+    TA_NOALLOC_MAX_WORKSPACE,
     TA_OK,
     TreeAttnError,
     build_mask,
     forward,
+    forward_noalloc,
     forward_workspace_size,
     kv_commit,
     load_library,
@@ -39,6 +41,7 @@ load_library()
 # The C names, for readers who know the ABI.
 tree_attn_build_mask = build_mask
 tree_attn_forward = forward
+tree_attn_forward_noalloc = forward_noalloc
 tree_attn_mask_and_forward = mask_and_forward
 tree_verify_greedy = verify_greedy
 tree_kv_commit = kv_commit

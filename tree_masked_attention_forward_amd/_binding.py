@@ -28,6 +28,7 @@ TA_MAX_NODES = 4096
 TA_MERGE_PLACEMENT = 1
 TA_MERGE_TIMEOUT = 2
 TA_MERGE_STALE = 4
+TA_NOALLOC_MAX_WORKSPACE = 64 << 20
 
 _c_void_p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -65,6 +66,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tree_attn_forward.argtypes = [ctypes.c_int] + [_c_void_p] * 9 + [
         _i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32, ctypes.c_float, _c_void_p, _c_void_p,
         _c_void_p, ctypes.c_size_t, _c_void_p]
+    lib.tree_attn_forward_noalloc.restype = ctypes.c_int
+    lib.tree_attn_forward_noalloc.argtypes = [ctypes.c_int] + [_c_void_p] * 9 + [
+        _i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32, ctypes.c_float, _c_void_p, _c_void_p,
+        _c_void_p, _c_void_p]
     lib.tree_attn_mask_and_forward.restype = ctypes.c_int
     lib.tree_attn_mask_and_forward.argtypes = [ctypes.c_int] + [_c_void_p] * 9 + [
         _i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32, ctypes.c_float] + [_c_void_p] * 6 + [
@@ -243,6 +248,51 @@ def forward(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor,
         a["total_prefix"], int(max_prefix), a["Hq"], a["Hkv"], a["D"], float(scale),
         _ptr(a["out"]), _ptr(a["lse"]), _ptr(a["workspace"]), a["ws_len"], _stream(a["dev"])))
     return (a["out"], a["lse"]) if (return_lse or lse is not None) else a["out"]
+
+
+def forward_noalloc(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor,
+                    k_prefix: torch.Tensor, v_prefix: torch.Tensor, prefix_offsets: torch.Tensor,
+                    node_offsets: torch.Tensor, mask: torch.Tensor, max_nodes: int,
+                    max_prefix: int, scale: float, *, out: torch.Tensor, lse: torch.Tensor = None,
+                    merge_status: Optional[torch.Tensor] = None,
+                    prefix_lens: Optional[torch.Tensor] = None):
+    """tree_attn_forward_noalloc: tree_attn_forward on the library's static
+    scratch (no workspace; the library allocates nothing).  `out` (and `lse`)
+    must be given, so that this call allocates nothing either.  merge_status
+    (uint32 [1], optional) receives the in-kernel merge's failure bits."""
+    dev = _device_of(q)
+    dtype = q.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q must be bfloat16 or float32")
+    _need(q, "q", dtype, dev, 3)
+    total, Hq, D = q.shape
+    for name, t in (("k_tree", k_tree), ("v_tree", v_tree), ("k_prefix", k_prefix),
+                    ("v_prefix", v_prefix), ("out", out)):
+        _need(t, name, dtype, dev, 3)
+    Hkv = k_tree.shape[1]
+    if out.shape != q.shape or k_tree.shape != (total, Hkv, D) or v_tree.shape != k_tree.shape:
+        raise ValueError("q/out [sum_N, Hq, D], k_tree/v_tree [sum_N, Hkv, D]")
+    if v_prefix.shape != k_prefix.shape or tuple(k_prefix.shape[1:]) != (Hkv, D):
+        raise ValueError("k_prefix/v_prefix must be [sum_L, Hkv, D]")
+    _need(prefix_offsets, "prefix_offsets", torch.int64, dev, 1)
+    _need(node_offsets, "node_offsets", torch.int32, dev, 1)
+    _need(mask, "mask", torch.uint64, dev, 2)
+    B = node_offsets.numel() - 1
+    if prefix_offsets.numel() != B + 1 or mask.shape != (total, mask_words(max_nodes)):
+        raise ValueError("offsets hold B+1 entries; mask is [sum_N, ceil(max_nodes/64)]")
+    if prefix_lens is not None:
+        _need(prefix_lens, "prefix_lens", torch.int64, dev, 1)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, 2)
+    if merge_status is not None:
+        _need(merge_status, "merge_status", torch.int32, dev, 1)
+    code = TA_BF16 if dtype == torch.bfloat16 else TA_F32
+    _check("tree_attn_forward_noalloc", load_library().tree_attn_forward_noalloc(
+        code, _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_prefix), _ptr(v_prefix),
+        _ptr(prefix_offsets), _ptr(prefix_lens), _ptr(node_offsets), _ptr(mask), B, total,
+        int(max_nodes), k_prefix.shape[0], int(max_prefix), Hq, Hkv, D, float(scale), _ptr(out),
+        _ptr(lse), _ptr(merge_status), _stream(dev)))
+    return out
 
 
 def mask_and_forward(parents: torch.Tensor, q: torch.Tensor, k_tree: torch.Tensor,

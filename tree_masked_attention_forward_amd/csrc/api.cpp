@@ -173,6 +173,45 @@ int run_forward(int dtype, const ta::FwdArgs& a, size_t workspace_bytes, hipStre
   return hip_status(ta::launch_forward_bf16(a, p, s));
 }
 
+// ---------------------------------------------------------------------------
+// Scratch for tree_attn_forward_noalloc: the split partials and the in-kernel
+// merge's counters live in this file-scope device array instead of a caller
+// workspace.  Each GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` only names the symbol; its device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// address is ever passed to a kernel.
+constexpr size_t kNoAllocBytes = (size_t)TA_NOALLOC_MAX_WORKSPACE;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+// Zeroes n 64-bit words (the counter block, once per device).
+__global__ void clear_words_kernel(unsigned long long* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0ull;
+}
+
+// Device address of this device's scratch (null on failure).  The first call
+// on a device also enqueues, on `stream`, the zeroing of the counter block
+// that the in-kernel merge needs at its first use.
+void* noalloc_scratch(hipStream_t stream, hipError_t& err) {
+  static std::mutex mu;
+  static std::vector<void*> ptrs;
+  int dev = 0;
+  err = hipGetDevice(&dev);
+  if (err != hipSuccess || dev < 0) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)ptrs.size() <= dev) ptrs.resize(dev + 1, nullptr);
+  if (!ptrs[dev]) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !ptr) return nullptr;
+    hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, stream,
+                       static_cast<unsigned long long*>(ptr), (int)(ta::kFwdCounterBytes / 8));
+    err = hipGetLastError();
+    if (err != hipSuccess) return nullptr;
+    ptrs[dev] = ptr;
+  }
+  return ptrs[dev];
+}
+
 // Largest tree the forward kernel builds its own mask for (rows in registers).
 constexpr int kFusedMaskMaxNodes = 128;
 
@@ -197,6 +236,35 @@ int tree_attn_forward(int dtype, const void* q, const void* k_tree, const void* 
   if (!mask) return TA_ERR_INVALID_ARG;
   a.mask = mask;
   return run_forward(dtype, a, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int tree_attn_forward_noalloc(int dtype, const void* q, const void* k_tree, const void* v_tree,
+                              const void* k_prefix, const void* v_prefix,
+                              const int64_t* prefix_offsets, const int64_t* prefix_lens,
+                              const int32_t* node_offsets, const uint64_t* mask, int32_t B,
+                              int32_t total_nodes, int32_t max_nodes, int64_t total_prefix,
+                              int64_t max_prefix, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                              void* out, float* lse, uint32_t* merge_status, void* stream) {
+  ta::FwdArgs a;
+  bool empty = false;
+  const int st = check_forward(dtype, q, k_tree, v_tree, k_prefix, v_prefix, prefix_offsets,
+                               prefix_lens, node_offsets, B, total_nodes, max_nodes, total_prefix,
+                               max_prefix, Hq, Hkv, D, scale, out, lse, nullptr, a, empty);
+  if (st != TA_OK || empty) return st;
+  if (!mask) return TA_ERR_INVALID_ARG;
+  a.mask = mask;
+  a.merge_status = merge_status;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == TA_F32) return hip_status(ta::launch_forward_f32(a, s));
+  const ta::FwdPlan p = ta::plan_forward_bf16(a.B, a.total_nodes, a.max_nodes, a.Hq, a.Hkv,
+                                              a.total_prefix, a.max_prefix);
+  if (p.ws_bytes > kNoAllocBytes) return TA_ERR_WORKSPACE;
+  if (p.ws_bytes > 0) {
+    hipError_t e = hipSuccess;
+    a.workspace = noalloc_scratch(s, e);
+    if (!a.workspace) return TA_ERR_HIP;
+  }
+  return hip_status(ta::launch_forward_bf16(a, p, s));
 }
 
 int tree_attn_mask_and_forward(int dtype, const int32_t* parents, const void* q,

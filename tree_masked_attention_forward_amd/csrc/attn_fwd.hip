@@ -1288,7 +1288,7 @@ hipError_t launch_shape(const KParams& kp, long long grid, long long merge_grid,
 constexpr long long kMaxMergeBlocks = 128;
 // Bytes of the counter block at the start of a workspace that holds partials
 // (status word and per-group words of the in-kernel merge).
-constexpr size_t kCounterBytes = 2048;
+constexpr size_t kCounterBytes = kFwdCounterBytes;
 
 // Pieces per CU for ragged batches (see plan_forward_bf16); measured on the
 // 32-sequence batch: 1 beats 2, 3 and 4 (each piece pays its own first-data
@@ -1406,7 +1406,7 @@ hipError_t launch_forward_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t s
     // MI355X (256 CUs); elsewhere the separate merge kernel runs.
     if (p.merge_in_kernel && device_cu_count() == 256) {
       kp.cnt = reinterpret_cast<unsigned long long*>(ws);
-      kp.merge_status = reinterpret_cast<unsigned int*>(ws);
+      kp.merge_status = a.merge_status ? a.merge_status : reinterpret_cast<unsigned int*>(ws);
       merge_blocks = p.groups * p.merge_wpg;
       kp.head_major = 1;
     }

@@ -60,6 +60,9 @@ struct FwdArgs {
   uint64_t* mask_out;
   int32_t* depth_out;
   int32_t* status_out;
+  // Where the in-kernel merge reports failures (TA_MERGE_* bits, by OR);
+  // null: the status word at byte 0 of the workspace.
+  uint32_t* merge_status;
 };
 
 // Raises a kernel's dynamic LDS limit to at least `bytes` on the current
@@ -70,6 +73,10 @@ hipError_t raise_dynamic_lds(const void* kernel, int bytes);
 
 // Compute units of the current device (cached per device; 0 if unknown).
 int device_cu_count();
+
+// Bytes of workspace at the start of every forward workspace that the
+// in-kernel merge's counters and status word occupy (zero before first use).
+constexpr size_t kFwdCounterBytes = 2048;
 
 FwdPlan plan_forward_bf16(int B, int total_nodes, int max_nodes, int Hq, int Hkv,
                           long long total_prefix, long long max_prefix);
