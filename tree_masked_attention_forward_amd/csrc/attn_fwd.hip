@@ -272,6 +272,12 @@ __device__ inline unsigned long long load_agent(const unsigned long long* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Loads of other workgroups' partials in the in-kernel merge: agent scope,
+// past the CU's L1 (plain loads measured the same).
+__device__ inline unsigned long long load_part(const unsigned long long* p) {
+  return load_agent(p);
+}
+
 // Stored partial of one row (split epilogue): 4 x fp16 per 8 bytes, each the
 // normalised value times 2^k, and the row's running max m and sum l, whose
 // low 8 mantissa bits hold k + 128 (a relative change of l below 2^-15).
@@ -453,45 +459,55 @@ __device__ void merge_in_kernel(const KParams& P, long long m) {
     }
   }
 
-  const int rg = unit >> 4;
+  const int rg = unit >> 4;   // the same for every wave of the workgroup (NW divides 16)
   const int e = (unit >> 2) & 3;
   const int j = unit & 3;
   const int hh = lane >> 5;
   const int rl = rg * 32 + (lane & 31);
   const long long item0 = item_index(P, b, g, 0, r);
   const long long split_stride = item_index(P, b, g, 1, r) - item0;
-  if (rl < rgn.rows_here) {
+  const bool row_here = rl < rgn.rows_here;
+  // The first kBatch splits: their (m, l) for the row group's 32 rows are
+  // loaded once per workgroup and shared through LDS (every wave needs the
+  // same rows), their partials are all requested before any is used, so the
+  // merge waits on one round trip instead of one per split.  Slots past the
+  // split count re-read split 0 and are ignored.
+  constexpr int kBatch = 16;
+  __shared__ unsigned long long ml_s[kBatch][32];
+  unsigned long long ov[kBatch];
+  auto o_ptr = [&](long long it) {
+    return reinterpret_cast<const unsigned long long*>(
+        P.ws_o + (((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane);
+  };
+  auto ml_ptr = [&](long long it, int row) {
+    return reinterpret_cast<const unsigned long long*>(P.ws_ml + (size_t)it * P.rows_wg + row);
+  };
+  if (coherent) {
+    for (int q = tid; q < kBatch * 32; q += NW * 64) {
+      const int s = q >> 5;
+      const int row = rg * 32 + (q & 31);
+      if (s < rgn.Sb && row < rgn.rows_here)
+        ml_s[s][q & 31] = load_part(ml_ptr(item0 + s * split_stride, row));
+    }
+    if (row_here) {
+#pragma unroll
+      for (int s = 0; s < kBatch; ++s)
+        ov[s] = load_part(o_ptr(item0 + (s < rgn.Sb ? s : 0) * split_stride));
+    }
+  }
+  __syncthreads();
+  if (row_here) {
     MergeAcc ma;
     if (coherent) {
-      // Agent-scope loads skip the CU's L1 and read this XCD's L2.  The first
-      // kBatch splits are all requested before any is used (slots past the
-      // split count re-read split 0 and are ignored), so the merge waits on
-      // one L2 round trip instead of one per split.
-      auto load_ml = [&](long long it) {
-        return load_agent(
-            reinterpret_cast<const unsigned long long*>(P.ws_ml + (size_t)it * P.rows_wg + rl));
-      };
-      auto load_o = [&](long long it) {
-        return load_agent(reinterpret_cast<const unsigned long long*>(
-            P.ws_o + (((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane));
-      };
-      constexpr int kBatch = 16;
-      unsigned long long mlv[kBatch], ov[kBatch];
-#pragma unroll
-      for (int s = 0; s < kBatch; ++s) {
-        const long long it = item0 + (s < rgn.Sb ? s : 0) * split_stride;
-        mlv[s] = load_ml(it);
-        ov[s] = load_o(it);
-      }
 #pragma unroll
       for (int s = 0; s < kBatch; ++s)
         if (s < rgn.Sb)
-          ma.add(__builtin_bit_cast(float2, mlv[s]), __builtin_bit_cast(u32x2_t, ov[s]),
-                 P.scale_log2);
+          ma.add(__builtin_bit_cast(float2, ml_s[s][lane & 31]),
+                 __builtin_bit_cast(u32x2_t, ov[s]), P.scale_log2);
       for (int s = kBatch; s < rgn.Sb; ++s) {
         const long long it = item0 + s * split_stride;
-        ma.add(__builtin_bit_cast(float2, load_ml(it)), __builtin_bit_cast(u32x2_t, load_o(it)),
-               P.scale_log2);
+        ma.add(__builtin_bit_cast(float2, load_part(ml_ptr(it, rl))),
+               __builtin_bit_cast(u32x2_t, load_part(o_ptr(it))), P.scale_log2);
       }
     } else {
       ma.M = __builtin_nanf("");
@@ -539,6 +555,7 @@ template <int RG, int KG, int TPW, int NS, bool MR>
 __global__ __launch_bounds__(RG * KG * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(KParams P) {
   static_assert(NS >= 3 && NS <= 4, "ring depth");
+  constexpr int kDepth = NS - 1;   // stages requested ahead of the one in use
   constexpr int NW = RG * KG;
   constexpr int NT = NW * 64;
   constexpr int kTilesPerStage = KG * TPW;
@@ -589,6 +606,17 @@ void fwd_bf16_kernel(KParams P) {
     b = (int)(t / P.S);
   }
   }
+  // The item is the same for every lane, but the longest-first decode moves
+  // values through lane shuffles, after which the compiler can no longer
+  // prove it: without this, everything derived from it (offsets, tile
+  // ranges, the key loop's trip count and addresses) would be computed per
+  // lane, and the key loop would run as a divergent loop under exec masks.
+  b = __builtin_amdgcn_readfirstlane(b);
+  g = __builtin_amdgcn_readfirstlane(g);
+  s = __builtin_amdgcn_readfirstlane(s);
+  r = __builtin_amdgcn_readfirstlane(r);
+  item = ((long long)__builtin_amdgcn_readfirstlane((int)(item >> 32)) << 32) |
+         (unsigned)__builtin_amdgcn_readfirstlane((int)item);
 
   Seq sq;
   if (!decode_seq(P, b, sq)) {
@@ -749,11 +777,11 @@ void fwd_bf16_kernel(KParams P) {
   // to stage it and all have passed the barrier.  The barrier carries no
   // memory fence (a fence would wait for the stages still in flight); the
   // empty asm statements keep the compiler from moving LDS accesses across.
-  // Stages issued after stage it: min(NS - 2, n_iter - 1 - it).
-  static_assert((NS - 2) * kLoads <= 63, "vmcnt range");
+  // Stages issued after stage it: min(kDepth - 1, n_iter - 1 - it).
+  static_assert((kDepth - 1) * kLoads <= 63, "vmcnt range");
   auto wait_stage = [&](int it, int n_iter) {
-    const int later = min(NS - 2, n_iter - 1 - it);
-    if (NS > 3 && later >= 2)
+    const int later = min(kDepth - 1, n_iter - 1 - it);
+    if (kDepth > 2 && later >= 2)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * kLoads>());
     else if (later >= 1)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm<kLoads>());
@@ -914,7 +942,7 @@ void fwd_bf16_kernel(KParams P) {
   issue_aux();
   issue_q();
 #pragma unroll
-  for (int k = 0; k < NS - 1; ++k)
+  for (int k = 0; k < kDepth; ++k)
     if (k < n_iter) issue_stage(k);
   if constexpr (MR) {
     if (P.build) {
@@ -922,7 +950,7 @@ void fwd_bf16_kernel(KParams P) {
       // query and stage loads issued after them stay in flight), share them
       // through the barrier, and build the rows while the first stages load.
       constexpr int kQLoads = RG * 8 / NW;
-      const int staged = n_iter < NS - 1 ? n_iter : NS - 1;   // stages issued so far
+      const int staged = n_iter < kDepth ? n_iter : kDepth;   // stages issued so far
       if (staged >= 2)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm<kQLoads + 2 * kLoads>());
       else if (staged == 1)
@@ -989,7 +1017,7 @@ void fwd_bf16_kernel(KParams P) {
         asm volatile("" ::: "memory");
       }
     }
-    if (it + NS - 1 < n_iter) issue_stage(it + NS - 1);
+    if (it + kDepth < n_iter) issue_stage(it + kDepth);
     // Stage base as one uniform value, so each LDS read needs one add.
     const unsigned char* st = lds + __builtin_amdgcn_readfirstlane(slot * kStage);
     slot = (slot + 1 == NS) ? 0 : slot + 1;
