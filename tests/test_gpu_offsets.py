@@ -42,30 +42,30 @@ def test_offset_prefix_in_kernel_merge_shape(ta, entry):
     """One sequence of the 8B-shaped layer (in-kernel merge) whose prefix is
     rows 8 .. 4103 of a 4104-row buffer, with max_prefix = 4104."""
     rng = np.random.default_rng(81)
-    c = synthetic.make_case("guess1", prefix_lens=[4104],
+    c = synthetic.make_case("offs1", prefix_lens=[4104],
                             trees=[synthetic.random_tree(rng, 64, 1, 6, 4).tolist()],
                             Hq=32, Hkv=8, D=128, seed=81)
     out, lse, ro, rl = _run(ta, c, [8, 4104], 4104, entry)
-    check_attention(out, lse, ro, rl, fp32=False, what=f"wrong guess, in-kernel merge, {entry}")
+    check_attention(out, lse, ro, rl, fp32=False, what=f"prefix past row 0, in-kernel merge, {entry}")
 
 
 def test_offset_prefix_separate_merge(ta):
     """Four sequences in a 4 x 300-row buffer whose first range is rows
     10 .. 299 (290 rows), the others 300 rows each."""
     rng = np.random.default_rng(82)
-    c = synthetic.make_case("guess2", prefix_lens=[300] * 4,
+    c = synthetic.make_case("offs2", prefix_lens=[300] * 4,
                             trees=[synthetic.random_tree(rng, 40, 1, 6, 4).tolist()
                                    for _ in range(4)],
                             Hq=16, Hkv=2, D=128, seed=82)
     out, lse, ro, rl = _run(ta, c, [10, 300, 600, 900, 1200], 300, "forward")
-    check_attention(out, lse, ro, rl, fp32=False, what="wrong guess, sequence 0")
+    check_attention(out, lse, ro, rl, fp32=False, what="prefix past row 0, sequence 0")
 
 
 def test_uniform_batch_packed_offsets(ta):
     """The plain uniform batch: every node against the oracle."""
     rng = np.random.default_rng(83)
-    c = synthetic.make_case("guess3", prefix_lens=[700] * 3,
+    c = synthetic.make_case("offs3", prefix_lens=[700] * 3,
                             trees=[synthetic.random_tree(rng, 48, 1, 6, 4).tolist()
                                    for _ in range(3)], Hq=32, Hkv=8, D=128, seed=83)
     out, lse, ro, rl = _run(ta, c, [0, 700, 1400, 2100], 700, "mask_and_forward")
-    check_attention(out, lse, ro, rl, fp32=False, what="uniform batch, guess holds")
+    check_attention(out, lse, ro, rl, fp32=False, what="uniform batch")
