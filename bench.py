@@ -1,28 +1,28 @@
-"""Benchmark: one verification step of tree attention on one MI355X.
+"""Benchmark: the tree attention forward of one layer, and the verification
+step around it, on one MI355X.
 
-A step is one pass of the whole hot path over one batch of synthetic input:
-the ancestor mask, the attention and the greedy verifier.  By default the mask
-is built inside the forward kernel (tree_attn_mask_and_forward ->
-tree_verify_greedy); --separate-mask runs tree_attn_build_mask ->
-tree_attn_forward -> tree_verify_greedy instead.  The default
-workload is the Llama-3-8B-shaped layer (B=1, Hq=32, Hkv=8, D=128, prefix
-L=4096, a 64-node draft tree of depth <= 6 and branching <= 4, bf16), with
-greedy verification over a 64 x 128256 bf16 logits block (draft token equal to
-the target argmax with probability 0.6).
+The headline is the forward call's throughput in tree tokens per second: the
+tree_attn_mask_and_forward call (the ancestor mask built inside the forward
+kernel; --separate-mask: tree_attn_forward on a mask from its own
+tree_attn_build_mask call) timed with HIP events over exactly --steps calls.
+The default workload is the Llama-3-8B-shaped layer (B=1, Hq=32, Hkv=8, D=128,
+prefix L=4096, a 64-node draft tree of depth <= 6 and branching <= 4, bf16).
+The whole step (mask, forward and the greedy verifier over a 64 x 128256 bf16
+logits block, draft token equal to the target argmax with probability 0.6) is
+timed over the same number of steps and reported in `detail`, with every call's
+own device time, the cost of one candidate against 64 at the same prefix (a
+one-node tree, `detail.M3`), the roofline of the forward, and the fp64 CPU
+oracle timed on a bounded sample of the same workload (cpu_baseline).
 
 Inputs are resident in HBM before timing starts.  To keep the 256 MB Infinity
-Cache from serving repeated reads, the step rotates over --sets copies of every
-input (16 x ~35 MB by default), so each step reads cold data.  Each step is
-captured once per copy into a HIP graph and replayed (--eager launches every
-call from Python instead); the graphs are checked bit for bit against eager
-steps before timing.
+Cache from serving repeated reads, calls rotate over copies of every input (at
+least 512 MB in rotation); the number of copies divides --steps, so the timed
+region is a whole number of rotation rounds.  Each round is captured once into
+a HIP graph and replayed (--eager launches every call from Python instead); the
+graphs are checked bit for bit against eager calls before timing.
 
-Prints ONE JSON line: tree-tokens/s of the whole step (value), plus per-call
-device times from HIP events on the launch stream, the roofline of the
-dominant kernel, and the fp64 CPU oracle timed on a bounded sample of the same
-workload (cpu_baseline).
-
-    python bench.py [--steps K] [--warmup W] [--config llama3_8b] [--sets 16]
+    python bench.py [--steps K] [--warmup W] [--config llama3_8b]
+    python bench.py --hbm-ceiling      # copy, streaming-read and launch floors
 """
 from __future__ import annotations
 
@@ -48,7 +48,9 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="llama3_8b")
-    p.add_argument("--sets", type=int, default=32)
+    p.add_argument("--sets", type=int, default=16,
+                   help="fewest input copies in rotation (more when 512 MB needs more; the count "
+                        "is rounded up to a divisor of --steps)")
     p.add_argument("--separate-mask", action="store_true",
                    help="build the mask with its own call (tree_attn_build_mask) instead of "
                         "inside the forward (tree_attn_mask_and_forward)")
@@ -60,10 +62,14 @@ def parse():
                         "verifier), so that profiler averages per kernel name cover the step")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--hbm-ceiling", action="store_true",
-                   help="time plain device copies and a read-only reduction at several sizes "
-                        "(the practical HBM ceiling) and print one JSON line")
+                   help="time plain device copies and a streaming read at several sizes (the "
+                        "practical HBM ceilings) and empty kernels (the launch floor); print one "
+                        "JSON line")
     p.add_argument("--summarize-ceiling", metavar="FILE",
-                   help="write profiles/hbm_ceiling.md from the --hbm-ceiling output in FILE")
+                   help="write profiles/hbm_ceiling.md and profiles/launch_floor.md from the "
+                        "--hbm-ceiling output in FILE")
+    p.add_argument("--no-m3", action="store_true",
+                   help="skip the one-node-tree variant of the workload")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a plain 256 MiB device-to-device copy (counter calibration)")
     p.add_argument("--summarize-mfma", metavar="DIR",
@@ -88,14 +94,14 @@ def src_hash(*names):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_key, current_hash):
-    """HBM bytes per launch from committed rocprofv3 --pmc summaries, or None
-    when absent or taken on a different kernel source."""
+def load_traffic(config, kernel_key, current_hash):
+    """HBM bytes per call from committed rocprofv3 --pmc summaries of this
+    workload, or None when absent or taken on a different kernel source."""
     path = os.path.join(PROFILES, "pmc_traffic.json")
     try:
         with open(path) as f:
-            rec = json.load(f).get(kernel_key)
-    except (OSError, ValueError):
+            rec = json.load(f).get(config, {}).get(kernel_key)
+    except (OSError, ValueError, AttributeError):
         return None
     if not rec or rec.get("source_hash") != current_hash:
         return None
@@ -119,55 +125,164 @@ def calib_copy():
 
 
 HBM_CEILING_CMD = "python -u bench.py --hbm-ceiling > gpurun_out/hbm_ceiling.json"
+LAUNCH_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_ceiling -o run -- "
+                    "python -u bench.py --hbm-ceiling")
 CEILING_SIZES_MB = (16, 32, 64, 256, 1024)
+READ_GRIDS = (1024, 2048, 4096, 8192)
+EMPTY_GRIDS = (1, 256, 2048, 16384)
+
+
+def _probes():
+    """The measurement probes (libtaprobes.so, built next to the library)."""
+    import ctypes
+    path = os.path.join(ROOT, "tree_masked_attention_forward_amd", "libtaprobes.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: run tree_masked_attention_forward_amd/build.py")
+    lib = ctypes.CDLL(path)
+    lib.ta_probe_read.restype = ctypes.c_int
+    lib.ta_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p]
+    lib.ta_probe_empty.restype = ctypes.c_int
+    lib.ta_probe_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    return lib
 
 
 def hbm_ceiling():
-    """The practical HBM rate on this GPU: torch's device-to-device copy (bytes
-    read + written) over buffers of each size, rotated over enough copies to
-    exceed twice the 256 MB Infinity Cache so every pass reads cold data; HIP
-    events around 50 passes."""
+    """Practical ceilings on this GPU, each timed with HIP events:
+    * copy: torch's device-to-device copy (bytes read + written) per size;
+    * read: a plain streaming read (16-byte nontemporal loads, libtaprobes.so)
+      per size, best over a few grid sizes -- the rate a read-bound kernel can
+      reach at that size;
+    * launch: back-to-back empty kernels per grid size, launched eagerly and
+      replayed from a captured graph -- the floor under a one-launch call.
+    Buffers rotate over >= 1 GiB so every pass reads cold data (the Infinity
+    Cache is 256 MB)."""
     import torch
     dev = torch.device("cuda:0")
-    out = []
+    torch.cuda.set_device(dev)
+    probes = _probes()
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device=dev)
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    def read(buf, grid):
+        rc = probes.ta_probe_read(buf.data_ptr(), buf.numel(), sink.data_ptr(), grid, sh)
+        if rc:
+            raise SystemExit(f"ta_probe_read failed ({rc})")
+
+    copy, reads = [], []
     for mb in CEILING_SIZES_MB:
         n = mb << 20
         sets = max(2, -(-1024 // mb))   # >= 1 GiB in rotation
         src = [torch.empty(n, dtype=torch.uint8, device=dev).fill_(1) for _ in range(sets)]
         dst = [torch.empty_like(src[0]) for _ in range(sets)]
         torch.cuda.synchronize()
-        for i in range(2 * sets):   # warm-up: touch every page
+        for i in range(2 * sets):   # touch every page
             dst[i % sets].copy_(src[i % sets])
-        reps = 50
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(reps):
-            dst[i % sets].copy_(src[i % sets])
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        res = {"MB": mb, "us": round(us, 2), "GBps": round(2 * n / (us * 1e-6) / 1e9, 1)}
-        out.append(res)
-        print(f"[ceiling] {res}", file=sys.stderr, flush=True)
-        del src, dst
+        us = timed(lambda i: dst[i % sets].copy_(src[i % sets]), 50)
+        copy.append({"MB": mb, "us": round(us, 2), "GBps": round(2 * n / (us * 1e-6) / 1e9, 1)})
+        del dst
+        best = None
+        per_grid = {}
+        for grid in READ_GRIDS:
+            for i in range(sets):
+                read(src[i], grid)
+            us = timed(lambda i: read(src[i % sets], grid), 50)
+            per_grid[grid] = round(n / (us * 1e-6) / 1e9, 1)
+            if best is None or us < best[0]:
+                best = (us, grid)
+        reads.append({"MB": mb, "us": round(best[0], 2), "grid": best[1],
+                      "GBps": round(n / (best[0] * 1e-6) / 1e9, 1), "GBps_per_grid": per_grid})
+        print(f"[ceiling] {mb} MB copy {copy[-1]['GBps']} GB/s read {reads[-1]['GBps']} GB/s",
+              file=sys.stderr, flush=True)
+        del src
         torch.cuda.empty_cache()
-    print(json.dumps({"hbm_ceiling": out, "peak_GBps": HBM_PEAK_GBS}))
+
+    launch = []
+    reps = 200
+    for grid in EMPTY_GRIDS:
+        def empty(i, grid=grid):
+            # the current stream: torch's capture stream while a graph is captured
+            rc = probes.ta_probe_empty(grid, 256, torch.cuda.current_stream(dev).cuda_stream)
+            if rc:
+                raise SystemExit(f"ta_probe_empty failed ({rc})")
+        for i in range(20):
+            empty(i)
+        eager = timed(empty, reps)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                empty(i)
+        g.replay()
+        torch.cuda.synchronize()
+        graph = timed(lambda i: g.replay(), 5) / reps
+        launch.append({"grid": grid, "block": 256, "eager_us": round(eager, 3),
+                       "graph_us": round(graph, 3)})
+        print(f"[launch] grid {grid}: eager {eager:.2f} us, graph {graph:.2f} us per launch",
+              file=sys.stderr, flush=True)
+    print(json.dumps({"hbm_copy": copy, "hbm_read": reads, "launch_floor": launch,
+                      "peak_GBps": HBM_PEAK_GBS}))
 
 
-def summarize_ceiling(path):
+def summarize_ceiling(path, trace_root=None):
     with open(path) as f:
         rec = json.loads(f.read().strip().splitlines()[-1])
-    lines = ["# Practical HBM ceiling on the MI355X box", "",
+    lines = ["# Practical HBM ceilings on the MI355X box", "",
              "Command (repository root, MI355X box):", "", "    " + HBM_CEILING_CMD, "",
-             "torch device-to-device copy of a buffer of each size (GB/s counts the bytes read "
-             "plus the bytes written), 50 passes timed with HIP events, buffers rotated over "
-             ">= 1 GiB so every pass reads cold data (the Infinity Cache is 256 MB). The "
-             "published peak is 8 TB/s. For scale: one 8B-shaped forward call moves 18.1 "
-             "algorithmic MB (35.9 MB counted by FETCH_SIZE + WRITE_SIZE).", "",
-             "| buffer | us per copy | GB/s (read + write) |", "|---|---|---|"]
-    for r in rec["hbm_ceiling"]:
-        lines.append(f"| {r['MB']} MB | {r['us']} | {r['GBps']} |")
+             "Buffers rotate over >= 1 GiB so every pass reads cold data (the Infinity Cache is "
+             "256 MB); HIP events around 50 passes. The published peak is 8 TB/s.", "",
+             "* **read**: a plain streaming read (`ta_probe_read` in `csrc/probes.hip`: 16-byte "
+             "nontemporal loads, eight in flight per thread, folded so they stay live), best over "
+             f"grids of {', '.join(map(str, READ_GRIDS))} workgroups of 256 threads. This is the "
+             "rate a read-bound kernel can reach at that size: the ceiling for the forward, "
+             "whose traffic is K/V reads.",
+             "* **copy**: torch's device-to-device copy; GB/s counts bytes read plus bytes "
+             "written.", "",
+             "| buffer | read us | read GB/s | best grid | copy us | copy GB/s (read + write) |",
+             "|---|---|---|---|---|---|"]
+    for r, c in zip(rec["hbm_read"], rec["hbm_copy"]):
+        lines.append(f"| {r['MB']} MB | {r['us']} | {r['GBps']} | {r['grid']} | {c['us']} | "
+                     f"{c['GBps']} |")
+    lines += ["", "Read GB/s per grid size:", "",
+              "| buffer | " + " | ".join(f"{g} WG" for g in READ_GRIDS) + " |",
+              "|---|" + "---|" * len(READ_GRIDS)]
+    for r in rec["hbm_read"]:
+        lines.append(f"| {r['MB']} MB | " + " | ".join(
+            str(r["GBps_per_grid"].get(str(g), r["GBps_per_grid"].get(g, ""))) for g in READ_GRIDS)
+            + " |")
     with open(os.path.join(PROFILES, "hbm_ceiling.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    lines = ["# Launch floor on the MI355X box", "",
+             "Command (repository root, MI355X box):", "", "    " + HBM_CEILING_CMD, "",
+             "An empty kernel (`ta_probe_empty` in `csrc/probes.hip`) of the given grid of "
+             "256-thread workgroups, 200 launches back to back on one stream, timed with HIP "
+             "events: eagerly from Python, and replayed from one captured HIP graph holding all "
+             "200. Microseconds per launch, launch to launch: the least any call of one launch "
+             "costs in a stream of calls.", "",
+             "| grid | eager us per launch | graph us per launch |", "|---|---|---|"]
+    for r in rec["launch_floor"]:
+        lines.append(f"| {r['grid']} | {r['eager_us']} | {r['graph_us']} |")
+    if trace_root:
+        stats = _read_csvs(trace_root, "kernel_stats.csv")
+        rows = [r for r in stats if "empty_kernel" in r["Name"] or "read_kernel" in r["Name"]]
+        if rows:
+            lines += ["", "Kernel trace of the same run (every grid size together):", "",
+                      "    " + LAUNCH_TRACE_CMD, "",
+                      "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+            for r in rows:
+                short = r["Name"].replace("(anonymous namespace)::", "").split("(")[0]
+                lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                             f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} |")
+    with open(os.path.join(PROFILES, "launch_floor.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
@@ -192,6 +307,10 @@ def _pmc_means(root, counter):
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
+def _short(name):
+    return name.replace("ta::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+
 def summarize_profiles(root):
     """Turn rocprofv3 CSV output (runs made by the commands in PROFILE_CMDS,
     written under root/<name>) into profiles/*.md and profiles/pmc_traffic.json."""
@@ -211,18 +330,16 @@ def summarize_profiles(root):
             other_calls += int(r["Calls"])
             other_ns += float(r["TotalDurationNs"])
             continue
-        short = name.replace("ta::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
-        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.3f} | "
+        lines.append(f"| `{_short(name)}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.3f} | "
                      f"{float(r['MinNs'])/1e3:.3f} | {float(r['MaxNs'])/1e3:.3f} | "
                      f"{float(r['Percentage']):.1f} |")
     if other_calls:
         lines += ["", f"Other kernels (input setup and the graph-vs-eager checks, outside the timed "
                       f"region): {other_calls} calls, {other_ns / 1e3:.1f} us in total."]
-    with open(os.path.join(PROFILES, "tree_attn_step_llama3_8b_kernel_trace.md"), "w") as f:
-        f.write("\n".join(lines) + "\n")
+    if stats:
+        with open(os.path.join(PROFILES, "tree_attn_step_llama3_8b_kernel_trace.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
     # HBM traffic from FETCH_SIZE / WRITE_SIZE, scaled by the copy calibration
-    fetch = _pmc_means(os.path.join(root, "prof_fetch"), "FETCH_SIZE")
-    write = _pmc_means(os.path.join(root, "prof_write"), "WRITE_SIZE")
     cf = _pmc_means(os.path.join(root, "prof_calib_fetch"), "FETCH_SIZE")
     cw = _pmc_means(os.path.join(root, "prof_calib_write"), "WRITE_SIZE")
     copy_f = max((v for k, v in cf.items() if "copy" in k.lower() or "elementwise" in k.lower()),
@@ -232,35 +349,61 @@ def summarize_profiles(root):
     sf = (CALIB_BYTES / 1024) / copy_f if copy_f else 1.0
     sw = (CALIB_BYTES / 1024) / copy_w if copy_w else 1.0
     # The profiled runs take the default step, whose forward call is
-    # tree_attn_mask_and_forward (the mask is built inside the forward kernel).
-    groups = {"tree_attn_mask_and_forward": ("fwd_bf16_kernel", "merge_bf16_kernel"),
-              "tree_verify_greedy": ("argmax_partial_kernel", "path_select_kernel"),
-              "tree_attn_build_mask": ("build_mask_kernel",)}
+    # tree_attn_mask_and_forward (the mask is built inside the forward kernel,
+    # or by build_mask_kernel within the call for trees above 128 nodes).
+    groups = {"tree_attn_mask_and_forward": ("fwd_bf16_kernel", "merge_bf16_kernel",
+                                             "build_mask_kernel"),
+              "tree_verify_greedy": ("argmax_partial_kernel", "path_select")}
     hashes = {"tree_attn_mask_and_forward": src_hash("attn_fwd.hip"),
-              "tree_verify_greedy": src_hash("verify.hip"),
-              "tree_attn_build_mask": src_hash("mask_build.hip")}
+              "tree_verify_greedy": src_hash("verify.hip")}
     rec = {"calibration": {"copy_bytes": CALIB_BYTES, "fetch_kib": copy_f, "write_kib": copy_w,
                            "fetch_scale": sf, "write_scale": sw}}
-    md = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
-          "Workload: one verification step of the Llama-3-8B-shaped layer (N=64, L=4096, bf16).",
-          "Counters are KiB per dispatch; each is scaled by what the same counter reads for a",
-          f"plain {CALIB_BYTES >> 20} MiB device copy (fetch x{sf:.3f}, write x{sw:.3f}).", "",
-          "Commands (repository root, MI355X box):", ""]
-    md += ["    " + PROFILE_CMDS[k] for k in ("prof_fetch", "prof_write", "prof_calib_fetch",
-                                             "prof_calib_write")]
-    md += ["", "| call | kernel | fetch KiB | write KiB | HBM bytes (scaled) |", "|---|---|---|---|---|"]
-    for call, kernels in groups.items():
-        total = 0.0
-        for kn in kernels:
-            fk = next((v for k, v in fetch.items() if kn in k), None)
-            wk = next((v for k, v in write.items() if kn in k), None)
-            if fk is None or wk is None:
+    md = ["# HBM traffic per call (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+          "Counters are KiB per dispatch, averaged over the run's dispatches of each kernel;",
+          "each is scaled by what the same counter reads for a plain",
+          f"{CALIB_BYTES >> 20} MiB device copy (fetch x{sf:.3f}, write x{sw:.3f}). `alg` is",
+          "the call's algorithmic bytes (K/V, Q, mask words, outputs) from the workload's bench",
+          "line; `ratio` = counted / algorithmic.", "",
+          "Commands (repository root, MI355X box), per workload name:", "",
+          "    " + PROFILE_CMDS["prof_fetch"], "    " + PROFILE_CMDS["prof_write"],
+          "    " + PROFILE_CMDS["prof_calib_fetch"], "    " + PROFILE_CMDS["prof_calib_write"], "",
+          "| workload | call | kernel | fetch KiB | write KiB | HBM bytes (scaled) | alg | ratio |",
+          "|---|---|---|---|---|---|---|---|"]
+    for name in CONFIG_NAMES:
+        fetch = _pmc_means(os.path.join(root, f"prof_fetch_{name}"), "FETCH_SIZE")
+        write = _pmc_means(os.path.join(root, f"prof_write_{name}"), "WRITE_SIZE")
+        if not fetch or not write:
+            continue
+        alg = {}
+        try:
+            with open(os.path.join(root, f"cfg_{name}.json")) as f:
+                d = json.loads(f.read().strip().splitlines()[-1])["detail"]
+            alg = {"tree_attn_mask_and_forward": d["forward"]["alg_bytes"],
+                   "tree_verify_greedy": d["verify"]["alg_bytes"]}
+        except (OSError, ValueError, IndexError, KeyError):
+            pass
+        rec[name] = {}
+        for call, kernels in groups.items():
+            total, parts = 0.0, []
+            for kn in kernels:
+                fk = next((v for k, v in fetch.items() if kn in k), None)
+                wk = next((v for k, v in write.items() if kn in k), None)
+                if fk is None or wk is None:
+                    continue
+                b = fk * 1024 * sf + wk * 1024 * sw
+                total += b
+                parts.append((kn, fk, wk, b))
+            if not parts:
                 continue
-            b = fk * 1024 * sf + wk * 1024 * sw
-            total += b
-            md.append(f"| {call} | `{kn}` | {fk:.1f} | {wk:.1f} | {b / 1e6:.3f} MB |")
-        rec[call] = {"source_hash": hashes[call], "hbm_bytes_per_launch": round(total)}
-    with open(os.path.join(PROFILES, "tree_attn_step_llama3_8b_hbm_traffic.md"), "w") as f:
+            a = alg.get(call)
+            for kn, fk, wk, b in parts:
+                md.append(f"| {name} | {call} | `{kn}` | {fk:.1f} | {wk:.1f} | {b / 1e6:.3f} MB | | |")
+            md.append(f"| {name} | {call} | **all** | | | **{total / 1e6:.3f} MB** | "
+                      f"{'' if a is None else f'{a / 1e6:.3f} MB'} | "
+                      f"{'' if a is None else f'{total / a:.2f}'} |")
+            rec[name][call] = {"source_hash": hashes[call], "hbm_bytes_per_launch": round(total),
+                               "alg_bytes": a}
+    with open(os.path.join(PROFILES, "tree_attn_hbm_traffic.md"), "w") as f:
         f.write("\n".join(md) + "\n")
     with open(os.path.join(PROFILES, "pmc_traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
@@ -269,11 +412,14 @@ def summarize_profiles(root):
 
 PROFILE_CMDS = {
     "prof_trace": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o run -- "
-                  "python -u bench.py --steps 50 --warmup 5 --no-cpu-baseline --no-extra-calls",
-    "prof_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch -o run -- "
-                  "python -u bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-extra-calls",
-    "prof_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_write -o run -- "
-                  "python -u bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-extra-calls",
+                  "python -u bench.py --steps 50 --warmup 5 --no-cpu-baseline --no-extra-calls "
+                  "--no-m3",
+    "prof_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch_{name} -o run -- "
+                  "python -u bench.py --config {name} --steps 10 --warmup 2 --no-cpu-baseline "
+                  "--no-extra-calls --no-m3",
+    "prof_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_write_{name} -o run -- "
+                  "python -u bench.py --config {name} --steps 10 --warmup 2 --no-cpu-baseline "
+                  "--no-extra-calls --no-m3",
     "prof_calib_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_calib_fetch -o run -- "
                         "python -u bench.py --calib-copy",
     "prof_calib_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_calib_write -o run -- "
@@ -282,20 +428,58 @@ PROFILE_CMDS = {
 
 
 # Per-workload runs: the bench line (per-call HIP-event times) and a kernel trace.
-CONFIG_NAMES = ("llama3_8b", "batched", "llama3_70b", "forest")
+CONFIG_NAMES = ("llama3_8b", "llama3_8b_n1", "batched", "llama3_70b", "forest", "tree_4096")
 CONFIG_CMDS = {
     "bench": "python -u bench.py --config {name} --steps 30 --warmup 5 --no-cpu-baseline "
              "> gpurun_out/cfg_{name}.json",
     "trace": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/cfg_trace_{name} -o run -- "
              "python -u bench.py --config {name} --steps 10 --warmup 2 --no-cpu-baseline "
-             "--no-extra-calls",
+             "--no-extra-calls --no-m3",
 }
 
 
+def summarize_m3(root):
+    """profiles/tree_attn_forward_m3.md: the 8B layer's forward with 64 nodes
+    against one node, from the two workloads' bench lines and kernel traces."""
+    rows = []
+    for name in ("llama3_8b", "llama3_8b_n1"):
+        try:
+            with open(os.path.join(root, f"cfg_{name}.json")) as f:
+                line = json.loads(f.read().strip().splitlines()[-1])
+        except (OSError, ValueError, IndexError):
+            return
+        stats = _read_csvs(os.path.join(root, f"cfg_trace_{name}"), "kernel_stats.csv")
+        ks = [(_short(x["Name"]), float(x["AverageNs"]) / 1e3) for x in stats
+              if "fwd_bf16_kernel" in x["Name"] or "merge_bf16_kernel" in x["Name"]
+              or "build_mask_kernel" in x["Name"]]
+        rows.append((name, line, ks))
+    (_, l64, k64), (_, l1, k1) = rows
+    m3 = l64["detail"].get("M3") or {}
+    t64, t1 = l64["ms_per_step"] * 1e3, l1["ms_per_step"] * 1e3
+    md = ["# One candidate against 64 at the same prefix (Llama-3-8B layer, L=4096)", "",
+          "Commands (repository root, MI355X box), for llama3_8b and llama3_8b_n1:", "",
+          "    " + CONFIG_CMDS["bench"], "    " + CONFIG_CMDS["trace"], "",
+          "The forward call (tree_attn_mask_and_forward) of the 8B-shaped layer with its 64-node",
+          "draft tree, and with a one-node tree over the same prefix length, each timed over 30",
+          "calls on cold rotated inputs (HIP events; graph replays). The pages hold that checking",
+          "many candidates costs about what checking one does, both reading the same prefix K/V.",
+          "", "| tree | us per call (events) | kernels (trace avg us) |", "|---|---|---|",
+          f"| 64 nodes | {t64:.3f} | " + ", ".join(f"`{k}` {v:.3f}" for k, v in k64) + " |",
+          f"| 1 node | {t1:.3f} | " + ", ".join(f"`{k}` {v:.3f}" for k, v in k1) + " |", "",
+          f"Ratio 64 / 1 across the two runs: **{t64 / t1:.3f}**."]
+    if m3:
+        md.append(f"Ratio measured inside the 64-node run (`detail.M3`, same process): "
+                  f"{m3['t_N_us']:.3f} / {m3['t_N1_us']:.3f} us = **{m3['ratio']:.3f}**.")
+    with open(os.path.join(PROFILES, "tree_attn_forward_m3.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
 def summarize_configs(root):
-    """One table over the workloads: the forward call's device time (HIP events, p50
-    over graph replays, and the kernel-trace average of its kernels), its algorithmic
-    rate against the roof that bounds it, and the verifier's time."""
+    """One table over the workloads: the forward call's device time (HIP events over
+    the timed calls, p50 over per-round graph replays, and the kernel-trace average of
+    its kernels), its algorithmic rate against the roof that bounds it, and the
+    verifier's time; then the one-node comparison (summarize_m3)."""
     rows = []
     for name in CONFIG_NAMES:
         try:
@@ -304,35 +488,39 @@ def summarize_configs(root):
         except (OSError, ValueError, IndexError):
             continue
         d = line["detail"]
-        fwd_call = line["roofline"]["kernel"] if line["roofline"]["kernel"] != "tree_verify_greedy" \
-            else line["detail"]["roofline_other"]["kernel"]
+        r = line["roofline"]
+        fwd_call = r["kernel"]
         fw = d["forward"]
-        r = line["roofline"] if line["roofline"]["kernel"] == fwd_call else d["roofline_other"]
         stats = _read_csvs(os.path.join(root, f"cfg_trace_{name}"), "kernel_stats.csv")
         fwd_ns = sum(float(x["AverageNs"]) for x in stats
-                     if "fwd_bf16_kernel" in x["Name"] or "merge_bf16_kernel" in x["Name"])
+                     if "fwd_bf16_kernel" in x["Name"] or "merge_bf16_kernel" in x["Name"]
+                     or "build_mask_kernel" in x["Name"])
         rows.append(f"| {name} | {line['config']['workload'].split(';')[0]} | "
+                    f"{line['ms_per_step'] * 1e3:.1f} | "
                     f"{d['us_per_call_spread'][fwd_call]['p50']:.1f} | {fwd_ns / 1e3:.1f} | "
                     f"{r['achieved']} {r['unit']} | {r['bound']} | {r['frac']:.3f} | "
                     f"{fw['t_roof_us']:.1f} | {d['us_per_call']['tree_verify_greedy']:.1f} |")
     md = ["# Forward call on every workload (MI355X, one GPU)", "",
           "Commands (repository root, MI355X box), for each workload name:", "",
           "    " + CONFIG_CMDS["bench"], "    " + CONFIG_CMDS["trace"], "",
-          "Times in microseconds per call. `events p50`: median over graph replays of the call on",
-          "resident inputs (HIP events on the launch stream); `trace`: kernel-trace average of",
-          "the forward's kernels (split kernel + merge kernel where there is one). The rate and",
-          "fraction are the algorithmic bytes or flops per call over the events mean, against",
-          "8 TB/s HBM or 2.5 PFLOP/s dense bf16 MFMA, whichever bounds the workload.", "",
-          "| workload | shape | events p50 | trace | achieved | bound | roofline frac | roof | verify |",
-          "|---|---|---|---|---|---|---|---|---|"] + rows
+          "Times in microseconds per call. `events`: the bench line's headline timing (HIP",
+          "events around the 30 timed calls on cold rotated inputs, graph replays); `p50`: median",
+          "per-call time over replays of one graph round; `trace`: kernel-trace average of the",
+          "forward's kernels (split kernel + merge kernel where there is one, mask kernel above",
+          "128 nodes). The rate and fraction are the algorithmic bytes or flops per call over",
+          "the events time, against 8 TB/s HBM or 2.5 PFLOP/s dense bf16 MFMA, whichever bounds",
+          "the workload; `roof` is that bound's time.", "",
+          "| workload | shape | events | p50 | trace | achieved | bound | roofline frac | roof | verify |",
+          "|---|---|---|---|---|---|---|---|---|---|"] + rows
     with open(os.path.join(PROFILES, "tree_attn_forward_configs.md"), "w") as f:
         f.write("\n".join(md) + "\n")
     print("\n".join(md))
+    summarize_m3(root)
 
 
 MFMA_CMD = ("rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 -f csv -d gpurun_out/mfma_{name} "
             "-o run -- python -u bench.py --config {name} --steps 10 --warmup 2 --no-cpu-baseline "
-            "--no-extra-calls")
+            "--no-extra-calls --no-m3")
 
 
 def summarize_mfma(root):
@@ -377,6 +565,20 @@ def summarize_mfma(root):
     print("\n".join(lines))
 
 
+def rotation_sets(steps, need, set_bytes):
+    """Copies of the inputs to rotate over: the smallest divisor of `steps` that
+    is at least `need` (all of them when steps < need), so that `steps` calls
+    are a whole number of rounds over the copies."""
+    if steps <= need:
+        return max(1, steps)
+    d = next(d for d in range(need, steps + 1) if steps % d == 0)
+    if d * set_bytes > 32 * 2**30:
+        raise SystemExit(f"--steps {steps} needs {d} input copies to be whole rotation rounds "
+                         f"({d * set_bytes / 2**30:.1f} GiB); pick a --steps with a divisor "
+                         f"near {need}")
+    return d
+
+
 def main():
     args = parse()
     if args.summarize_profiles:
@@ -395,7 +597,8 @@ def main():
         hbm_ceiling()
         return
     if args.summarize_ceiling:
-        summarize_ceiling(args.summarize_ceiling)
+        summarize_ceiling(args.summarize_ceiling, os.path.join(
+            os.path.dirname(os.path.abspath(args.summarize_ceiling)), "prof_ceiling"))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -427,9 +630,10 @@ def main():
         "kp": case.k_prefix.to(dev), "vp": case.v_prefix.to(dev),
         "logits": case.logits.to(dev), "draft": torch.from_numpy(case.draft).to(dev),
     }
-    # Enough distinct copies to cycle through 2x the 256 MB Infinity Cache.
+    # Enough distinct copies to cycle through 2x the 256 MB Infinity Cache, their
+    # count a divisor of --steps so that the timed region is whole rounds.
     set_bytes = sum(v.numel() * v.element_size() for v in base.values())
-    n_sets = max(1, min(args.sets, -(-2 * 256 * 2**20 // set_bytes)))
+    n_sets = rotation_sets(args.steps, max(args.sets, -(-2 * 256 * 2**20 // set_bytes)), set_bytes)
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_sets - 1)]
     mask = torch.empty((sum_n, W), dtype=torch.uint64, device=dev)
     depth = torch.empty(sum_n, dtype=torch.int32, device=dev)
@@ -503,51 +707,78 @@ def main():
     n_rot = len(sets)
     if use_graphs:
         # A graph launch itself costs host time comparable to a step, so one graph holds
-        # the steps of all rotation sets in order; single-step graphs cover the rest.
-        step_graphs = [capture(one_step, [i]) for i in range(n_rot)]
+        # the steps of all rotation sets in order.
         round_graph = capture(one_step, range(n_rot))
-        # Every graph must reproduce the eager step bit for bit, replayed twice with eager
+        # The graph must reproduce the eager step bit for bit, replayed twice with eager
         # work on other inputs in between.
-        for k, g in ((0, step_graphs[0]), (n_rot - 1, step_graphs[n_rot - 1]),
-                     (n_rot - 1, round_graph)):
-            step(k)
+        step(n_rot - 1)
+        torch.cuda.synchronize()
+        ref = outputs()
+        for rep in range(2):
+            step(n_rot)
             torch.cuda.synchronize()
-            ref = outputs()
-            for rep in range(2):
-                step(k + 1)
-                torch.cuda.synchronize()
-                g.replay()
-                torch.cuda.synchronize()
-                for a, b in zip(outputs(), ref):
-                    if not torch.equal(a, b):
-                        raise SystemExit(f"graph replay {rep} (last set {k}) differs from the "
-                                         "eager step")
+            round_graph.replay()
+            torch.cuda.synchronize()
+            for a, b in zip(outputs(), ref):
+                if not torch.equal(a, b):
+                    raise SystemExit(f"graph replay {rep} differs from the eager step")
 
-        def run_steps(k):
-            for _ in range(k // n_rot):
-                round_graph.replay()
-            for i in range(k % n_rot):
-                step_graphs[i].replay()
+    stream = torch.cuda.current_stream(dev)
+
+    def timed_steps(fn_round):
+        """Device time (HIP events on the launch stream) and host time of exactly
+        args.steps calls: args.steps / n_rot rounds over the input copies."""
+        rounds = args.steps // n_rot
+        fn_round()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(rounds):
+            fn_round()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        host = time.perf_counter() - t0
+        return e0.elapsed_time(e1) * 1e-3, host
+
+    # --- headline: exactly --steps forward calls ------------------------------------------
+    if use_graphs:
+        fwd_round_graph = capture(fwd_fn, range(n_rot))
+        fwd_round = fwd_round_graph.replay
+        # The forward graph must give the eager call's bits as well.
+        fwd_fn(sets[n_rot - 1])
+        torch.cuda.synchronize()
+        ref = outputs()
+        fwd_fn(sets[0])
+        fwd_round()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(outputs()[:4], ref[:4])):
+            raise SystemExit("the forward graph's replay differs from the eager call")
     else:
-        def run_steps(k):
-            for i in range(k):
-                step(i)
-
-    # --- whole-step timing ----------------------------------------------------------------
-    run_steps(n_rot)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run_steps(args.steps)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = sum_n * args.steps / elapsed
-    print(f"[bench] {args.steps} steps in {elapsed:.4f} s ({'graphs' if use_graphs else 'eager'})",
+        def fwd_round():
+            for i in range(n_rot):
+                fwd_fn(sets[i])
+    fwd_dev, fwd_host = timed_steps(fwd_round)
+    t_fwd = fwd_dev * 1e6 / args.steps
+    value = sum_n * args.steps / fwd_dev
+    print(f"[bench] {args.steps} forward calls: {fwd_dev * 1e3:.4f} ms device, "
+          f"{fwd_host * 1e3:.4f} ms host ({'graphs' if use_graphs else 'eager'})",
           file=sys.stderr, flush=True)
+
+    # --- the whole step over as many steps --------------------------------------------------
+    if use_graphs:
+        step_round = round_graph.replay
+    else:
+        def step_round():
+            for i in range(n_rot):
+                one_step(sets[i])
+    step_dev, step_host = timed_steps(step_round)
+    ms_step = step_dev * 1e3 / args.steps
+    print(f"[bench] {args.steps} whole steps: {step_dev * 1e3:.4f} ms device, "
+          f"{step_host * 1e3:.4f} ms host", file=sys.stderr, flush=True)
 
     # --- per-call device time with HIP events on the launch stream ------------------------
     # One graph holds one call per rotation set; events bracket whole replays.
-    stream = torch.cuda.current_stream(dev)
 
     def event_time(fn, n):
         """Mean device time per call (us) over about n calls, and the p10 / p50 /
@@ -611,7 +842,7 @@ def main():
 
     do_mask(sets[0])
     t_mask, d_mask = event_time(do_mask, args.steps)
-    t_fwd, d_fwd = event_time(fwd_fn, args.steps)
+    t_fwd_ev, d_fwd = event_time(fwd_fn, args.steps)
     t_ver, d_ver = event_time(do_verify, args.steps)
     t_commit = t_vnext = d_commit = d_vnext = None
     if not args.no_extra_calls:
@@ -619,8 +850,13 @@ def main():
         t_vnext, d_vnext = event_time(do_verify_next, args.steps)
     if t_commit is not None and not bool((commit_status == 0).all()):
         raise SystemExit("tree_kv_commit reported a failure in the timing loop")
-    print(f"[bench] per call us: mask {t_mask:.2f} forward {t_fwd:.2f} verify {t_ver:.2f}",
-          file=sys.stderr, flush=True)
+    print(f"[bench] per call us: mask {t_mask:.2f} forward {t_fwd:.2f} ({t_fwd_ev:.2f} in the "
+          f"per-call graphs) verify {t_ver:.2f}", file=sys.stderr, flush=True)
+
+    # --- one candidate against N at the same prefix (the N=1 variant) ---------------------
+    m3 = None
+    if not args.no_m3 and max_nodes > 1:
+        m3 = one_node_ratio(case, ta, dev, args.steps, t_fwd, args.separate_mask)
 
     # --- algorithmic bytes / flops --------------------------------------------------------
     depth_h = depth.cpu().numpy().astype(np.int64)
@@ -649,16 +885,15 @@ def main():
             else:
                 r = {"bound": "mfma", "achieved": round(fwd_tfs, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
-            r["traffic"] = load_traffic(fwd_call, fwd_hash)
+            r["traffic"] = load_traffic(args.config, fwd_call, fwd_hash)
             r["kernel"] = fwd_call
             return r
         r = {"bound": "hbm", "achieved": round(ver_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
              "frac": round(ver_gbs / HBM_PEAK_GBS, 4),
-             "traffic": load_traffic("tree_verify_greedy", ver_hash), "kernel": "tree_verify_greedy"}
+             "traffic": load_traffic(args.config, "tree_verify_greedy", ver_hash),
+             "kernel": "tree_verify_greedy"}
         return r
 
-    dominant = "forward" if t_fwd >= t_ver else "verify"
-    other = "verify" if dominant == "forward" else "forward"
 
     # --- CPU baseline: the fp64 oracle on a bounded sample ----------------------------------
     cpu = None
@@ -672,7 +907,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(t_fwd * 1e-3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -681,16 +916,23 @@ def main():
         "config": {
             "workload": f"{args.config}: B={B} Hq={Hq} Hkv={Hkv} D={D} L={max_prefix} N={max_nodes} "
                         f"(sum_L={sum_l}, sum_N={sum_n}); greedy verify over V={V} bf16 logits",
-            "step": " + ".join(n for n, _ in calls) + ", inputs rotated over "
-                    f"{len(sets)} resident copies of {set_bytes / 2**20:.1f} MiB, "
-                    + ("replayed from captured HIP graphs (one per round over the copies)"
-                       if use_graphs else "launched eagerly from Python"),
+            "timed": f"{args.steps} {fwd_call} calls ({args.steps // n_rot} rounds over "
+                     f"{n_rot} resident input copies of {set_bytes / 2**20:.1f} MiB), "
+                     + ("replayed from a captured HIP graph per round" if use_graphs
+                        else "launched eagerly from Python")
+                     + "; HIP events on the launch stream",
             "global_batch": B, "seq_len": max_prefix, "tree_nodes": sum_n,
         },
-        "roofline": roof(dominant),
+        "roofline": roof("forward"),
         "cpu_baseline": cpu,
         "detail": {
-            "us_per_call": {fwd_call: round(t_fwd, 3), "tree_verify_greedy": round(t_ver, 3),
+            "step": {"calls": " + ".join(n for n, _ in calls), "steps": args.steps,
+                     "ms_per_step": round(ms_step, 6),
+                     "tree_tokens_per_s": round(sum_n * args.steps / step_dev, 1),
+                     "host_ms_per_step": round(step_host * 1e3 / args.steps, 6)},
+            "forward_host_ms_per_call": round(fwd_host * 1e3 / args.steps, 6),
+            "M3": m3,
+            "us_per_call": {fwd_call: round(t_fwd_ev, 3), "tree_verify_greedy": round(t_ver, 3),
                             "tree_attn_build_mask (standalone)": round(t_mask, 3),
                             "tree_kv_commit (standalone)": t_commit and round(t_commit, 3),
                             "tree_verify_greedy_next (standalone)": t_vnext and round(t_vnext, 3)},
@@ -700,18 +942,84 @@ def main():
                                    "tree_verify_greedy_next (standalone)": d_vnext},
             "commit": {"accepted_rows": int(acc_len.sum()),
                        "alg_bytes": int(acc_len.sum()) * Hkv * D * base["kt"].element_size() * 4},
-            "forward": {"tree_tokens_per_s": round(sum_n / (t_fwd * 1e-6), 1),
+            "forward": {"tree_tokens_per_s": round(value, 1),
                         "kv_GBps": round(kv_bytes / (t_fwd * 1e-6) / 1e9, 1),
                         "alg_GBps": round(fwd_gbs, 1), "alg_TFLOPs": round(fwd_tfs, 2),
                         "alg_bytes": fwd_bytes, "alg_flops": fwd_flops,
                         "t_roof_us": round(t_roof_fwd * 1e6, 3),
                         "roofline_frac": round(t_roof_fwd / (t_fwd * 1e-6), 4)},
-            "verify": {"alg_bytes": ver_bytes, "alg_GBps": round(ver_gbs, 1)},
-            "roofline_other": roof(other),
+            "verify": {"alg_bytes": ver_bytes, "alg_GBps": round(ver_gbs, 1),
+                       "roofline": roof("verify")},
             "source_hash": {"attn_fwd.hip": fwd_hash, "verify.hip": ver_hash},
         },
     }
     print(json.dumps(line), flush=True)
+
+
+def one_node_ratio(case, ta, dev, steps, t_fwd_us, separate_mask):
+    """The forward of the same workload with every sequence's tree cut to its
+    first root (same prefix lengths, fresh inputs): device time per call over
+    exactly `steps` calls, rotated over cold copies and replayed from a graph,
+    and the ratio of the N-node call to it ("Speculative Tree Attention: How
+    Multi-Candidate Draft Models and Parallel Verification Deliver 4x LLM
+    Speedups", news.premlal.in, The Speculative Paradigm: checking many
+    candidates at once costs about what checking one does, both being bound by
+    reading the prefix's K/V)."""
+    import numpy as np
+    import torch
+
+    import synthetic
+    lens = [int(x) for x in np.diff(case.prefix_offsets)]
+    c1 = synthetic.make_case(case.name + "_n1", prefix_lens=lens, trees=[[-1]] * case.B,
+                             Hq=case.Hq, Hkv=case.Hkv, D=case.D, dtype=case.dtype,
+                             seed=case.seed + 1000)
+    base = {"parents": torch.from_numpy(c1.parents).to(dev),
+            "noffs": torch.from_numpy(c1.node_offsets).to(dev),
+            "poffs": torch.from_numpy(c1.prefix_offsets).to(dev),
+            "q": c1.q.to(dev), "kt": c1.k_tree.to(dev), "vt": c1.v_tree.to(dev),
+            "kp": c1.k_prefix.to(dev), "vp": c1.v_prefix.to(dev)}
+    set_bytes = sum(v.numel() * v.element_size() for v in base.values())
+    n = rotation_sets(steps, -(-2 * 256 * 2**20 // set_bytes), set_bytes)
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n - 1)]
+    B, max_prefix = c1.B, c1.max_prefix
+    mask = torch.empty((c1.total_nodes, 1), dtype=torch.uint64, device=dev)
+    depth = torch.empty(c1.total_nodes, dtype=torch.int32, device=dev)
+    status = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty_like(base["q"])
+    ws = torch.zeros(max(ta.forward_workspace_size(c1.dtype, B, c1.total_nodes, 1, c1.Hq, c1.Hkv,
+                                                   c1.D, c1.total_prefix, max_prefix), 16),
+                     dtype=torch.uint8, device=dev)
+
+    def call(s):
+        if separate_mask:
+            ta.forward(s["q"], s["kt"], s["vt"], s["kp"], s["vp"], s["poffs"], s["noffs"], mask, 1,
+                       max_prefix, c1.scale, out=out, workspace=ws)
+        else:
+            ta.mask_and_forward(s["parents"], s["q"], s["kt"], s["vt"], s["kp"], s["vp"],
+                                s["poffs"], s["noffs"], 1, max_prefix, c1.scale, out=out,
+                                mask=mask, depth=depth, status=status, workspace=ws)
+
+    ta.build_mask(base["parents"], base["noffs"], 1, mask=mask, depth=depth, status=status)
+    for s in sets:
+        call(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in sets:
+            call(s)
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps // n):
+        g.replay()
+    e1.record(stream)
+    e1.synchronize()
+    t1 = e0.elapsed_time(e1) * 1e3 / steps
+    return {"what": f"forward with {case.max_nodes}-node trees over the time with one-node trees, "
+                    "same prefixes", "t_N_us": round(t_fwd_us, 3), "t_N1_us": round(t1, 3),
+            "N": case.max_nodes, "ratio": round(t_fwd_us / t1, 4)}
 
 
 def cpu_baseline(case, seconds):

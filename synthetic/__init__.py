@@ -202,12 +202,20 @@ CONFIGS = {
                        dtype="bf16", vocab=0, seed=4),
     "forest": dict(B=8, Hq=32, Hkv=8, D=128, L=16384, tree=(512, 8, 16, None),
                    dtype="bf16", vocab=128256, seed=5),
+    # The 8B layer with a one-node tree: the denominator of the cost ratio of
+    # 64 candidates against one at the same prefix.
+    "llama3_8b_n1": dict(B=1, Hq=32, Hkv=8, D=128, L=4096, tree=(1, 1, 6, 4),
+                         dtype="bf16", vocab=128256, seed=2),
+    # A tree-heavy layer: 4096 draft nodes over a 1024-token prefix, a random
+    # recursive forest of 16 roots (no depth or branching cap: deep and bushy).
+    "tree_4096": dict(B=1, Hq=32, Hkv=8, D=128, L=1024, tree=(4096, 16, None, None),
+                      dtype="bf16", vocab=128256, seed=6),
 }
 
 
 def make_config_case(name: str, *, with_logits: Optional[bool] = None,
                      seed: Optional[int] = None) -> TreeAttnCase:
-    """Inputs of one of the five named workloads.
+    """Inputs of one of the named workloads.
 
     Each sequence draws its own tree from ``default_rng(seed * 1000 + b)``;
     ragged prefix lengths (the batched workload) come from

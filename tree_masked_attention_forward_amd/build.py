@@ -3,7 +3,9 @@
     python tree_masked_attention_forward_amd/build.py
 
 Each source is compiled to an object file in parallel, then linked into
-``tree_masked_attention_forward_amd/libtreeattn.so``.  Packed-fp32 VALU
+``tree_masked_attention_forward_amd/libtreeattn.so``; the benchmark's
+measurement probes (``csrc/probes.hip``) go into ``libtaprobes.so`` beside it,
+which the package never loads.  Packed-fp32 VALU
 instructions are switched off for all device code.  The attention kernels are
 scheduled for instruction-level parallelism (LLVM's AMDGPU ``max-ilp``
 strategy): their loop is a dependent MFMA -> softmax -> MFMA chain per wave,
@@ -24,6 +26,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtreeattn.so")
+# The benchmark's measurement probes (streaming read, empty launch) live in a
+# library of their own, never loaded by the package.
+PROBE_LIB = os.path.join(PKG, "libtaprobes.so")
+PROBE_SOURCES = ["probes.hip"]
 SOURCES = ["api.cpp", "mask_build.hip", "attn_fwd.hip", "attn_fwd_f32.hip", "verify.hip",
            "kv_commit.hip"]
 ARCH = os.environ.get("TREE_ATTN_ARCH", "gfx950")
@@ -46,6 +52,12 @@ def compile_flags():
 
 
 def build(verbose: bool = False) -> str:
+    _build_one(SOURCES, LIB, verbose)
+    _build_one(PROBE_SOURCES, PROBE_LIB, verbose)
+    return LIB
+
+
+def _build_one(sources, lib, verbose):
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="treeattn_build_") as tmp:
         def one(src):
@@ -62,14 +74,13 @@ def build(verbose: bool = False) -> str:
             return obj
 
         with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-            objs = list(ex.map(one, SOURCES))
-        tmp_lib = LIB + ".tmp"
+            objs = list(ex.map(one, sources))
+        tmp_lib = lib + ".tmp"
         cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{r.stderr}")
-        os.replace(tmp_lib, LIB)
-    return LIB
+        os.replace(tmp_lib, lib)
 
 
 if __name__ == "__main__":
