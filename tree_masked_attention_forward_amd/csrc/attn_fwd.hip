@@ -504,10 +504,21 @@ __device__ void merge_in_kernel(const KParams& P, long long m) {
         if (s < rgn.Sb)
           ma.add(__builtin_bit_cast(float2, ml_s[s][lane & 31]),
                  __builtin_bit_cast(u32x2_t, ov[s]), P.scale_log2);
-      for (int s = kBatch; s < rgn.Sb; ++s) {
-        const long long it = item0 + s * split_stride;
-        ma.add(__builtin_bit_cast(float2, load_part(ml_ptr(it, rl))),
-               __builtin_bit_cast(u32x2_t, load_part(o_ptr(it))), P.scale_log2);
+      // Splits past the first kBatch (at most 32 in all): requested together
+      // too, then folded in.
+      if (rgn.Sb > kBatch) {
+        unsigned long long mv[kBatch];
+#pragma unroll
+        for (int s = 0; s < kBatch; ++s) {
+          const long long it = item0 + (kBatch + s < rgn.Sb ? kBatch + s : 0) * split_stride;
+          mv[s] = load_part(ml_ptr(it, rl));
+          ov[s] = load_part(o_ptr(it));
+        }
+#pragma unroll
+        for (int s = 0; s < kBatch; ++s)
+          if (kBatch + s < rgn.Sb)
+            ma.add(__builtin_bit_cast(float2, mv[s]), __builtin_bit_cast(u32x2_t, ov[s]),
+                   P.scale_log2);
       }
     } else {
       ma.M = __builtin_nanf("");
@@ -1285,11 +1296,22 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
     if (k < Sb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) ma[e].add(ml[k], h[k][e], c2);
-  for (int s = kPre; s < Sb; ++s) {
-    const long long it = item0 + s * split_stride;
-    const float2 m_l = P.ws_ml[(size_t)it * P.rows_wg + rl];
+  // The rest kPre splits at a time, each batch requested before it is used.
+  for (int s0 = kPre; s0 < Sb; s0 += kPre) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ma[e].add(m_l, P.ws_o[oslot(it, e)], c2);
+    for (int k = 0; k < kPre; ++k) {
+      if (s0 + k < Sb) {
+        const long long it = item0 + (s0 + k) * split_stride;
+        ml[k] = P.ws_ml[(size_t)it * P.rows_wg + rl];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[k][e] = P.ws_o[oslot(it, e)];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kPre; ++k)
+      if (s0 + k < Sb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ma[e].add(ml[k], h[k][e], c2);
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) store_merged(P, sq, g, r, rl, e, j, hh, ma[e]);
