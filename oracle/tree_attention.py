@@ -13,9 +13,13 @@ Readings of the pages taken here (where they are silent or disagree):
     Attention Mask; [ZT] How It Works, Common Confusions).  The comparison
     table's remark that attention crosses branches at equal depth contradicts
     both pages and is not followed.
-  * a tree is a parent array in flattened (topological) order: parent[i] is -1
-    (a root; several roots make a forest) or lies in [0, i).  Anything else
-    makes the whole sequence invalid.
+  * a tree is a parent array over the sequence's nodes: parent[i] is -1 (a
+    root; several roots make a forest) or the index of another node of the
+    same sequence, and following parents from any node reaches a root.  The
+    flattened order is free: a reranked draft ([ZT] Where It Appears: EAGLE-2
+    builds the ancestry mask after reranking its tree) may list a child before
+    its parent.  An out-of-range parent or a cycle makes the whole sequence
+    invalid.
   * query head h reads KV head h // (Hq // Hkv).
   * softmax is natural-base with a caller-given scale; lse is natural log.
   * greedy acceptance: row i of the logits is the target's distribution for
@@ -52,8 +56,21 @@ def _f64(x) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def tree_is_valid(parents: Sequence[int]) -> bool:
-    """Every parent is -1 or an earlier node of the same sequence."""
-    return all(p == -1 or 0 <= p < i for i, p in enumerate(int(x) for x in parents))
+    """Every parent is -1 or another node of the same sequence, and the parent
+    pointers form a forest: walking them from any node reaches -1 within n
+    steps (a longer walk has entered a cycle)."""
+    par = [int(x) for x in parents]
+    n = len(par)
+    if any(not (p == -1 or (0 <= p < n and p != i)) for i, p in enumerate(par)):
+        return False
+    for i in range(n):
+        p, steps = par[i], 0
+        while p != -1:
+            steps += 1
+            if steps > n:
+                return False
+            p = par[p]
+    return True
 
 
 def root_path(parents: Sequence[int], i: int) -> List[int]:
@@ -101,8 +118,8 @@ def build_mask(parents: np.ndarray, node_offsets: np.ndarray, max_nodes: int
     Returns (mask uint64 [sum_N][W], depth int32 [sum_N], status int32 [B])
     with W = ceil(max_nodes / 64).  A sequence whose offsets are malformed gets
     STATUS_INVALID_ARG and its rows are left untouched (zero); a sequence whose
-    parent array is not a topologically ordered forest gets STATUS_INVALID_TREE,
-    all-zero mask rows and depth -1.
+    parent array is not a forest (a parent out of range, a cycle) gets
+    STATUS_INVALID_TREE, all-zero mask rows and depth -1.
     """
     parents = np.asarray(parents, dtype=np.int64)
     node_offsets = np.asarray(node_offsets, dtype=np.int64)

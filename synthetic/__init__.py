@@ -31,6 +31,7 @@ __all__ = [
     "CONFIGS",
     "TreeAttnCase",
     "random_tree",
+    "rerank_tree",
     "make_case",
     "make_config_case",
     "EXAMPLE_PARENTS",
@@ -74,6 +75,19 @@ def random_tree(rng: np.random.Generator, n_nodes: int, n_roots: int = 1,
         depth[i] = depth[p] + 1
         kids[p] += 1
     return parents
+
+
+def rerank_tree(parents: Sequence[int], perm: Sequence[int]) -> np.ndarray:
+    """The same tree listed in another order: node k of the result is node
+    perm[k] of `parents` (perm is a permutation of range(n)).  Parent links
+    follow their nodes, so a child may now come before its parent, as in a
+    draft tree reordered by score."""
+    par = np.asarray(parents, dtype=np.int64)
+    perm = np.asarray(perm, dtype=np.int64)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(len(perm))
+    old = par[perm]
+    return np.where(old < 0, -1, inv[np.maximum(old, 0)]).astype(np.int32)
 
 
 @dataclass

@@ -112,13 +112,66 @@ def test_mask_multiword_packing_and_invariants():
 
 
 def test_mask_rejects_invalid_trees_and_offsets():
-    off = np.array([0, 3, 6, 9], np.int32)
-    parents = np.array([-1, 0, 1,    -1, 2, 0,    -1, 0, 3], np.int32)
+    off = np.array([0, 3, 6, 9, 12, 15], np.int32)
+    parents = np.array([-1, 0, 1,    -1, 2, 0,    -1, 0, 3,    -1, 1, 1,    1, 2, 0], np.int32)
     mask, depth, status = oracle.build_mask(parents, off, 3)
-    assert status.tolist() == [0, 2, 2]           # self/forward parent, out of range
-    assert (mask[3:] == 0).all() and (depth[3:] == -1).all()
+    # a later parent is fine (a reranked tree: 0 <- 2 <- 1); a parent out of
+    # range, a self-parent and a cycle (0 -> 1 -> 2 -> 0, no root) are not
+    assert status.tolist() == [0, 0, 2, 2, 2]
+    assert mask[3:6, 0].tolist() == [0b001, 0b111, 0b101] and depth[3:6].tolist() == [0, 2, 1]
+    assert (mask[6:] == 0).all() and (depth[6:] == -1).all()
     mask, depth, status = oracle.build_mask(parents[:6], np.array([0, 3, 6], np.int32), 2)
     assert status.tolist() == [1, 1]              # more nodes than max_nodes
+
+
+def _all_parent_arrays(n):
+    """Every array with entries in {-1} U [0, n): (n + 1)^n of them, in any
+    order, with cycles and self-parents among them."""
+    return itertools.product(range(-1, n), repeat=n)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_validity_is_acyclicity_for_every_tiny_parent_array(n):
+    """A parent array is a forest iff its child -> parent adjacency matrix is
+    nilpotent (no walk of length n exists: the n-th boolean power is zero);
+    valid ones, in whatever order, get the transitive closure as their mask."""
+    for parents in _all_parent_arrays(n):
+        a = np.zeros((n, n), dtype=np.int64)
+        for i, p in enumerate(parents):
+            if p >= 0:
+                a[i, p] = 1
+        nilpotent = not np.linalg.matrix_power(a, n).any()
+        self_free = all(p != i for i, p in enumerate(parents))
+        assert oracle.tree_is_valid(parents) == (nilpotent and self_free), parents
+        if nilpotent:
+            np.testing.assert_array_equal(oracle.ancestor_mask_dense(list(parents)),
+                                          _closure_by_matrix_powers(list(parents)))
+
+
+def _perm_matrix_check(parents, perm):
+    """Mask of the reranked tree = P M P^T: row k, column k' of the reranked
+    mask is row perm[k], column perm[k'] of the original one."""
+    re = synthetic.rerank_tree(parents, perm)
+    d0 = oracle.ancestor_mask_dense(parents)
+    d1 = oracle.ancestor_mask_dense(re)
+    np.testing.assert_array_equal(d1, d0[np.ix_(perm, perm)])
+    return re
+
+
+def test_reranked_tree_mask_and_depth_follow_the_permutation():
+    rng = np.random.default_rng(23)
+    for n, roots in ((9, 1), (70, 3), (200, 5)):
+        parents = synthetic.random_tree(rng, n, n_roots=roots)
+        perm = rng.permutation(n)
+        re = _perm_matrix_check(parents, perm)
+        W = -(-n // 64)
+        m0, d0, s0 = oracle.build_mask(parents, np.array([0, n], np.int32), n)
+        m1, d1, s1 = oracle.build_mask(re, np.array([0, n], np.int32), n)
+        assert s1.tolist() == [0]
+        np.testing.assert_array_equal(d1, d0[perm])
+        assert any(re[k] > k for k in range(n)), "the reranked order should not be topological"
+        np.testing.assert_array_equal(m1, _pack_with_numpy(_closure_by_matrix_powers(re.tolist()),
+                                                           W))
 
 
 # ------------------------------------------------------------ attention pins
@@ -348,6 +401,51 @@ def test_verify_matches_dfs_brute_force(seed):
         assert anodes[b, :len(best)].tolist() == best
         assert (anodes[b, len(best):] == -1).all()
         assert atok[b, :len(best)].tolist() == [int(draft[lo + j]) for j in best]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_verify_reranked_matches_dfs_brute_force(seed):
+    """Trees listed in a random order (children before parents): the DFS over
+    children lists does not use the order, so it pins the oracle there too."""
+    rng = np.random.default_rng(200 + seed)
+    trees = []
+    for _ in range(3):
+        t = synthetic.random_tree(rng, int(rng.integers(1, 40)), int(rng.integers(1, 4)), 6, 3)
+        trees.append(synthetic.rerank_tree(t, rng.permutation(len(t))))
+    parents = np.concatenate(trees).astype(np.int32)
+    off = np.zeros(4, np.int32)
+    off[1:] = np.cumsum([len(t) for t in trees])
+    V = 50
+    pred = rng.integers(0, V, len(parents))
+    draft = np.where(rng.random(len(parents)) < 0.8, pred, rng.integers(0, V, len(parents)))
+    lg = _logits_for(pred, V, rng)
+    maxn = max(len(t) for t in trees)
+    p, alen, anodes, atok = oracle.verify_greedy(lg, draft, parents, off, maxn)
+    for b, t in enumerate(trees):
+        lo = off[b]
+        match = [draft[lo + i] == pred[lo + i] for i in range(len(t))]
+        best = _best_path_by_dfs(t.tolist(), match)
+        assert alen[b] == len(best)
+        assert anodes[b, :len(best)].tolist() == best
+        assert atok[b, :len(best)].tolist() == [int(draft[lo + j]) for j in best]
+
+
+def test_reranked_tree_attention_is_the_permuted_attention():
+    """Listing the nodes of a tree in another order (their rows and parent
+    links moved along) permutes the outputs and changes nothing else: every
+    node's visible set is the same set of rows."""
+    rng = np.random.default_rng(41)
+    n = 37
+    parents = synthetic.random_tree(rng, n, n_roots=2, max_depth=7)
+    c0 = _case([11], [parents.tolist()], Hq=4, Hkv=2, D=16, seed=41)
+    perm = rng.permutation(n)
+    c1 = _case([11], [synthetic.rerank_tree(parents, perm).tolist()], Hq=4, Hkv=2, D=16, seed=41)
+    c1.q, c1.k_tree, c1.v_tree = c0.q[perm], c0.k_tree[perm], c0.v_tree[perm]
+    c1.k_prefix, c1.v_prefix = c0.k_prefix, c0.v_prefix
+    o0, l0 = _run(c0)
+    o1, l1 = _run(c1)
+    np.testing.assert_array_equal(o1, o0[perm])
+    np.testing.assert_array_equal(l1, l0[perm])
 
 
 def test_verify_on_chain_equals_flat_scan():
