@@ -12,12 +12,15 @@
  *     Parallel Verification Deliver 4x LLM Speedups", news.premlal.in, its
  *     code listing (build_tree_attention_mask, verify_candidate_tree).
  *
- * A draft tree is flattened into one token sequence in topological order: in
- * sequence b, node i (local index 0..N_b-1) has parent[i] = -1 (a root; more
- * than one root makes a forest) or 0 <= parent[i] < i.  Every node attends to
- * the sequence's whole verified prefix (the KV cache), to itself and to its
- * ancestors, and to nothing else: no sibling, no node of another branch or
- * another tree.
+ * A draft tree is flattened into one token sequence: in sequence b, node i
+ * (local index 0..N_b-1) has parent[i] = -1 (a root; more than one root makes
+ * a forest) or the local index of another node of the sequence, and the
+ * parent links form a forest (no cycle).  The order is free: a tree reranked
+ * after drafting may list a child before its parent (zhongzhoutan-coder
+ * "Tree Attention", Where It Appears: EAGLE-2 builds the ancestry mask after
+ * reranking).  Every node attends to the sequence's whole verified prefix
+ * (the KV cache), to itself and to its ancestors, and to nothing else: no
+ * sibling, no node of another branch or another tree.
  *
  * Conventions shared by every call:
  *   - Array arguments are DEVICE pointers unless marked [host].  Every buffer is
@@ -63,7 +66,7 @@ extern "C" {
 typedef enum {
   TA_OK = 0,
   TA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad offsets */
-  TA_ERR_INVALID_TREE = 2,  /* parent array is not a topologically ordered forest */
+  TA_ERR_INVALID_TREE = 2,  /* parent array is not a forest (out of range, cycle) */
   TA_ERR_UNSUPPORTED = 3,   /* head size / dtype / node count outside the limits */
   TA_ERR_WORKSPACE = 4,     /* workspace missing or smaller than the size query */
   TA_ERR_HIP = 5            /* a HIP runtime call failed */
@@ -94,14 +97,16 @@ typedef enum { TA_F32 = 0, TA_BF16 = 1 } ta_dtype;
  *          bits are 0.
  *   depth  out int32 [sum_N], nullable: root = 0.
  *   tree_status out int32 [B], nullable: per sequence TA_OK;
- *          TA_ERR_INVALID_TREE if some parent is outside {-1} U [0, i) (then the
+ *          TA_ERR_INVALID_TREE if some parent is outside {-1} U [0, N_b), is
+ *          the node itself, or the parents form a cycle (then the
  *          sequence's mask rows are 0 and its depths -1); TA_ERR_INVALID_ARG if
  *          its offsets are decreasing, exceed max_nodes or total_nodes (then
  *          its rows are not written).
  * The mask is computed once per verification step and reused by every layer.
  * Up to 1024 nodes one workgroup per sequence builds the rows in LDS by
  * pointer jumping; larger trees are split over workgroups of 64 rows, each
- * walking its rows' parent chains (time grows with the tree's depth).
+ * walking its rows' parent chains (time grows with the tree's depth, and
+ * with the tree's size too when a child is listed before its parent).
  */
 TA_API int tree_attn_build_mask(const int32_t* parents, const int32_t* node_offsets, int32_t B,
                          int32_t total_nodes, int32_t max_nodes, uint64_t* mask,

@@ -65,7 +65,7 @@ CASES = [
     ([1000], [(9, 2, 6, 4)], 16, 2),                  # forest, G = 8
     ([100, 200], [(128, 3, 10, 3), (128, 1, 127, 1)], 4, 1),   # 128 nodes: chain of 128
     ([129, 2049], [(130, 3, 6, 4), (33, 3, 6, 4)], 4, 1),      # 130 nodes: two-call path
-    ([64, 64, 64], [[-1, 0, 1], [-1, 2, 0], [0, -1]], 8, 2),   # invalid trees: status 2
+    ([64, 64, 64], [[-1, 0, 1], [-1, 2, 0], [0, -1]], 8, 2),   # reranked tree; self-parent: status 2
     ([37, 50, 300], [(17, 1, 6, 4), [], (70, 1, 6, 4)], 8, 2),  # a sequence without nodes
 ]
 

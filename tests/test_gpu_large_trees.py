@@ -46,7 +46,7 @@ def test_large_masks_bit_exact(ta):
 
 def test_large_mask_invalid_tree_and_chain_at_the_limit(ta):
     bad = _trees(2, [(1500, 1, 12, None)])[0]
-    bad[700] = 900                                   # a parent after its child
+    bad[0] = 900                                     # the root under a descendant: a cycle
     chain = [-1] + list(range(4095))
     c = synthetic.make_case("lbad", prefix_lens=[0] * 3, trees=[bad, chain, [-1, 0]], Hq=1,
                             Hkv=1, D=8, dtype=torch.float32, seed=2)

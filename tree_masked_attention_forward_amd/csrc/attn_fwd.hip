@@ -169,7 +169,10 @@ __device__ inline bool row_tile_range(const KParams& P, const Seq& sq, int r, Ra
   g.rows_here = min(P.rows_wg, rows_b - row0);
   g.n_hi = (row0 + g.rows_here - 1) / P.G;
   g.Lt = (sq.L + kKT - 1) / kKT;
-  g.T = g.Lt + (g.n_hi + kKT) / kKT;
+  // Every tree tile of the sequence: in a reranked tree an ancestor may be
+  // listed after its descendant, so the row tile's own nodes do not bound
+  // the keys it sees (the mask drops the rest).
+  g.T = g.Lt + (sq.nn + kKT - 1) / kKT;
   const int sb = P.piece > 0 ? (g.T + P.piece - 1) / P.piece
                              : (int)(((long long)P.S * g.T + P.tmax - 1) / P.tmax);
   g.Sb = max(1, min(sb, min(P.S, g.T)));
@@ -972,23 +975,35 @@ void fwd_bf16_kernel(KParams P) {
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       // Ancestor rows from the parents (scope of tree_attn_build_mask):
-      // node i sees itself and every node on its path to the root.  A
-      // tree is valid iff every parent p of node k satisfies -1 <= p < k
-      // (each workgroup checks the whole sequence, so all agree); an
-      // invalid tree gets all-zero rows, depth -1 and status 2.
+      // node i sees itself and every node on its path to the root, in
+      // whatever order the nodes are listed.  A tree is valid iff every
+      // parent is -1 or another node of the sequence and no chain of
+      // parents is longer than the sequence (no cycle); each wave checks
+      // the whole sequence, so all agree.  An invalid tree gets all-zero
+      // rows, depth -1 and status 2.
       const int32_t* par = reinterpret_cast<const int32_t*>(aux);
       bool bad = false;
       for (int h = 0; h * 64 < sq.nn; ++h) {
         const int k = h * 64 + lane;
         if (k < sq.nn) {
           const int p = par[k];
-          bad = bad || p < -1 || p >= k;
+          bad = bad || p < -1 || p >= sq.nn || p == k;
         }
       }
       bad = __ballot(bad) != 0;
+      if (!bad) {
+        for (int h = 0; h * 64 < sq.nn; ++h) {
+          const int k = h * 64 + lane;
+          int steps = 0;
+          for (int cur = k < sq.nn ? par[k] : -1; cur >= 0 && steps <= sq.nn; cur = par[cur])
+            ++steps;
+          bad = bad || steps > sq.nn;
+        }
+        bad = __ballot(bad) != 0;
+      }
       uint64_t lo = 0, hi = 0;
       if (!bad) {
-        for (int cur = node; cur >= 0; cur = par[cur]) {   // parents strictly decrease
+        for (int cur = node; cur >= 0; cur = par[cur]) {   // ends: the parents form a forest
           if (cur < 64)
             lo |= 1ull << cur;
           else

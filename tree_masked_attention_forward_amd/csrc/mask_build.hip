@@ -16,18 +16,25 @@
 // needs ceil(log2(d + 1)) rounds.  R is updated in place: a row read while
 // its owner is extending it is still a subset of that node's ancestors, and
 // J is double buffered, so the covered distance never falls behind J.  The
-// depth of i is |R(i)| - 1.
+// depth of i is |R(i)| - 1.  Nothing here depends on the order in which the
+// nodes are listed: a reranked tree may list a child before its parent ("Tree
+// Attention", zhongzhoutan-coder.github.io, Where It Appears: EAGLE-2 builds
+// the mask after reranking).  A parent out of range or equal to its node is
+// invalid, and so is a cycle, found as a jump still pending after the
+// ceil(log2(n + 1)) rounds any forest of n nodes needs.
 //
 // Trees above 1024 nodes (up to TA_MAX_NODES): the rows no longer fit in LDS.
 // build_mask_large_kernel spreads a sequence over several workgroups; each
 // keeps the whole parent array in LDS (4 bytes per node), validates it, and
 // writes the rows of its own block of nodes straight to global memory.  Lane
-// (row i, word w) follows the parent chain of i, whose indices fall strictly
-// (parents precede children), and sets the bits of the ancestors inside word
-// w, stopping as soon as the chain drops below the word.  A row's depth is
-// the popcount summed over its lanes, minus one.  The walk costs depth + 1
-// LDS steps for the lane of the root's word: fast for bushy trees, linear in
-// N for a long chain.
+// (row i, word w) follows the parent chain of i and sets the bits of the
+// ancestors inside word w, stopping as soon as the chain drops below the word
+// when the order is
+// topological (every parent before its child: the chain's indices fall), and
+// following it to the root otherwise.  A row's depth is the popcount summed
+// over its lanes, minus one.  The walk costs up to depth + 1 LDS steps per
+// lane: fast for bushy trees, linear in N for a long chain.  Cycles are found
+// first, by pointer jumping over the parent array in LDS.
 #include "internal.h"
 
 namespace ta {
@@ -84,26 +91,37 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
     const int i = tid + k * kThreads;
     if (i < n) {
       const int p = pv[k];
-      bad |= (p < -1 || p >= i);
+      bad |= (p < -1 || p >= n || p == i);
       any |= (p >= 0);
       jmp0[i] = p;
       for (int w = 0; w < W; ++w) rows[i * W + w] = (i >> 6) == w ? 1ull << (i & 63) : 0ull;
     }
   }
   bad = __syncthreads_or(bad);
-  if (bad) {
+  auto invalid = [&]() {
     for (int i = tid; i < n; i += kThreads) {
       for (int w = 0; w < W; ++w) mask[(size_t)(n0 + i) * W + w] = 0ull;
       if (depth) depth[n0 + i] = -1;
     }
     if (tid == 0 && status) status[b] = 2;  // TA_ERR_INVALID_TREE
+  };
+  if (bad) {
+    invalid();
     return;
   }
   any = __syncthreads_or(any);
 
+  // Rounds any forest of n nodes needs (2^rounds > n > depth); a jump still
+  // pending after them lies on a cycle.
+  int rounds = 1;
+  while ((1 << rounds) <= n) ++rounds;
   int32_t* jcur = jmp0;
   int32_t* jnext = jmp1;
-  while (any) {
+  for (int round = 0; any; ++round) {
+    if (round == rounds) {
+      invalid();
+      return;
+    }
     for (int idx = tid; idx < n * W; idx += kThreads) {
       const int i = idx / W;
       const int j = jcur[i];
@@ -158,13 +176,34 @@ __global__ __launch_bounds__(kLargeThreads) void build_mask_large_kernel(
   }
   // Every workgroup checks the whole parent array, so all of them agree on
   // whether the tree is valid.
+  __shared__ int32_t jmp[2][TA_MAX_NODES];
   int bad = 0;
+  int later = 0;   // some parent after its child: walk whole chains below
   for (int i = tid; i < n; i += kLargeThreads) {
     const int p = parents[n0 + i];
-    bad |= (p < -1 || p >= i);
+    bad |= (p < -1 || p >= n || p == i);
+    later |= p > i;
     par[i] = p;
+    jmp[0][i] = p;
   }
   bad = __syncthreads_or(bad);
+  later = __syncthreads_or(later);
+  if (!bad && later) {
+    // Cycle check by pointer jumping: after k rounds jmp holds the ancestor
+    // 2^k steps up; in a forest of n nodes every one is -1 once 2^k > n.
+    int cur = 0;
+    for (int k = 0; (1 << k) <= n; ++k) {
+      for (int i = tid; i < n; i += kLargeThreads) {
+        const int j = jmp[cur][i];
+        jmp[cur ^ 1][i] = j >= 0 ? jmp[cur][j] : -1;
+      }
+      __syncthreads();
+      cur ^= 1;
+    }
+    int cyc = 0;
+    for (int i = tid; i < n; i += kLargeThreads) cyc |= jmp[cur][i] >= 0;
+    bad = __syncthreads_or(cyc);
+  }
   const int r1 = min(n, r0 + kLargeRows);
   if (bad) {
     for (int idx = tid; idx < (r1 - r0) * W; idx += kLargeThreads)
@@ -182,9 +221,10 @@ __global__ __launch_bounds__(kLargeThreads) void build_mask_large_kernel(
     uint64_t word = 0ull;
     if (i < r1 && w < W) {
       const int lo = 64 * w;
+      const int stop = later ? 0 : lo;   // topological: the chain's indices fall
       int x = i;
-      while (x >= lo) {   // ends: x falls strictly along the chain, down to -1
-        if (x < lo + 64) word |= 1ull << (x - lo);
+      while (x >= stop) {   // ends at -1: the tree is a forest
+        if (x >= lo && x < lo + 64) word |= 1ull << (x - lo);
         x = par[x];
       }
       mask[(size_t)(n0 + i) * W + w] = word;

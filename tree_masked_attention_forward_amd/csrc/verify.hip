@@ -18,15 +18,15 @@
 //       accepts node i iff mask[i] is a subset of the match set (every node on
 //       its root path matches), and picks the accepted node with the most mask
 //       bits (the longest path), lowest index on ties.  The accepted path is
-//       the set bits of that node's mask in increasing order, which is root to
-//       leaf because parents precede children.
+//       the set bits of that node's mask, each placed at its depth (the
+//       popcount of its own row minus one), so root to leaf in whatever order
+//       the nodes are listed.
 //
 // Next-token rows (tree_verify_greedy_next): row i holds the target's
 // distribution of the token that follows node i, and one more row per
 // sequence that of the token after the prefix.  A node's draft token is then
 // checked against the prediction of its parent's row (a root's against the
-// prefix row); the parent is the highest set bit of the node's mask row below
-// the node itself.  The prediction after the accepted leaf (after the prefix
+// prefix row); the parent is the deepest of the node's proper ancestors.  The prediction after the accepted leaf (after the prefix
 // when nothing is accepted) is the bonus token the step emits on top.
 #include "internal.h"
 
@@ -324,15 +324,31 @@ __global__ __launch_bounds__(kThreads) void path_select_kernel(
 
   // Match set: node i matches iff its draft token is the target's argmax.
   // Thread t, slot k holds node t + 256k, so wave w's ballot is word 4k + w.
+  // Depth of node j: its row holds itself and its ancestors.
+  auto depth_of = [&](int j) {
+    int c = 0;
+    for (int w = 0; w < W; ++w) c += __popcll(rows[j * W + w]);
+    return c - 1;
+  };
   auto expected = [&](int i) {
     if constexpr (NEXT) {
-      // parent = highest ancestor index below i (parents precede children)
-      for (int w = i >> 6; w >= 0; --w) {
+      // parent = the deepest proper ancestor (in whatever order the nodes
+      // are listed)
+      int par = -1, par_d = -1;
+      for (int w = 0; w < W; ++w) {
         uint64_t mw = rows[i * W + w];
-        if (w == (i >> 6)) mw &= (1ull << (i & 63)) - 1ull;
-        if (mw) return tgt[64 * w + 63 - __builtin_clzll(mw)];
+        if (w == (i >> 6)) mw &= ~(1ull << (i & 63));
+        while (mw) {
+          const int j = 64 * w + __builtin_ctzll(mw);
+          mw &= mw - 1ull;
+          const int d = depth_of(j);
+          if (d > par_d) {
+            par_d = d;
+            par = j;
+          }
+        }
       }
-      return root_pred;
+      return par >= 0 ? tgt[par] : root_pred;
     } else {
       return tgt[i];
     }
@@ -378,9 +394,10 @@ __global__ __launch_bounds__(kThreads) void path_select_kernel(
   const int len = (int)(key >> 32);
   const int best = (int)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
 
-  // The accepted path is the set bits of the best node's row in increasing
-  // order (root to leaf); each of its nodes is placed by the thread that
-  // holds its draft token.
+  // The accepted path is the set bits of the best node's row, placed root
+  // to leaf by depth (each node's depth is its position on the path, in
+  // whatever order the nodes are listed) by the thread that holds its draft
+  // token.
   int32_t* an = accept_nodes + (size_t)b * max_nodes;
   int32_t* at = accept_tokens + (size_t)b * max_nodes;
   for (int pos = tid; pos < max_nodes; pos += kThreads)
@@ -392,11 +409,8 @@ __global__ __launch_bounds__(kThreads) void path_select_kernel(
     const uint64_t* brow = rows + (size_t)best * W;
     auto place = [&](int j, int32_t d) {
       if (j >= nn) return;
-      const int wj = j >> 6;
-      const uint64_t mw = brow[wj];
-      if (!((mw >> (j & 63)) & 1ull)) return;
-      int pos = __popcll(mw & ((1ull << (j & 63)) - 1ull));
-      for (int w = 0; w < wj; ++w) pos += __popcll(brow[w]);
+      if (!((brow[j >> 6] >> (j & 63)) & 1ull)) return;
+      const int pos = depth_of(j);
       an[pos] = j;
       at[pos] = d;
     };
@@ -433,6 +447,7 @@ __global__ __launch_bounds__(kBigThreads) void path_select_large_kernel(
     int32_t* __restrict__ accept_tokens, const float2* __restrict__ ws_root,
     int32_t* __restrict__ bonus_token) {
   __shared__ int32_t tgt[TA_MAX_NODES];
+  __shared__ int32_t dep[TA_MAX_NODES];
   __shared__ int32_t par[NEXT ? TA_MAX_NODES : 1];
   __shared__ uint64_t match_w[TA_MAX_NODES / 64];
   __shared__ unsigned long long red[kBigThreads / 64];
@@ -486,14 +501,30 @@ __global__ __launch_bounds__(kBigThreads) void path_select_large_kernel(
     if (lim - 64 * w < 64) mw &= (1ull << (lim - 64 * w)) - 1ull;
     return mw;
   };
+  // Depth of every node (its row's popcount minus one): a node's position on
+  // any root path, in whatever order the nodes are listed.
+  for (int base = 0; base < nn; base += rows_per_pass) {
+    const int i = base + tid / Wp;
+    int c = __popcll(row_word(i, nn));
+    for (int o = Wp >> 1; o > 0; o >>= 1) c += __shfl_xor(c, o);
+    if (i < nn && w == 0) dep[i] = c - 1;
+  }
+  __syncthreads();
   if constexpr (NEXT) {
-    // Parent of i: the highest ancestor below i.
+    // Parent of i: its deepest proper ancestor, as (depth, index) packed for
+    // one max over the row's lanes.
     for (int base = 0; base < nn; base += rows_per_pass) {
       const int i = base + tid / Wp;
-      const uint64_t mw = row_word(i, i);
-      int hi = mw ? 64 * w + 63 - __builtin_clzll(mw) : -1;
-      for (int o = Wp >> 1; o > 0; o >>= 1) hi = max(hi, __shfl_xor(hi, o));
-      if (i < nn && w == 0) par[i] = hi;
+      uint64_t mw = row_word(i, nn);
+      if (i < nn && (i >> 6) == w) mw &= ~(1ull << (i & 63));
+      int best = -1;
+      while (mw) {
+        const int j = 64 * w + __builtin_ctzll(mw);
+        mw &= mw - 1ull;
+        best = max(best, (dep[j] << 16) | j);
+      }
+      for (int o = Wp >> 1; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o));
+      if (i < nn && w == 0) par[i] = best >= 0 ? (best & 0xffff) : -1;
     }
   }
   __syncthreads();
@@ -546,25 +577,17 @@ __global__ __launch_bounds__(kBigThreads) void path_select_large_kernel(
     at[pos] = -1;
   }
   if (len > 0 && wave == 0) {
-    // Lane k holds word k of the best row (W <= 64); its bits go after the
-    // popcounts of the lower words.
+    // Lane k holds word k of the best row (W <= 64); each of its nodes goes
+    // to the position given by its depth.
     uint64_t mw = 0ull;
     if (lane < W && 64 * lane < nn) {
       mw = mask[(size_t)(n0 + best) * W + lane];
       if (nn - 64 * lane < 64) mw &= (1ull << (nn - 64 * lane)) - 1ull;
     }
-    const int c = __popcll(mw);
-    int incl = c;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
-    int pos = incl - c;
     while (mw) {
       const int j = 64 * lane + __builtin_ctzll(mw);
-      an[pos] = j;
-      at[pos] = draft[n0 + j];
-      ++pos;
+      an[dep[j]] = j;
+      at[dep[j]] = draft[n0 + j];
       mw &= mw - 1ull;
     }
   }
