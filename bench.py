@@ -49,8 +49,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="llama3_8b")
     p.add_argument("--sets", type=int, default=16,
-                   help="fewest input copies in rotation (more when 512 MB needs more; the count "
-                        "is rounded up to a divisor of --steps)")
+                   help="most input copies in rotation needed to pass 512 MB (the count is then "
+                        "rounded up to a divisor of --steps)")
     p.add_argument("--separate-mask", action="store_true",
                    help="build the mask with its own call (tree_attn_build_mask) instead of "
                         "inside the forward (tree_attn_mask_and_forward)")
@@ -633,7 +633,7 @@ def main():
     # Enough distinct copies to cycle through 2x the 256 MB Infinity Cache, their
     # count a divisor of --steps so that the timed region is whole rounds.
     set_bytes = sum(v.numel() * v.element_size() for v in base.values())
-    n_sets = rotation_sets(args.steps, max(args.sets, -(-2 * 256 * 2**20 // set_bytes)), set_bytes)
+    n_sets = rotation_sets(args.steps, min(args.sets, -(-2 * 256 * 2**20 // set_bytes)), set_bytes)
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_sets - 1)]
     mask = torch.empty((sum_n, W), dtype=torch.uint64, device=dev)
     depth = torch.empty(sum_n, dtype=torch.int32, device=dev)
