@@ -224,6 +224,40 @@ __device__ inline unsigned long long wave_max_u64(unsigned long long x) {
   return m;
 }
 
+// Sum and maximum over each Wp-lane segment of the wave (Wp = 32 or 64), in
+// every lane of the segment: DPP moves inside each 16-lane row (the pairings
+// of wave_best), then the rows' results read as scalars.  No LDS permutes.
+template <int CTRL>
+__device__ inline int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+__device__ inline int seg_sum(int x, int Wp) {
+  x += dpp_i<0xB1>(x);
+  x += dpp_i<0x4E>(x);
+  x += dpp_i<0x141>(x);
+  x += dpp_i<0x140>(x);
+  const int r0 = __builtin_amdgcn_readlane(x, 0), r1 = __builtin_amdgcn_readlane(x, 16);
+  const int r2 = __builtin_amdgcn_readlane(x, 32), r3 = __builtin_amdgcn_readlane(x, 48);
+  if (Wp == 64) return r0 + r1 + r2 + r3;
+  return (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
+}
+__device__ inline int seg_max(int x, int Wp) {
+  x = max(x, dpp_i<0xB1>(x));
+  x = max(x, dpp_i<0x4E>(x));
+  x = max(x, dpp_i<0x141>(x));
+  x = max(x, dpp_i<0x140>(x));
+  const int r0 = __builtin_amdgcn_readlane(x, 0), r1 = __builtin_amdgcn_readlane(x, 16);
+  const int r2 = __builtin_amdgcn_readlane(x, 32), r3 = __builtin_amdgcn_readlane(x, 48);
+  if (Wp == 64) return max(max(r0, r1), max(r2, r3));
+  return (threadIdx.x & 32) ? max(r2, r3) : max(r0, r1);
+}
+// Any lane of the segment set?
+__device__ inline bool seg_any(bool b, int Wp) {
+  const uint64_t bb = __ballot(b);
+  if (Wp == 64) return bb != 0ull;
+  return ((threadIdx.x & 32) ? (bb >> 32) : (bb & 0xffffffffull)) != 0ull;
+}
+
 // Inputs of one sequence that path_select_kernel keeps in registers: slot k
 // of thread t holds item t + 256k of the chunk results, of the draft tokens
 // and of the mask words.  Items past kSpec slots are read where they are used.
@@ -464,20 +498,31 @@ __global__ __launch_bounds__(kBigThreads) void path_select_large_kernel(
 
   // Target argmax per node: a node's cpr chunk results sit in cpr
   // consecutive lanes (cpr a power of two <= 64); ties -> lowest index.
+  // Every scan below requests kScanBatch passes' loads before using any, so
+  // one workgroup walks 4096 rows in a few dozen round trips, not hundreds.
+  constexpr int kPairBatch = 4;
   const int pairs = nn * cpr;
-  for (int p0 = 0; p0 < pairs; p0 += kBigThreads) {
-    const int pidx = p0 + tid;
-    float bv = kNegInf;
-    int bi = 0x7fffffff;
-    if (pidx < pairs) {
-      const float2 x = ws[(size_t)n0 * cpr + pidx];
-      bv = x.x;
-      bi = __float_as_int(x.y);
+  for (int p0 = 0; p0 < pairs; p0 += kBigThreads * kPairBatch) {
+    float2 x[kPairBatch];
+#pragma unroll
+    for (int u = 0; u < kPairBatch; ++u) {
+      const int pidx = p0 + u * kBigThreads + tid;
+      x[u] = pidx < pairs ? ws[(size_t)n0 * cpr + pidx] : make_float2(kNegInf, 0.f);
     }
-    seg_best(bv, bi, cpr);
-    if (pidx < pairs && (pidx & (cpr - 1)) == 0) {
-      tgt[pidx / cpr] = bi;
-      if (target_argmax) target_argmax[n0 + pidx / cpr] = bi;
+#pragma unroll
+    for (int u = 0; u < kPairBatch; ++u) {
+      const int pidx = p0 + u * kBigThreads + tid;
+      float bv = kNegInf;
+      int bi = 0x7fffffff;
+      if (pidx < pairs) {
+        bv = x[u].x;
+        bi = __float_as_int(x[u].y);
+      }
+      seg_best(bv, bi, cpr);
+      if (pidx < pairs && (pidx & (cpr - 1)) == 0) {
+        tgt[pidx / cpr] = bi;
+        if (target_argmax) target_argmax[n0 + pidx / cpr] = bi;
+      }
     }
   }
   if (NEXT && wave == 0) {
@@ -501,21 +546,42 @@ __global__ __launch_bounds__(kBigThreads) void path_select_large_kernel(
     if (lim - 64 * w < 64) mw &= (1ull << (lim - 64 * w)) - 1ull;
     return mw;
   };
-  // Depth of every node (its row's popcount minus one): a node's position on
-  // any root path, in whatever order the nodes are listed.
-  for (int base = 0; base < nn; base += rows_per_pass) {
-    const int i = base + tid / Wp;
-    int c = __popcll(row_word(i, nn));
-    for (int o = Wp >> 1; o > 0; o >>= 1) c += __shfl_xor(c, o);
-    if (i < nn && w == 0) dep[i] = c - 1;
-  }
-  __syncthreads();
+  // Row scans: kScanBatch passes of rows_per_pass rows each per step, the
+  // words of all of them requested first.
+  constexpr int kScanBatch = 16;
+  // The loads are branch-free (rows past the end re-read the sequence's
+  // first row and are zeroed after), so all of a step's loads are issued
+  // before the first is used.
+  const bool w_in = w < W;
+  const uint64_t w_keep = 64 * w + 64 <= nn ? ~0ull : (64 * w < nn ? (1ull << (nn - 64 * w)) - 1ull : 0ull);
+  auto scan_rows = [&](auto&& visit) {
+    for (int base = 0; base < nn; base += rows_per_pass * kScanBatch) {
+      uint64_t mw[kScanBatch];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) {
+        const int i = base + u * rows_per_pass + tid / Wp;
+        mw[u] = mask[(size_t)(n0 + min(i, nn - 1)) * W + (w_in ? w : 0)];
+      }
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) {
+        const int i = base + u * rows_per_pass + tid / Wp;
+        mw[u] = (i < nn && w_in) ? (mw[u] & w_keep) : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) visit(base + u * rows_per_pass + tid / Wp, mw[u]);
+    }
+  };
   if constexpr (NEXT) {
-    // Parent of i: its deepest proper ancestor, as (depth, index) packed for
+    // Depth of every node (its row's popcount minus one: a node's position
+    // on any root path, in whatever order the nodes are listed), then the
+    // parent of i: its deepest proper ancestor, as (depth, index) packed for
     // one max over the row's lanes.
-    for (int base = 0; base < nn; base += rows_per_pass) {
-      const int i = base + tid / Wp;
-      uint64_t mw = row_word(i, nn);
+    scan_rows([&](int i, uint64_t mw) {
+      const int c = seg_sum(__popcll(mw), Wp);
+      if (i < nn && w == 0) dep[i] = c - 1;
+    });
+    __syncthreads();
+    scan_rows([&](int i, uint64_t mw) {
       if (i < nn && (i >> 6) == w) mw &= ~(1ull << (i & 63));
       int best = -1;
       while (mw) {
@@ -523,9 +589,9 @@ __global__ __launch_bounds__(kBigThreads) void path_select_large_kernel(
         mw &= mw - 1ull;
         best = max(best, (dep[j] << 16) | j);
       }
-      for (int o = Wp >> 1; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o));
+      best = seg_max(best, Wp);
       if (i < nn && w == 0) par[i] = best >= 0 ? (best & 0xffff) : -1;
-    }
+    });
   }
   __syncthreads();
 
@@ -546,22 +612,18 @@ __global__ __launch_bounds__(kBigThreads) void path_select_large_kernel(
   __syncthreads();
 
   // Accepted iff the row (cut at nn) lies inside the match set; the longest
-  // accepted path wins, lowest index on ties.
+  // accepted path wins, lowest index on ties.  The same scan leaves every
+  // node's depth for the placement below (the next-token mode has it).
   unsigned long long key = 0ull;
-  for (int base = 0; base < nn; base += rows_per_pass) {
-    const int i = base + tid / Wp;
-    const uint64_t mw = row_word(i, nn);
-    int badw = (mw & ~(mw ? match_w[w] : 0ull)) != 0ull;
-    int len = __popcll(mw);
-    for (int o = Wp >> 1; o > 0; o >>= 1) {
-      badw |= __shfl_xor(badw, o);
-      len += __shfl_xor(len, o);
-    }
+  scan_rows([&](int i, uint64_t mw) {
+    const bool badw = seg_any((mw & ~(mw ? match_w[w] : 0ull)) != 0ull, Wp);
+    const int len = seg_sum(__popcll(mw), Wp);
+    if (!NEXT && i < nn && w == 0) dep[i] = len - 1;
     if (i < nn && w == 0 && !badw && len > 0) {
       const unsigned long long k = ((unsigned long long)len << 32) | (0xffffffffu - (uint32_t)i);
       key = k > key ? k : key;
     }
-  }
+  });
   key = wave_max_u64(key);
   if (lane == 0) red[wave] = key;
   __syncthreads();
