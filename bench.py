@@ -68,6 +68,10 @@ def parse():
     p.add_argument("--summarize-ceiling", metavar="FILE",
                    help="write profiles/hbm_ceiling.md and profiles/launch_floor.md from the "
                         "--hbm-ceiling output in FILE")
+    p.add_argument("--compute-ceiling", action="store_true",
+                   help="time the MFMA and VALU rate probes and print one JSON line")
+    p.add_argument("--summarize-compute", metavar="FILE",
+                   help="write profiles/compute_ceiling.md from the --compute-ceiling output in FILE")
     p.add_argument("--no-m3", action="store_true",
                    help="skip the one-node-tree variant of the workload")
     p.add_argument("--calib-copy", action="store_true",
@@ -144,7 +148,81 @@ def _probes():
                                   ctypes.c_void_p]
     lib.ta_probe_empty.restype = ctypes.c_int
     lib.ta_probe_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.ta_probe_mfma.restype = ctypes.c_int
+    lib.ta_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ta_probe_valu.restype = ctypes.c_int
+    lib.ta_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p]
     return lib
+
+
+COMPUTE_CEILING_CMD = "python -u bench.py --compute-ceiling > gpurun_out/compute_ceiling.json"
+SIMDS, CLOCK_HZ = 256 * 4, 2.4e9   # MI355X: 256 CUs of 4 SIMDs, 2.4 GHz
+
+
+def compute_ceiling():
+    """Sustained matrix and vector rates: 512 workgroups of 8 waves (two per
+    SIMD) running independent v_mfma_f32_32x32x16_bf16 chains, fp32 FMA chains
+    and exp2 chains; HIP events around one launch each (after a warm-up)."""
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    probes = _probes()
+    stream = torch.cuda.current_stream(dev)
+    grid = 512
+    sink = torch.zeros(grid, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3
+
+    def check(rc, what):
+        if rc:
+            raise SystemExit(f"{what} failed ({rc})")
+
+    out = {}
+    iters = 4096
+    t = timed(lambda: check(probes.ta_probe_mfma(grid, iters, sink.data_ptr(), stream.cuda_stream),
+                            "ta_probe_mfma"))
+    flops = grid * 8 * 4 * iters * 32768
+    out["mfma_bf16_32x32x16"] = {"s": t, "TFLOPs": round(flops / t / 1e12, 1),
+                                 "frac_of_2500": round(flops / t / 2.5e15, 3),
+                                 "cycles_per_mfma_per_simd": round(SIMDS * CLOCK_HZ * t /
+                                                                   (grid * 8 * 4 * iters), 2)}
+    for op, name in ((0, "fma_f32"), (1, "exp2_f32")):
+        iters = 16384
+        t = timed(lambda: check(probes.ta_probe_valu(grid, iters, op, sink.data_ptr(),
+                                                     stream.cuda_stream), "ta_probe_valu"))
+        instr = grid * 8 * 8 * iters   # wave64 instructions
+        out[name] = {"s": t, "wave_instr_per_s": instr / t,
+                     "cycles_per_wave_instr_per_simd": round(SIMDS * CLOCK_HZ * t / instr, 2)}
+    print(json.dumps({"compute_ceiling": out}))
+
+
+def summarize_compute(path):
+    with open(path) as f:
+        rec = json.loads(f.read().strip().splitlines()[-1])["compute_ceiling"]
+    m, fma, ex = rec["mfma_bf16_32x32x16"], rec["fma_f32"], rec["exp2_f32"]
+    lines = ["# Matrix and vector rates on the MI355X box", "",
+             "Command (repository root, MI355X box):", "", "    " + COMPUTE_CEILING_CMD, "",
+             "Probes in `csrc/probes.hip` (`libtaprobes.so`): 512 workgroups of 8 waves (two per "
+             "SIMD), each wave running independent dependency chains; one launch timed with HIP "
+             "events after a warm-up; cycles per instruction per SIMD at 2.4 GHz over 1024 SIMDs.",
+             "", "| probe | rate | cycles per wave instruction per SIMD |", "|---|---|---|",
+             f"| `v_mfma_f32_32x32x16_bf16`, 4 chains per wave | {m['TFLOPs']} TFLOP/s "
+             f"({m['frac_of_2500']} of 2.5 PFLOP/s) | {m['cycles_per_mfma_per_simd']} |",
+             f"| fp32 FMA, 8 chains per thread | {fma['wave_instr_per_s'] / 1e12:.2f} T wave "
+             f"instr/s | {fma['cycles_per_wave_instr_per_simd']} |",
+             f"| `v_exp_f32` (exp2), 8 chains per thread | {ex['wave_instr_per_s'] / 1e12:.2f} T wave "
+             f"instr/s | {ex['cycles_per_wave_instr_per_simd']} |"]
+    with open(os.path.join(PROFILES, "compute_ceiling.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def hbm_ceiling():
@@ -595,6 +673,12 @@ def main():
         return
     if args.hbm_ceiling:
         hbm_ceiling()
+        return
+    if args.compute_ceiling:
+        compute_ceiling()
+        return
+    if args.summarize_compute:
+        summarize_compute(args.summarize_compute)
         return
     if args.summarize_ceiling:
         summarize_ceiling(args.summarize_ceiling, os.path.join(
