@@ -84,6 +84,31 @@ def test_large_forward_bf16_sampled_at_the_limit(ta):
     check_attention(out[nodes], lse[nodes], ref_o, ref_l, fp32=False, what="bf16 N=4096 sampled")
 
 
+@pytest.mark.parametrize("order", ["root_first", "leaf_first"])
+@pytest.mark.parametrize("Hkv", [1, 2])
+def test_large_forward_chain_gathered_and_dense_splits(ta, order, Hkv):
+    """A 4096-node chain: a workgroup's rows near the root see few tree keys
+    (listed and gathered), those near the leaf see thousands (more than the
+    key list holds, so the split walks the dense tree tiles that hold a
+    visible key); both kinds of split in one call, on the 128-row two-key-
+    group shape (one KV head) and the 256-row shape (two).  Leaf first lists
+    every parent after its child."""
+    n = 4096
+    chain = [-1] + list(range(n - 1)) if order == "root_first" else list(range(1, n)) + [-1]
+    c = synthetic.make_case("lchainf", prefix_lens=[100], trees=[chain], Hq=4 * Hkv, Hkv=Hkv,
+                            D=128, seed=8 + Hkv)
+    dc, mask = _check_mask(ta, c)
+    out, lse = gpu_forward(ta, dc, mask)
+    rng = np.random.default_rng(9)
+    nodes = sorted(set(range(40)) | set(range(n - 40, n)) | set(range(2000, 2100)) |
+                   set(rng.choice(n, 120, replace=False).tolist()))
+    ref_o, ref_l = oracle.tree_attention(c.q, c.k_tree, c.v_tree, c.k_prefix, c.v_prefix,
+                                         c.parents, c.node_offsets, c.prefix_offsets, c.scale,
+                                         nodes=nodes)
+    check_attention(out[nodes], lse[nodes], ref_o, ref_l, fp32=False,
+                    what=f"bf16 chain {order} Hkv={Hkv}")
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_large_forward_full(ta, dtype):
     D = 128 if dtype == torch.bfloat16 else 64

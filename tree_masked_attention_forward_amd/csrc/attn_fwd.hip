@@ -662,62 +662,174 @@ void fwd_bf16_kernel(KParams P) {
   const int Lt = rgn.Lt;
   const int row0 = r * P.rows_wg;
 
-  // Block-sparse tree tiles (SKIP: above 128 nodes, mask rows read from
-  // memory): a split keeps only the tree tiles in which some row of the
-  // workgroup sees a key, the OR of those rows' mask dwords over the tile.  The split's
-  // bounds stay those of the dense tile range (every split of a row tile,
-  // and the merge, agree on them without reading the mask); its loop walks
-  // its prefix tiles, then the kept tree tiles, listed in LDS.  A split left
-  // with no tile still runs one (masked) iteration, so its query and stage
-  // loads are waited for before it ends.
+  // Sparse tree keys (SKIP: above 128 nodes, mask rows read from memory).
+  // A split's tree keys are those of its dense tree tiles; it needs only the
+  // ones some row of the workgroup sees: the union of those rows' ancestor
+  // sets.  Gather mode lists that union in LDS (s_keys, ascending) and walks
+  // it in 32-key tiles whose K/V rows are loaded through the list, with each
+  // row's visibility bits for each gathered tile precomputed in LDS
+  // (s_gbits); when the union or the bits would not fit, the split keeps
+  // instead the dense tree tiles in which some row sees a key (tile
+  // compaction, s_tt).  The split's bounds stay those of the dense tile range
+  // (every split of a row tile, and the merge, agree on them without reading
+  // the mask); its loop walks its prefix tiles, then the gathered or kept
+  // tiles.  A split left with no tile still runs one (masked) iteration, so
+  // its query and stage loads are waited for before it ends.
+  constexpr int kGatherMaxKeys = 2048;
+  constexpr int kGatherBitWords = 2048;
+  constexpr int kGath = 1 << 24;   // gathered tile t is walked as "tile" kGath + t
   __shared__ int s_tt[TA_MAX_NODES / kKT];
   __shared__ unsigned char s_act[TA_MAX_NODES / kKT];
   __shared__ int s_nact;
+  __shared__ unsigned long long s_u[TA_MAX_NODES / 64];
+  __shared__ int s_ust[TA_MAX_NODES / 64];
+  __shared__ int16_t s_keys[kGatherMaxKeys];
+  __shared__ uint32_t s_gbits[kGatherBitWords];
+  __shared__ int s_ng;
   int n_pre = t_hi - t_lo;   // tiles walked in order from t_lo
   int n_act = 0;             // kept tree tiles after them (compact mode)
-  bool compact = false;
+  int n_gt = 0;              // gathered tiles after them (gather mode)
+  int n_g = 0;               // gathered keys
+  int g_lo = 0;              // the workgroup's first node (rows of s_gbits)
+  bool compact = false, gather = false;
   if constexpr (SKIP && !MR) {
     if (sq.nn > 128 && t_hi > Lt) {
-      compact = true;
       const int ta0 = max(t_lo, Lt) - Lt;   // the split's tree tiles: [ta0, ta0 + nt)
       const int nt = t_hi - Lt - ta0;
       n_pre = max(0, min(t_hi, Lt) - t_lo);
-      for (int k = tid; k < nt; k += NT) s_act[k] = 0;
-      __syncthreads();
       const int n_lo = row0 / P.G;
-      const int per = NT / nt;   // threads per tile (nt <= 128 <= NT)
-      if (tid < per * nt) {
-        const int k = tid % nt;
-        uint32_t acc = 0u;
-#pragma unroll 8
-        for (int n = n_lo + tid / nt; n <= rgn.n_hi; n += per)
-          acc |= reinterpret_cast<const uint32_t*>(P.mask + (size_t)(sq.n0 + n) * P.W)[ta0 + k];
-        if (acc) s_act[k] = 1;
+      const int nodes = rgn.n_hi - n_lo + 1;
+      const uint64_t* mrows = P.mask + (size_t)(sq.n0 + n_lo) * P.W;
+      // Keys [k_lo, k_hi) of those tiles lie in mask words [w_lo, w_lo + nw).
+      const int k_lo = ta0 * kKT;
+      const int k_hi = min(sq.nn, (ta0 + nt) * kKT);
+      const int w_lo = k_lo / 64;
+      const int nw = (k_hi + 63) / 64 - w_lo;
+      for (int w = tid; w < nw; w += NT) s_u[w] = 0ull;
+      __syncthreads();
+      // Union of the rows' words, four loads in flight per thread.
+      const int total = nodes * nw;
+      for (int q0 = 0; q0 < total; q0 += NT * 4) {
+        uint64_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = min(q0 + u * NT + tid, total - 1);
+          v[u] = mrows[(size_t)(q / nw) * P.W + w_lo + q % nw];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = q0 + u * NT + tid;
+          if (q < total && v[u]) atomicOr(&s_u[q % nw], (unsigned long long)v[u]);
+        }
       }
       __syncthreads();
+      // Clip to [k_lo, k_hi); key positions: an exclusive scan of popcounts.
       if (wave == 0) {
         int base = 0;
-        for (int k0 = 0; k0 < nt; k0 += 64) {
-          const int k = k0 + lane;
-          const bool act = k < nt && s_act[k] != 0;
-          const uint64_t bal = __ballot(act);
-          if (act) s_tt[base + __popcll(bal & ((1ull << lane) - 1ull))] = ta0 + k;
-          base += __popcll(bal);
+        for (int w0 = 0; w0 < nw; w0 += 64) {
+          const int w = w0 + lane;
+          uint64_t v = 0ull;
+          if (w < nw) {
+            v = s_u[w];
+            const int lo = 64 * (w_lo + w);
+            if (lo < k_lo) v &= ~0ull << (k_lo - lo);
+            if (k_hi - lo < 64) v &= (1ull << (k_hi - lo)) - 1ull;
+            s_u[w] = v;
+          }
+          const int c = __popcll(v);
+          int incl = c;
+          for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o);
+            if (lane >= o) incl += t;
+          }
+          if (w < nw) s_ust[w] = base + incl - c;
+          base += __shfl(incl, 63);
         }
-        if (lane == 0) s_nact = base;
+        if (lane == 0) s_ng = base;
       }
       __syncthreads();
-      n_act = s_nact;
+      n_g = __builtin_amdgcn_readfirstlane(s_ng);
+      n_gt = (n_g + kKT - 1) / kKT;
+      gather = n_g <= kGatherMaxKeys && nodes * n_gt <= kGatherBitWords;
+      if (gather) {
+        g_lo = n_lo;
+        // The key list: a wave per word, a lane per bit.
+        for (int w = wave; w < nw; w += NW) {
+          const uint64_t v = s_u[w];
+          if ((v >> lane) & 1ull)
+            s_keys[s_ust[w] + __popcll(v & ((1ull << lane) - 1ull))] =
+                (int16_t)(64 * (w_lo + w) + lane);
+        }
+        for (int q = tid; q < nodes * n_gt; q += NT) s_gbits[q] = 0u;
+        __syncthreads();
+        // Visibility bits: for each (row node, word) pair, each key the node
+        // sees in the word (a node sees few keys, so few steps) set at its
+        // position in the list: the word's start plus the union's bits below.
+        for (int q0 = 0; q0 < total; q0 += NT * 4) {
+          uint64_t v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int q = min(q0 + u * NT + tid, total - 1);
+            v[u] = mrows[(size_t)(q / nw) * P.W + w_lo + q % nw];
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int q = q0 + u * NT + tid;
+            if (q >= total) continue;
+            const int nd = q / nw;
+            const int w = q % nw;
+            const uint64_t uu = s_u[w];
+            uint64_t vv = v[u] & uu;
+            while (vv) {
+              const int b = __builtin_ctzll(vv);
+              vv &= vv - 1ull;
+              const int pos = s_ust[w] + __popcll(uu & ((1ull << b) - 1ull));
+              atomicOr(&s_gbits[nd * n_gt + (pos >> 5)], 1u << (pos & 31));
+            }
+          }
+        }
+        __syncthreads();
+      } else {
+        compact = true;
+        for (int k = tid; k < nt; k += NT) s_act[k] = 0;
+        __syncthreads();
+        const int per = NT / nt;   // threads per tile (nt <= 128 <= NT)
+        if (tid < per * nt) {
+          const int k = tid % nt;
+          uint32_t acc = 0u;
+#pragma unroll 8
+          for (int n = n_lo + tid / nt; n <= rgn.n_hi; n += per)
+            acc |= reinterpret_cast<const uint32_t*>(P.mask + (size_t)(sq.n0 + n) * P.W)[ta0 + k];
+          if (acc) s_act[k] = 1;
+        }
+        __syncthreads();
+        if (wave == 0) {
+          int base = 0;
+          for (int k0 = 0; k0 < nt; k0 += 64) {
+            const int k = k0 + lane;
+            const bool act = k < nt && s_act[k] != 0;
+            const uint64_t bal = __ballot(act);
+            if (act) s_tt[base + __popcll(bal & ((1ull << lane) - 1ull))] = ta0 + k;
+            base += __popcll(bal);
+          }
+          if (lane == 0) s_nact = base;
+        }
+        __syncthreads();
+        n_act = __builtin_amdgcn_readfirstlane(s_nact);
+      }
     }
   }
-  const int n_log = max(1, n_pre + n_act);
-  // Tile of the split's li-th step: prefix tiles in order, then the kept tree
-  // tiles; past the end, t_hi (loaded in bounds, masked as inactive).
+  const int n_log = max(1, n_pre + (gather ? n_gt : n_act));
+  // Tile of the split's li-th step: prefix tiles in order, then the gathered
+  // or kept tree tiles; past the end, t_hi (loaded in bounds, masked as
+  // inactive).
   auto phys = [&](int li) -> int {
-    if (!SKIP || !compact || li < n_pre) return t_lo + li;
+    if (!SKIP || (!compact && !gather) || li < n_pre) return t_lo + li;
+    if (gather) return li < n_pre + n_gt ? kGath + (li - n_pre) : t_hi;
     if (li < n_pre + n_act) return __builtin_amdgcn_readfirstlane(Lt + s_tt[li - n_pre]);
     return t_hi;
   };
+  auto is_active = [&](int tile) { return tile < t_hi || (SKIP && tile >= kGath); };
 
   // This lane's query row.
   const int my_row = row0 + rg * 32 + l32;
@@ -796,7 +908,15 @@ void fwd_bf16_kernel(KParams P) {
       for (int u = 0; u < kPasses; ++u) {
         const uint16_t* gk;
         const uint16_t* gv;
-        if (tile < L_full) {
+        if (SKIP && tile >= kGath) {
+          // Gathered tile: row `row` holds listed key 32 * (tile - kGath) + row
+          // (node 0 past the list's end; its scores are masked).
+          const int row = ld_key + kRowsPerPass * u;
+          const int idx = kKT * (tile - kGath) + row;
+          const size_t off = (size_t)(idx < n_g ? (int)s_keys[idx] : 0) * kv_row;
+          gk = kt + off + ((ld_slot ^ (row & 15)) << 3);
+          gv = vt + off + ((ld_slot ^ ((row & 3) << 2)) << 3);
+        } else if (tile < L_full) {
           gk = pk[u] + (size_t)tile * tile_stride;
           gv = pv[u] + (size_t)tile * tile_stride;
         } else {
@@ -1112,7 +1232,7 @@ void fwd_bf16_kernel(KParams P) {
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
       tl[j] = phys((it * KG + kg) * TPW + j);
-      ac[j] = group_active && tl[j] < t_hi;
+      ac[j] = group_active && is_active(tl[j]);
       // Unconditional, so the MFMA chains of the wave's tiles share one basic
       // block (an idle tile's scores come from in-bounds rows and are dropped).
       sc[j] = qk(st + (kg * TPW + j) * kTileBytes);
@@ -1126,6 +1246,8 @@ void fwd_bf16_kernel(KParams P) {
       if constexpr (MR) {
         const int d = tl[j] - Lt;   // uniform; only tree tiles (d >= 0) use the bits
         mbits = d <= 0 ? mw[0] : d == 1 ? mw[1] : d == 2 ? mw[2] : mw[3];
+      } else if (SKIP && tl[j] >= kGath) {
+        mbits = row_ok ? s_gbits[(node - g_lo) * n_gt + (tl[j] - kGath)] : 0u;
       } else {
         mbits = *reinterpret_cast<const uint32_t*>(st + kMaskOff + (wave * TPW + j) * 256 +
                                                    lane * 4);
