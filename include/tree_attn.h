@@ -258,6 +258,9 @@ TA_API int tree_attn_mask_and_forward(int dtype, const int32_t* parents, const v
 
 /*
  * Bytes of device workspace tree_verify_greedy needs.  Pure host arithmetic.
+ * total_nodes: the logits rows (sum_N; sum_N + B for tree_verify_greedy_next);
+ * max_nodes: as passed to the call (above 1024 the size includes the
+ * many-workgroup path selection's scratch).  0 for no rows.
  */
 TA_API size_t tree_verify_greedy_workspace_size(int32_t total_nodes, int32_t max_nodes, int32_t V);
 
@@ -288,7 +291,12 @@ TA_API size_t tree_verify_greedy_workspace_size(int32_t total_nodes, int32_t max
  *   accept_nodes   out int32 [B][max_nodes]: local node ids, root first, padded
  *                  with -1.
  *   accept_tokens  out int32 [B][max_nodes]: their draft tokens, padded with -1.
- *   workspace      at least tree_verify_greedy_workspace_size() bytes.
+ *   workspace      at least tree_verify_greedy_workspace_size() bytes (it
+ *                  grows by 24 bytes per node when max_nodes > 1024, where the
+ *                  path selection runs over many workgroups and keeps
+ *                  per-node scratch there).
+ * Sequences must not overlap (node_offsets non-decreasing); a sequence whose
+ * offsets do not decode is treated as empty (accept_len 0).
  */
 TA_API int tree_verify_greedy(int logits_dtype, const void* logits, const int32_t* draft_tokens,
                        const uint64_t* mask, const int32_t* node_offsets, int32_t B,

@@ -313,9 +313,8 @@ int tree_attn_mask_and_forward(int dtype, const int32_t* parents, const void* q,
 }
 
 size_t tree_verify_greedy_workspace_size(int32_t total_nodes, int32_t max_nodes, int32_t V) {
-  (void)max_nodes;
-  if (total_nodes <= 0 || V <= 0) return 0;
-  return ta::plan_verify(total_nodes, V).ws_bytes;
+  if (total_nodes <= 0 || V <= 0 || max_nodes < 1) return 0;
+  return ta::plan_verify(total_nodes, V, max_nodes).ws_bytes;
 }
 
 int tree_verify_greedy(int logits_dtype, const void* logits, const int32_t* draft_tokens,
@@ -329,7 +328,7 @@ int tree_verify_greedy(int logits_dtype, const void* logits, const int32_t* draf
   if (max_nodes > TA_MAX_NODES) return TA_ERR_UNSUPPORTED;
   if (!node_offsets || !accept_len || !accept_nodes || !accept_tokens) return TA_ERR_INVALID_ARG;
   if (total_nodes > 0 && (!logits || !draft_tokens || !mask)) return TA_ERR_INVALID_ARG;
-  const ta::VerifyPlan p = ta::plan_verify(total_nodes, V);
+  const ta::VerifyPlan p = ta::plan_verify(total_nodes, V, max_nodes);
   if (total_nodes > 0 && (!workspace || workspace_bytes < p.ws_bytes || misaligned16(workspace)))
     return TA_ERR_WORKSPACE;
   return hip_status(ta::launch_verify(logits_dtype == TA_BF16, logits, draft_tokens, mask,
@@ -352,7 +351,7 @@ int tree_verify_greedy_next(int logits_dtype, const void* logits, const void* ro
       !root_logits)
     return TA_ERR_INVALID_ARG;
   if (total_nodes > 0 && (!logits || !draft_tokens || !mask)) return TA_ERR_INVALID_ARG;
-  const ta::VerifyPlan p = ta::plan_verify(total_nodes + B, V);
+  const ta::VerifyPlan p = ta::plan_verify(total_nodes + B, V, max_nodes);
   if (!workspace || workspace_bytes < p.ws_bytes || misaligned16(workspace))
     return TA_ERR_WORKSPACE;
   return hip_status(ta::launch_verify(logits_dtype == TA_BF16, logits, draft_tokens, mask,

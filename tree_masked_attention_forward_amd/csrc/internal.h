@@ -89,12 +89,16 @@ hipError_t launch_forward_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t s
 hipError_t launch_forward_f32(const FwdArgs& a, hipStream_t stream);
 
 struct VerifyPlan {
-  int cpr;          // vocabulary chunks per logits row
-  int chunk;        // vocabulary entries per chunk (multiple of 8)
-  size_t ws_bytes;  // one (value, index) pair per (row, chunk)
+  int cpr;             // vocabulary chunks per logits row
+  int chunk;           // vocabulary entries per chunk (multiple of 8)
+  bool large;          // trees above kLdsTreeMaxNodes: many-workgroup path selection
+  size_t scratch_off;  // its scratch, after the chunk results (large only)
+  size_t ws_bytes;     // one (value, index) pair per (row, chunk), then the scratch
 };
 
-VerifyPlan plan_verify(int total_nodes, int V);
+// rows: logits rows (the node rows, plus one prefix row per sequence for
+// next-token verification).
+VerifyPlan plan_verify(int rows, int V, int max_nodes);
 
 hipError_t launch_verify(bool bf16, const void* logits, const int32_t* draft,
                          const uint64_t* mask, const int32_t* node_offsets, int B,

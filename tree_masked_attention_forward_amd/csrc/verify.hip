@@ -462,207 +462,295 @@ __global__ __launch_bounds__(kThreads) void path_select_kernel(
   }
 }
 
-// Trees above 1024 nodes (up to TA_MAX_NODES): the mask rows (W <= 64 words
-// each) stay in global memory and are read a whole row per Wp lanes, Wp = W
-// rounded up to a power of two.  The steps and the tie rules are those of
-// path_select_kernel: per-node argmax from the chunk results; for next-token
-// rows each node's parent (the highest set bit of its row below itself) into
-// LDS; the match set by ballots; then one more pass over the rows for the
-// accepted test and the path length; the best row's bits, placed by a prefix
-// sum of word popcounts, give the path.
-constexpr int kBigThreads = 1024;
+// Trees above 1024 nodes (up to TA_MAX_NODES): the path selection is spread
+// over many workgroups, each taking 64 rows of one sequence (Wp lanes per row,
+// Wp = the row's W words rounded up to a power of two, 32 or 64), with the
+// steps and tie rules of path_select_kernel:
+//   large_rows_kernel     per node: target argmax from its chunk results,
+//                         depth (row popcount minus one) and, for same-row
+//                         predictions, the match bit; a ballot packs each
+//                         64 nodes' bits into one word of the match set.
+//   large_parents_kernel  next-token rows only: per node the parent (its
+//                         deepest proper ancestor, depths from LDS) and the
+//                         match bit against the parent's (or the prefix's)
+//                         prediction.
+//   large_accept_kernel   per node: accepted iff its row lies inside the
+//                         match set; (length, lowest index) keys, one atomic
+//                         maximum per workgroup into the sequence's key.
+//   large_place_kernel    per sequence: the best node's row, each node placed
+//                         at its depth, and the outputs.
+// Scratch (node-indexed, so disjoint sequences never share an entry):
+// predictions, depths, match words (sequence word w of the sequence starting
+// at node n0 is stored at n0 + 64w) and keys (the sequence's at n0).
+constexpr int kLargeThreads = 1024;
+constexpr int kLargeRows = 64;   // rows per workgroup
+
+struct LargeScratch {
+  int32_t* tgt;
+  int32_t* dep;
+  uint64_t* match;
+  unsigned long long* key;
+};
+
+// Sequence b's first node and node count; nn = 0 when its offsets do not
+// decode (nothing accepted, as in path_select_kernel).
+__device__ inline void seq_range(const int32_t* node_offsets, int b, int total_nodes,
+                                 int max_nodes, int& n0, int& nn) {
+  n0 = node_offsets[b];
+  const int n1 = node_offsets[b + 1];
+  nn = n1 - n0;
+  if (n0 < 0 || nn < 0 || nn > max_nodes || n1 > total_nodes || max_nodes > TA_MAX_NODES) {
+    n0 = 0;
+    nn = 0;
+  }
+}
+
+// The match bits of the workgroup's 64 rows (flags in LDS), packed by wave 0
+// into the sequence's word c.
+__device__ inline void pack_match(const unsigned char* flag, uint64_t* match, int n0, int c,
+                                  int nn) {
+  if (threadIdx.x < 64) {
+    const int i = kLargeRows * c + (int)threadIdx.x;
+    const uint64_t bits = __ballot(i < nn && flag[threadIdx.x] != 0);
+    if (threadIdx.x == 0) match[n0 + kLargeRows * c] = bits;
+  }
+}
 
 template <bool NEXT>
-__global__ __launch_bounds__(kBigThreads) void path_select_large_kernel(
+__global__ __launch_bounds__(kLargeThreads) void large_rows_kernel(
     const float2* __restrict__ ws, int cpr, const int32_t* __restrict__ draft,
     const uint64_t* __restrict__ mask, const int32_t* __restrict__ node_offsets,
-    int total_nodes, int max_nodes, int W, int Wp, int32_t* __restrict__ target_argmax,
-    int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
-    int32_t* __restrict__ accept_tokens, const float2* __restrict__ ws_root,
-    int32_t* __restrict__ bonus_token) {
-  __shared__ int32_t tgt[TA_MAX_NODES];
-  __shared__ int32_t dep[TA_MAX_NODES];
-  __shared__ int32_t par[NEXT ? TA_MAX_NODES : 1];
-  __shared__ uint64_t match_w[TA_MAX_NODES / 64];
-  __shared__ unsigned long long red[kBigThreads / 64];
-  __shared__ int32_t root_pred;
-  const int b = blockIdx.x;
+    int total_nodes, int max_nodes, int W, int Wp, int chunks, int32_t* __restrict__ target_argmax,
+    LargeScratch sc) {
+  __shared__ unsigned char flag[kLargeRows];
+  const int b = blockIdx.x / chunks;
+  const int c = blockIdx.x % chunks;
+  int n0, nn;
+  seq_range(node_offsets, b, total_nodes, max_nodes, n0, nn);
+  if (kLargeRows * c >= nn) return;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int n0 = node_offsets[b];
-  const int n1 = node_offsets[b + 1];
-  int nn = n1 - n0;
-  if (n0 < 0 || nn < 0 || nn > max_nodes || n1 > total_nodes || max_nodes > TA_MAX_NODES)
-    nn = 0;   // nothing accepted
-
-  // Target argmax per node: a node's cpr chunk results sit in cpr
-  // consecutive lanes (cpr a power of two <= 64); ties -> lowest index.
-  // Every scan below requests kScanBatch passes' loads before using any, so
-  // one workgroup walks 4096 rows in a few dozen round trips, not hundreds.
-  constexpr int kPairBatch = 4;
-  const int pairs = nn * cpr;
-  for (int p0 = 0; p0 < pairs; p0 += kBigThreads * kPairBatch) {
-    float2 x[kPairBatch];
+  const int w = tid & (Wp - 1);
+  const int rpp = kLargeThreads / Wp;   // rows per pass
+  const int passes = kLargeRows / rpp;  // 2 or 4
+  constexpr int kMaxPasses = 4;
+  // Every load first: the rows' mask words, each lane's chunk results (lane w
+  // takes chunks w and w + Wp), and the draft token; rows past the sequence
+  // re-read its last row and are dropped below.
+  uint64_t mw[kMaxPasses];
+  float2 x0[kMaxPasses], x1[kMaxPasses];
+  int32_t d[kMaxPasses];
 #pragma unroll
-    for (int u = 0; u < kPairBatch; ++u) {
-      const int pidx = p0 + u * kBigThreads + tid;
-      x[u] = pidx < pairs ? ws[(size_t)n0 * cpr + pidx] : make_float2(kNegInf, 0.f);
-    }
-#pragma unroll
-    for (int u = 0; u < kPairBatch; ++u) {
-      const int pidx = p0 + u * kBigThreads + tid;
-      float bv = kNegInf;
-      int bi = 0x7fffffff;
-      if (pidx < pairs) {
-        bv = x[u].x;
-        bi = __float_as_int(x[u].y);
-      }
-      seg_best(bv, bi, cpr);
-      if (pidx < pairs && (pidx & (cpr - 1)) == 0) {
-        tgt[pidx / cpr] = bi;
-        if (target_argmax) target_argmax[n0 + pidx / cpr] = bi;
-      }
-    }
+  for (int u = 0; u < kMaxPasses; ++u) {
+    if (u >= passes) break;
+    const int i = min(kLargeRows * c + u * rpp + tid / Wp, nn - 1);
+    mw[u] = mask[(size_t)(n0 + i) * W + (w < W ? w : 0)];
+    const float2* xr = ws + (size_t)(n0 + i) * cpr;
+    x0[u] = xr[w < cpr ? w : 0];
+    x1[u] = xr[w + Wp < cpr ? w + Wp : 0];
+    d[u] = draft[n0 + i];
   }
-  if (NEXT && wave == 0) {
+  const uint64_t keep =
+      64 * w + 64 <= nn ? ~0ull : (64 * w < nn ? (1ull << (nn - 64 * w)) - 1ull : 0ull);
+#pragma unroll
+  for (int u = 0; u < kMaxPasses; ++u) {
+    if (u >= passes) break;
+    const int i = kLargeRows * c + u * rpp + tid / Wp;
+    const int len = seg_sum(__popcll(w < W ? (mw[u] & keep) : 0ull), Wp);
     float bv = kNegInf;
     int bi = 0x7fffffff;
-    if (lane < cpr) {
-      const float2 x = ws_root[(size_t)b * cpr + lane];
+    if (w < cpr) {
+      bv = x0[u].x;
+      bi = __float_as_int(x0[u].y);
+    }
+    if (w + Wp < cpr && better(x1[u].x, __float_as_int(x1[u].y), bv, bi)) {
+      bv = x1[u].x;
+      bi = __float_as_int(x1[u].y);
+    }
+    seg_best(bv, bi, Wp);
+    if (w == 0 && i < nn) {
+      sc.dep[n0 + i] = len - 1;
+      sc.tgt[n0 + i] = bi;
+      if (target_argmax) target_argmax[n0 + i] = bi;
+      flag[i - kLargeRows * c] = !NEXT && d[u] == bi;
+    }
+  }
+  if (c == 0 && tid == 0) sc.key[n0] = 0ull;
+  if constexpr (!NEXT) {
+    __syncthreads();
+    pack_match(flag, sc.match, n0, c, nn);
+  }
+}
+
+__device__ inline void large_root_pred(const float2* ws_root, int b, int cpr, int32_t* out) {
+  // Wave 0: the prefix row's prediction (its chunk results, ties -> lowest
+  // index) into *out.
+  if (threadIdx.x < 64) {
+    float bv = kNegInf;
+    int bi = 0x7fffffff;
+    if ((int)threadIdx.x < cpr) {
+      const float2 x = ws_root[(size_t)b * cpr + threadIdx.x];
       bv = x.x;
       bi = __float_as_int(x.y);
     }
     wave_best(bv, bi);
-    if (lane == 0) root_pred = bi;
+    if (threadIdx.x == 0) *out = bi;
   }
+}
 
+__global__ __launch_bounds__(kLargeThreads) void large_parents_kernel(
+    const int32_t* __restrict__ draft, const uint64_t* __restrict__ mask,
+    const int32_t* __restrict__ node_offsets, int total_nodes, int max_nodes, int W, int Wp,
+    int chunks, const float2* __restrict__ ws_root, int cpr, LargeScratch sc) {
+  __shared__ int32_t dep[TA_MAX_NODES];
+  __shared__ unsigned char flag[kLargeRows];
+  __shared__ int32_t root_pred;
+  const int b = blockIdx.x / chunks;
+  const int c = blockIdx.x % chunks;
+  int n0, nn;
+  seq_range(node_offsets, b, total_nodes, max_nodes, n0, nn);
+  if (kLargeRows * c >= nn) return;
+  const int tid = threadIdx.x;
+  for (int j = tid; j < nn; j += kLargeThreads) dep[j] = sc.dep[n0 + j];
+  large_root_pred(ws_root, b, cpr, &root_pred);
   const int w = tid & (Wp - 1);
-  const int rows_per_pass = kBigThreads / Wp;
-  // Word w of row i, with the bits at or above `lim` cleared.
-  auto row_word = [&](int i, int lim) -> uint64_t {
-    if (i >= nn || w >= W || 64 * w >= lim) return 0ull;
-    uint64_t mw = mask[(size_t)(n0 + i) * W + w];
-    if (lim - 64 * w < 64) mw &= (1ull << (lim - 64 * w)) - 1ull;
-    return mw;
-  };
-  // Row scans: kScanBatch passes of rows_per_pass rows each per step, the
-  // words of all of them requested first.
-  constexpr int kScanBatch = 16;
-  // The loads are branch-free (rows past the end re-read the sequence's
-  // first row and are zeroed after), so all of a step's loads are issued
-  // before the first is used.
-  const bool w_in = w < W;
-  const uint64_t w_keep = 64 * w + 64 <= nn ? ~0ull : (64 * w < nn ? (1ull << (nn - 64 * w)) - 1ull : 0ull);
-  auto scan_rows = [&](auto&& visit) {
-    for (int base = 0; base < nn; base += rows_per_pass * kScanBatch) {
-      uint64_t mw[kScanBatch];
+  const int rpp = kLargeThreads / Wp;
+  const int passes = kLargeRows / rpp;
+  constexpr int kMaxPasses = 4;
+  uint64_t mw[kMaxPasses];
+  int32_t d[kMaxPasses];
 #pragma unroll
-      for (int u = 0; u < kScanBatch; ++u) {
-        const int i = base + u * rows_per_pass + tid / Wp;
-        mw[u] = mask[(size_t)(n0 + min(i, nn - 1)) * W + (w_in ? w : 0)];
-      }
+  for (int u = 0; u < kMaxPasses; ++u) {
+    if (u >= passes) break;
+    const int i = min(kLargeRows * c + u * rpp + tid / Wp, nn - 1);
+    mw[u] = mask[(size_t)(n0 + i) * W + (w < W ? w : 0)];
+    d[u] = draft[n0 + i];
+  }
+  const uint64_t keep =
+      64 * w + 64 <= nn ? ~0ull : (64 * w < nn ? (1ull << (nn - 64 * w)) - 1ull : 0ull);
+  __syncthreads();
 #pragma unroll
-      for (int u = 0; u < kScanBatch; ++u) {
-        const int i = base + u * rows_per_pass + tid / Wp;
-        mw[u] = (i < nn && w_in) ? (mw[u] & w_keep) : 0ull;
-      }
-#pragma unroll
-      for (int u = 0; u < kScanBatch; ++u) visit(base + u * rows_per_pass + tid / Wp, mw[u]);
+  for (int u = 0; u < kMaxPasses; ++u) {
+    if (u >= passes) break;
+    const int i = kLargeRows * c + u * rpp + tid / Wp;
+    // The deepest proper ancestor, as (depth, index) packed for one maximum.
+    uint64_t m = w < W ? (mw[u] & keep) : 0ull;
+    if ((i >> 6) == w) m &= ~(1ull << (i & 63));
+    int best = -1;
+    while (m) {
+      const int j = 64 * w + __builtin_ctzll(m);
+      m &= m - 1ull;
+      best = max(best, (dep[j] << 16) | j);
     }
-  };
-  if constexpr (NEXT) {
-    // Depth of every node (its row's popcount minus one: a node's position
-    // on any root path, in whatever order the nodes are listed), then the
-    // parent of i: its deepest proper ancestor, as (depth, index) packed for
-    // one max over the row's lanes.
-    scan_rows([&](int i, uint64_t mw) {
-      const int c = seg_sum(__popcll(mw), Wp);
-      if (i < nn && w == 0) dep[i] = c - 1;
-    });
-    __syncthreads();
-    scan_rows([&](int i, uint64_t mw) {
-      if (i < nn && (i >> 6) == w) mw &= ~(1ull << (i & 63));
-      int best = -1;
-      while (mw) {
-        const int j = 64 * w + __builtin_ctzll(mw);
-        mw &= mw - 1ull;
-        best = max(best, (dep[j] << 16) | j);
-      }
-      best = seg_max(best, Wp);
-      if (i < nn && w == 0) par[i] = best >= 0 ? (best & 0xffff) : -1;
-    });
+    best = seg_max(best, Wp);
+    if (w == 0 && i < nn) {
+      const int e = best >= 0 ? sc.tgt[n0 + (best & 0xffff)] : root_pred;
+      flag[i - kLargeRows * c] = d[u] == e;
+    }
   }
   __syncthreads();
+  pack_match(flag, sc.match, n0, c, nn);
+}
 
-  // Match set: node i matches iff its draft token is the prediction it is
-  // checked against; wave w's ballot over nodes base + 64w .. is one word.
-  for (int base = 0; base < nn; base += kBigThreads) {
-    const int i = base + tid;
-    bool m = false;
-    if (i < nn) {
-      int e;
-      if constexpr (NEXT) e = par[i] >= 0 ? tgt[par[i]] : root_pred;
-      else e = tgt[i];
-      m = draft[n0 + i] == e;
-    }
-    const uint64_t bits = __ballot(m);
-    if (lane == 0 && base + 64 * wave < nn) match_w[(base >> 6) + wave] = bits;
+__global__ __launch_bounds__(kLargeThreads) void large_accept_kernel(
+    const uint64_t* __restrict__ mask, const int32_t* __restrict__ node_offsets, int total_nodes,
+    int max_nodes, int W, int Wp, int chunks, LargeScratch sc) {
+  __shared__ uint64_t match_w[TA_MAX_NODES / 64];
+  __shared__ unsigned long long red[kLargeThreads / 64];
+  const int b = blockIdx.x / chunks;
+  const int c = blockIdx.x % chunks;
+  int n0, nn;
+  seq_range(node_offsets, b, total_nodes, max_nodes, n0, nn);
+  if (kLargeRows * c >= nn) return;
+  const int tid = threadIdx.x;
+  if (tid < W && 64 * tid < nn) match_w[tid] = sc.match[n0 + 64 * tid];
+  const int w = tid & (Wp - 1);
+  const int rpp = kLargeThreads / Wp;
+  const int passes = kLargeRows / rpp;
+  constexpr int kMaxPasses = 4;
+  uint64_t mw[kMaxPasses];
+#pragma unroll
+  for (int u = 0; u < kMaxPasses; ++u) {
+    if (u >= passes) break;
+    const int i = min(kLargeRows * c + u * rpp + tid / Wp, nn - 1);
+    mw[u] = mask[(size_t)(n0 + i) * W + (w < W ? w : 0)];
   }
+  const uint64_t keep =
+      64 * w + 64 <= nn ? ~0ull : (64 * w < nn ? (1ull << (nn - 64 * w)) - 1ull : 0ull);
   __syncthreads();
-
   // Accepted iff the row (cut at nn) lies inside the match set; the longest
-  // accepted path wins, lowest index on ties.  The same scan leaves every
-  // node's depth for the placement below (the next-token mode has it).
+  // accepted path wins, lowest index on ties.
   unsigned long long key = 0ull;
-  scan_rows([&](int i, uint64_t mw) {
-    const bool badw = seg_any((mw & ~(mw ? match_w[w] : 0ull)) != 0ull, Wp);
-    const int len = seg_sum(__popcll(mw), Wp);
-    if (!NEXT && i < nn && w == 0) dep[i] = len - 1;
-    if (i < nn && w == 0 && !badw && len > 0) {
+#pragma unroll
+  for (int u = 0; u < kMaxPasses; ++u) {
+    if (u >= passes) break;
+    const int i = kLargeRows * c + u * rpp + tid / Wp;
+    const uint64_t m = w < W ? (mw[u] & keep) : 0ull;
+    const bool bad = seg_any((m & ~(m ? match_w[w] : 0ull)) != 0ull, Wp);
+    const int len = seg_sum(__popcll(m), Wp);
+    if (i < nn && w == 0 && !bad && len > 0) {
       const unsigned long long k = ((unsigned long long)len << 32) | (0xffffffffu - (uint32_t)i);
       key = k > key ? k : key;
     }
-  });
+  }
   key = wave_max_u64(key);
-  if (lane == 0) red[wave] = key;
+  if ((tid & 63) == 0) red[tid >> 6] = key;
   __syncthreads();
-  key = red[0];
-  for (int k = 1; k < kBigThreads / 64; ++k) key = red[k] > key ? red[k] : key;
+  if (tid == 0) {
+    for (int k = 1; k < kLargeThreads / 64; ++k) key = red[k] > key ? red[k] : key;
+    if (key) atomicMax(sc.key + n0, key);
+  }
+}
+
+template <bool NEXT>
+__global__ __launch_bounds__(kLargeThreads) void large_place_kernel(
+    const int32_t* __restrict__ draft, const uint64_t* __restrict__ mask,
+    const int32_t* __restrict__ node_offsets, int total_nodes, int max_nodes, int W,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
+    int32_t* __restrict__ accept_tokens, const float2* __restrict__ ws_root, int cpr,
+    int32_t* __restrict__ bonus_token, LargeScratch sc) {
+  __shared__ uint64_t brow[TA_MAX_NODES / 64];
+  __shared__ int32_t root_pred;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  int n0, nn;
+  seq_range(node_offsets, b, total_nodes, max_nodes, n0, nn);
+  if (NEXT) large_root_pred(ws_root, b, cpr, &root_pred);
+  const unsigned long long key = nn > 0 ? sc.key[n0] : 0ull;
   const int len = (int)(key >> 32);
   const int best = (int)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
-
   int32_t* an = accept_nodes + (size_t)b * max_nodes;
   int32_t* at = accept_tokens + (size_t)b * max_nodes;
-  for (int pos = len + tid; pos < max_nodes; pos += kBigThreads) {
+  for (int pos = len + tid; pos < max_nodes; pos += kLargeThreads) {
     an[pos] = -1;
     at[pos] = -1;
   }
-  if (len > 0 && wave == 0) {
-    // Lane k holds word k of the best row (W <= 64); each of its nodes goes
-    // to the position given by its depth.
-    uint64_t mw = 0ull;
-    if (lane < W && 64 * lane < nn) {
-      mw = mask[(size_t)(n0 + best) * W + lane];
-      if (nn - 64 * lane < 64) mw &= (1ull << (nn - 64 * lane)) - 1ull;
+  if (len > 0) {
+    // The accepted path: the best row's bits, each node placed at its depth
+    // (its position on the path, in whatever order the nodes are listed).
+    if (tid < W) {
+      uint64_t m = 64 * tid < nn ? mask[(size_t)(n0 + best) * W + tid] : 0ull;
+      if (64 * tid < nn && nn - 64 * tid < 64) m &= (1ull << (nn - 64 * tid)) - 1ull;
+      brow[tid] = m;
     }
-    while (mw) {
-      const int j = 64 * lane + __builtin_ctzll(mw);
-      an[dep[j]] = j;
-      at[dep[j]] = draft[n0 + j];
-      mw &= mw - 1ull;
+    __syncthreads();
+    for (int j = tid; j < nn; j += kLargeThreads) {
+      if ((brow[j >> 6] >> (j & 63)) & 1ull) {
+        const int pos = sc.dep[n0 + j];
+        an[pos] = j;
+        at[pos] = draft[n0 + j];
+      }
     }
   }
+  __syncthreads();
   if (tid == 0) {
     accept_len[b] = len;
-    if (NEXT) bonus_token[b] = len > 0 ? tgt[best] : root_pred;
+    if (NEXT) bonus_token[b] = len > 0 ? sc.tgt[n0 + best] : root_pred;
   }
 }
 
 }  // namespace
 
-VerifyPlan plan_verify(int total_nodes, int V) {
-  (void)total_nodes;
+VerifyPlan plan_verify(int rows, int V, int max_nodes) {
   VerifyPlan p{};
   // One chunk is one pass of the unrolled scan (32768 entries for bf16 or
   // fp32), so each workgroup streams 64 or 128 KB; chunks per row are a power
@@ -674,7 +762,15 @@ VerifyPlan plan_verify(int total_nodes, int V) {
   chunk = (chunk + 7) / 8 * 8;
   p.cpr = cpr;
   p.chunk = chunk;
-  p.ws_bytes = (size_t)total_nodes * p.cpr * sizeof(float2);
+  p.ws_bytes = (size_t)rows * p.cpr * sizeof(float2);
+  p.large = max_nodes > kLdsTreeMaxNodes;
+  if (p.large) {
+    // Scratch of the many-workgroup path selection, per row: prediction and
+    // depth (int32), match word and key (64 bits), each array 256-aligned.
+    const auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    p.scratch_off = a256(p.ws_bytes);
+    p.ws_bytes = p.scratch_off + 2 * a256((size_t)rows * 4) + 2 * a256((size_t)rows * 8);
+  }
   return p;
 }
 
@@ -721,19 +817,43 @@ hipError_t launch_verify(bool bf16, const void* logits, const int32_t* draft,
   hipError_t e = launch_argmax(bf16, logits, total_nodes, root_logits, root_logits ? B : 0, V, p,
                                ws, stream);
   if (e != hipSuccess) return e;
-  if (max_nodes > kLdsTreeMaxNodes) {
+  if (p.large) {
     int Wp = 1;
     while (Wp < W) Wp <<= 1;
+    // Scratch laid out as plan_verify sized it, for `rows` rows (node rows,
+    // and the prefix rows of next-token verification).
+    const int rows = total_nodes + (root_logits ? B : 0);
+    const auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    unsigned char* base = static_cast<unsigned char*>(workspace) + p.scratch_off;
+    LargeScratch sc;
+    sc.tgt = reinterpret_cast<int32_t*>(base);
+    sc.dep = reinterpret_cast<int32_t*>(base + a256((size_t)rows * 4));
+    sc.match = reinterpret_cast<uint64_t*>(base + 2 * a256((size_t)rows * 4));
+    sc.key = reinterpret_cast<unsigned long long*>(base + 2 * a256((size_t)rows * 4) +
+                                                   a256((size_t)rows * 8));
+    const int chunks = (max_nodes + kLargeRows - 1) / kLargeRows;
+    const dim3 grid((unsigned)((long long)B * chunks));
+    if (root_logits) {
+      hipLaunchKernelGGL(large_rows_kernel<true>, grid, dim3(kLargeThreads), 0, stream, ws, p.cpr,
+                         draft, mask, node_offsets, total_nodes, max_nodes, W, Wp, chunks,
+                         target_argmax, sc);
+      hipLaunchKernelGGL(large_parents_kernel, grid, dim3(kLargeThreads), 0, stream, draft, mask,
+                         node_offsets, total_nodes, max_nodes, W, Wp, chunks, ws_root, p.cpr, sc);
+    } else {
+      hipLaunchKernelGGL(large_rows_kernel<false>, grid, dim3(kLargeThreads), 0, stream, ws,
+                         p.cpr, draft, mask, node_offsets, total_nodes, max_nodes, W, Wp, chunks,
+                         target_argmax, sc);
+    }
+    hipLaunchKernelGGL(large_accept_kernel, grid, dim3(kLargeThreads), 0, stream, mask,
+                       node_offsets, total_nodes, max_nodes, W, Wp, chunks, sc);
     if (root_logits)
-      hipLaunchKernelGGL(path_select_large_kernel<true>, dim3(B), dim3(kBigThreads), 0, stream,
-                         ws, p.cpr, draft, mask, node_offsets, total_nodes, max_nodes, W, Wp,
-                         target_argmax, accept_len, accept_nodes, accept_tokens, ws_root,
-                         bonus_token);
+      hipLaunchKernelGGL(large_place_kernel<true>, dim3(B), dim3(kLargeThreads), 0, stream, draft,
+                         mask, node_offsets, total_nodes, max_nodes, W, accept_len, accept_nodes,
+                         accept_tokens, ws_root, p.cpr, bonus_token, sc);
     else
-      hipLaunchKernelGGL(path_select_large_kernel<false>, dim3(B), dim3(kBigThreads), 0, stream,
-                         ws, p.cpr, draft, mask, node_offsets, total_nodes, max_nodes, W, Wp,
-                         target_argmax, accept_len, accept_nodes, accept_tokens, nullptr,
-                         nullptr);
+      hipLaunchKernelGGL(large_place_kernel<false>, dim3(B), dim3(kLargeThreads), 0, stream, draft,
+                         mask, node_offsets, total_nodes, max_nodes, W, accept_len, accept_nodes,
+                         accept_tokens, nullptr, p.cpr, nullptr, sc);
     return hipGetLastError();
   }
   const size_t lds = (size_t)max_nodes * W * sizeof(uint64_t);
