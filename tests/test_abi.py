@@ -80,6 +80,14 @@ def test_workspace_queries_are_pure_host(lib):
     assert b.forward_workspace_size(torch.float32, 1, 5, 5, 1, 1, 64, 16, 16) == 0
     assert b.verify_workspace_size(64, 64, 128256) >= 64 * 8
     assert b.verify_workspace_size(0, 1, 10) == 0
+    # Up to 1024 nodes the workspace is the chunk results only (4 chunks of a
+    # 128256-entry row, 8 bytes each); above, per-row scratch follows them
+    # (prediction and depth 4 bytes, match word and key 8 bytes, each array
+    # 256-byte aligned).
+    small = b.verify_workspace_size(4096, 1024, 128256)
+    assert small == 4096 * 4 * 8
+    big = b.verify_workspace_size(4096, 4096, 128256)
+    assert big == small + 2 * 4096 * 4 + 2 * 4096 * 8
 
 
 def test_build_mask_and_verify_host_validation(lib):
