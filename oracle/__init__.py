@@ -14,7 +14,10 @@ Sources (the pages this follows):
   [PL]  "Speculative Tree Attention: How Multi-Candidate Draft Models and
         Parallel Verification Deliver 4x LLM Speedups", news.premlal.in:
         the code listing (build_tree_attention_mask, verify_candidate_tree and
-        its __main__ demo).
+        its __main__ demo); section "Production Inference Runtimes" (the
+        claim that the speculative step leaves the target's output
+        distribution unchanged), for the stochastic verifier, whose rule the
+        pages do not give: speculative_sampling.py takes the published one.
 """
 from .tree_attention import (  # noqa: F401
     STATUS_OK,
@@ -31,4 +34,9 @@ from .tree_attention import (  # noqa: F401
     verify_greedy,
     verify_greedy_next,
     kv_commit,
+)
+from .speculative_sampling import (  # noqa: F401
+    softmax_t,
+    sample_inverse_cdf,
+    speculative_sample,
 )
