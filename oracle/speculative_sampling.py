@@ -36,7 +36,7 @@ Readings (the pages are silent on all of these):
 """
 from __future__ import annotations
 
-from typing import List
+from typing import List, Optional
 
 import numpy as np
 
@@ -75,16 +75,19 @@ def residual(P: np.ndarray, Q: np.ndarray) -> np.ndarray:
 
 
 def speculative_sample(logits, root_logits, draft_probs, root_draft_probs, draft, parents,
-                       node_offsets, temperature: float, u_accept, u_final, max_nodes: int):
+                       node_offsets, temperature: float, u_accept, u_final, max_nodes: int,
+                       final_p: Optional[list] = None):
     """Stochastic verification of every sequence's tree.
 
     Returns (accept_len [B], accept_nodes [B][max_nodes], accept_tokens
     [B][max_nodes], bonus [B], margin [B]).  accept_nodes lists the accepted
-    path root first (local node ids, -1 padded); margin[b] is the smallest
-    distance, over sequence b's decisions, between the two sides of an accept
-    test (u * Q(x) against P(x)) or between u_final and a cumulative boundary:
-    an implementation computing in lower precision takes the same decisions
-    when its errors stay below it.
+    path root first (local node ids, -1 padded).  margin[b] is the smallest
+    relative distance, over sequence b's accept tests, between the two sides
+    u * Q(x) and P(x), relative to the size of the operands P(x) was computed
+    from (after residuals, P - Q before cancellation): an implementation
+    whose relative rounding stays below it takes the same accept decisions
+    (inf when nothing was tested).  If ``final_p`` is a list, the
+    distribution the bonus was drawn from is appended per sequence.
     """
     draft = np.asarray(draft, dtype=np.int64)
     parents = np.asarray(parents, dtype=np.int64)
@@ -102,6 +105,7 @@ def speculative_sample(logits, root_logits, draft_probs, root_draft_probs, draft
         par = parents[lo:hi].tolist()
         nn = hi - lo if tree_is_valid(par) else 0
         P = softmax_t(root_logits[b], temperature)
+        E = P                       # operand size behind each P(v), for the margin
         Q = _f64(root_draft_probs[b])
         cur = -1
         path: List[int] = []
@@ -110,19 +114,27 @@ def speculative_sample(logits, root_logits, draft_probs, root_draft_probs, draft
             for c in (i for i in range(nn) if par[i] == cur):
                 x = int(draft[lo + c])
                 lhs, rhs = u_accept[lo + c] * Q[x], P[x]
-                margin[b] = min(margin[b], abs(lhs - rhs))
+                size = max(E[x], lhs)
+                if size > 0:
+                    margin[b] = min(margin[b], abs(lhs - rhs) / size)
                 if lhs < rhs:
                     taken = c
                     break
+                R = np.maximum(P - Q, 0.0)
+                Z = R.sum()
                 P = residual(P, Q)
+                if Z > 0:
+                    E = (E + Q) / Z
             if taken is None:
                 break
             path.append(taken)
             cur = taken
             P = softmax_t(logits[lo + cur], temperature)
+            E = P
             Q = _f64(draft_probs[lo + cur])
-        v, m = sample_inverse_cdf(P, float(u_final[b]))
-        margin[b] = min(margin[b], m)
+        v, _ = sample_inverse_cdf(P, float(u_final[b]))
+        if final_p is not None:
+            final_p.append(P)
         acc_len[b] = len(path)
         for k, j in enumerate(path):
             acc_nodes[b, k] = j
