@@ -924,6 +924,34 @@ def main():
         ta.kv_commit(s["kt"], s["vt"], s["noffs"], acc_len, acc_nodes, k_cache, v_cache,
                      cache_offs, cache_lens, status=commit_status)
 
+    # Stochastic verification (rejection sampling down the tree) on the same trees and
+    # vocabulary: synthetic target logits and draft distributions close to them, each
+    # node's token drawn from its parent's draft row, fixed uniforms.  Set up only where
+    # the fp32 draft rows stay small (sum_N * V <= 2^26).
+    samp = None
+    if not args.no_extra_calls and sum_n * V <= (1 << 26):
+        trees = [case.parents[int(case.node_offsets[b]):int(case.node_offsets[b + 1])].tolist()
+                 for b in range(B)]
+        sc = synthetic.make_sampling_case(trees, V, dtype=base["logits"].dtype, seed=7,
+                                          temperature=1.0, noise=0.5, max_nodes=max_nodes)
+        sd = {k: (v.to(dev) if isinstance(v, torch.Tensor) else torch.from_numpy(v).to(dev))
+              for k, v in (("lg", sc.logits), ("rl", sc.root_logits), ("q", sc.draft_probs),
+                           ("rq", sc.root_draft_probs), ("d", sc.draft), ("p", sc.parents),
+                           ("o", sc.node_offsets), ("ua", sc.u_accept), ("uf", sc.u_final))}
+        sws = torch.empty(max(ta.verify_sample_workspace_size(B, V), 16), dtype=torch.uint8,
+                          device=dev)
+        so = [torch.empty(B, dtype=torch.int32, device=dev),
+              torch.empty((B, max_nodes), dtype=torch.int32, device=dev),
+              torch.empty((B, max_nodes), dtype=torch.int32, device=dev),
+              torch.empty(B, dtype=torch.int32, device=dev)]
+
+        def do_sample(s):
+            ta.verify_sample(sd["lg"], sd["rl"], sd["q"], sd["rq"], sd["d"], sd["p"], sd["o"],
+                             max_nodes, sc.temperature, sd["ua"], sd["uf"], workspace=sws,
+                             accept_len=so[0], accept_nodes=so[1], accept_tokens=so[2],
+                             bonus_token=so[3])
+        samp = do_sample
+
     do_mask(sets[0])
     t_mask, d_mask = event_time(do_mask, args.steps)
     t_fwd_ev, d_fwd = event_time(fwd_fn, args.steps)
@@ -932,6 +960,10 @@ def main():
     if not args.no_extra_calls:
         t_commit, d_commit = event_time(do_commit, args.steps)
         t_vnext, d_vnext = event_time(do_verify_next, args.steps)
+    t_samp = d_samp = None
+    if samp is not None:
+        t_samp, d_samp = event_time(samp, args.steps)
+        samp_len = so[0].float().mean().item()
     if t_commit is not None and not bool((commit_status == 0).all()):
         raise SystemExit("tree_kv_commit reported a failure in the timing loop")
     print(f"[bench] per call us: mask {t_mask:.2f} forward {t_fwd:.2f} ({t_fwd_ev:.2f} in the "
@@ -1019,11 +1051,16 @@ def main():
             "us_per_call": {fwd_call: round(t_fwd_ev, 3), "tree_verify_greedy": round(t_ver, 3),
                             "tree_attn_build_mask (standalone)": round(t_mask, 3),
                             "tree_kv_commit (standalone)": t_commit and round(t_commit, 3),
-                            "tree_verify_greedy_next (standalone)": t_vnext and round(t_vnext, 3)},
+                            "tree_verify_greedy_next (standalone)": t_vnext and round(t_vnext, 3),
+                            "tree_verify_sample (standalone)": t_samp and round(t_samp, 3)},
             "us_per_call_spread": {fwd_call: d_fwd, "tree_verify_greedy": d_ver,
                                    "tree_attn_build_mask (standalone)": d_mask,
                                    "tree_kv_commit (standalone)": d_commit,
-                                   "tree_verify_greedy_next (standalone)": d_vnext},
+                                   "tree_verify_greedy_next (standalone)": d_vnext,
+                                   "tree_verify_sample (standalone)": d_samp},
+            "sample": t_samp and {"accept_len_mean": round(samp_len, 3),
+                                  "inputs": "target logits 2*randn, draft = softmax(logits + "
+                                            "0.5*randn), T=1, tokens drawn from the draft"},
             "commit": {"accepted_rows": int(acc_len.sum()),
                        "alg_bytes": int(acc_len.sum()) * Hkv * D * base["kt"].element_size() * 4},
             "forward": {"tree_tokens_per_s": round(value, 1),

@@ -385,6 +385,68 @@ TA_API int tree_kv_commit(int dtype, const void* k_tree, const void* v_tree,
                           void* v_cache, const int64_t* cache_offsets, int64_t* cache_lens,
                           int64_t total_cache, int32_t* commit_status, void* stream);
 
+/*
+ * Bytes of device workspace tree_verify_sample needs (two fp32 rows of V per
+ * sequence).  Pure host arithmetic.
+ */
+TA_API size_t tree_verify_sample_workspace_size(int32_t B, int32_t V);
+
+/*
+ * Stochastic verification: rejection sampling down the tree, which keeps the
+ * emitted tokens distributed as the target model's own samples would be.
+ *
+ * Follows: premlal "Speculative Tree Attention", Production Inference
+ * Runtimes (the speculative step leaves the output distribution unchanged);
+ * the pages give no rule, so the published one is taken: speculative
+ * sampling's accept test and residual (Leviathan et al. 2023; Chen et al.
+ * 2023) applied child by child down the tree (SpecInfer's multi-step
+ * speculative sampling, Miao et al. 2024).  Lossless when the children of
+ * each node were drawn independently from that node's draft distribution.
+ *
+ *   logits_dtype   TA_BF16 or TA_F32 (the logits; draft probabilities are
+ *                  always fp32).
+ *   logits         [sum_N][V]: row i, the target's logits for the token after
+ *                  node i (as tree_verify_greedy_next).
+ *   root_logits    [B][V]: the target's logits after sequence b's prefix.
+ *   draft_probs    fp32 [sum_N][V]: row i, the draft distribution node i's
+ *                  children were drawn from.
+ *   root_draft_probs fp32 [B][V]: the one sequence b's roots were drawn from.
+ *   draft_tokens   int32 [sum_N].
+ *   parents        int32 [sum_N]: local parent ids, -1 for a root (any node
+ *                  order, as tree_attn_build_mask).
+ *   node_offsets   int32 [B+1], non-decreasing.
+ *   B, total_nodes, max_nodes, V [host]; temperature [host] > 0: the target
+ *                  distribution is softmax(logits / temperature).
+ *   u_accept       fp32 [sum_N] uniforms in [0, 1), one per node (read only
+ *                  when the node is tested); u_final fp32 [B], one per sequence.
+ *   accept_len     out int32 [B]; accept_nodes, accept_tokens out int32
+ *                  [B][max_nodes]: the accepted path, local ids root first,
+ *                  and its draft tokens, -1 padded.
+ *   bonus_token    out int32 [B]: the token drawn after the accepted path.
+ *   workspace      at least tree_verify_sample_workspace_size(B, V) bytes,
+ *                  16-byte aligned, any content.
+ * The walk: with P the target's and Q the draft's distribution above the
+ * roots, the children of the current node are tested in increasing index
+ * order; child c with token x is accepted iff u_accept[c] * Q(x) < P(x) and
+ * becomes the current node (P, Q from its rows); a rejection turns P into
+ * max(0, P - Q) renormalised (kept when that is all zero).  When no child is
+ * left, the bonus is the lowest token whose cumulative P exceeds u_final[b].
+ * Computed in fp32 (an fp64 evaluation can decide differently only where the
+ * two sides of a test, or u_final and a cumulative boundary, are within
+ * rounding of each other).  A tree with an out-of-range parent or a cycle,
+ * or a sequence whose offsets do not decode, is walked as empty.  Asynchronous
+ * on `stream`; one workgroup per sequence.
+ */
+TA_API int tree_verify_sample(int logits_dtype, const void* logits, const void* root_logits,
+                              const float* draft_probs, const float* root_draft_probs,
+                              const int32_t* draft_tokens, const int32_t* parents,
+                              const int32_t* node_offsets, int32_t B, int32_t total_nodes,
+                              int32_t max_nodes, int32_t V, float temperature,
+                              const float* u_accept, const float* u_final, int32_t* accept_len,
+                              int32_t* accept_nodes, int32_t* accept_tokens,
+                              int32_t* bonus_token, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* Static text for a status code; never NULL. */
 TA_API const char* tree_attn_status_string(int status);
 

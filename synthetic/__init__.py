@@ -17,6 +17,12 @@ Recipe (the same for every consumer):
   * logits: the same torch generator, ``randn`` fp32 then bf16; each draft
     token equals the row's target argmax (``torch.argmax``, a library call)
     with probability ``p_match``, else it is uniform over the vocabulary.
+  * stochastic verification (make_sampling_case): target logits
+    ``scale * randn`` (bf16 or fp32) from ``default_rng(seed)``; the draft
+    distribution of each row is ``softmax((logits + noise * randn) / T)``
+    (a stand-in draft model close to the target), in fp32; each node's draft
+    token is drawn from its parent's draft row (the prefix row for a root);
+    uniforms in [0, 1) in fp32.
 """
 from __future__ import annotations
 
@@ -34,6 +40,8 @@ __all__ = [
     "rerank_tree",
     "make_case",
     "make_config_case",
+    "SamplingCase",
+    "make_sampling_case",
     "EXAMPLE_PARENTS",
     "EXAMPLE_TOKENS",
 ]
@@ -269,3 +277,59 @@ def make_config_case(name: str, *, with_logits: Optional[bool] = None,
                 want = tok if i in (0, 1, 3) else (tok + 1) % vocab
                 lg[base + i, want] = 8.0
     return case
+
+
+@dataclass
+class SamplingCase:
+    """Inputs of one tree_verify_sample call (host arrays / CPU tensors)."""
+    parents: np.ndarray          # int32 [sum_N]
+    node_offsets: np.ndarray     # int32 [B+1]
+    logits: torch.Tensor         # [sum_N][V] bf16 or fp32
+    root_logits: torch.Tensor    # [B][V]
+    draft_probs: np.ndarray      # fp32 [sum_N][V]
+    root_draft_probs: np.ndarray  # fp32 [B][V]
+    draft: np.ndarray            # int32 [sum_N]
+    u_accept: np.ndarray         # fp32 [sum_N]
+    u_final: np.ndarray          # fp32 [B]
+    temperature: float
+    max_nodes: int
+
+
+def _softmax_rows(z: np.ndarray) -> np.ndarray:
+    z = z - z.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def make_sampling_case(trees: Sequence[Sequence[int]], V: int, *, dtype=torch.bfloat16,
+                       seed: int = 0, temperature: float = 1.0, scale: float = 2.0,
+                       noise: float = 0.5, max_nodes: Optional[int] = None) -> SamplingCase:
+    """Seeded inputs for stochastic verification over the given parent arrays
+    (recipe in the module docstring).  Parents that are not a valid tree are
+    kept as given (their nodes draw from the prefix row)."""
+    rng = np.random.default_rng(seed)
+    sizes = [len(t) for t in trees]
+    B = len(trees)
+    offs = np.zeros(B + 1, dtype=np.int32)
+    offs[1:] = np.cumsum(sizes)
+    total = int(offs[-1])
+    parents = np.array([p for t in trees for p in t], dtype=np.int32)
+    lg = (scale * rng.standard_normal((total + B, V))).astype(np.float32)
+    lt = torch.from_numpy(lg).to(dtype)
+    lg_exact = lt.to(torch.float64).numpy()
+    q = _softmax_rows((lg_exact + noise * rng.standard_normal((total + B, V))) / temperature)
+    q = q.astype(np.float32)
+    draft = np.zeros(total, dtype=np.int32)
+    for b in range(B):
+        lo = int(offs[b])
+        for i, p in enumerate(trees[b]):
+            row = q[total + b] if not (0 <= p < sizes[b]) else q[lo + p]
+            pr = row.astype(np.float64)
+            draft[lo + i] = int(rng.choice(V, p=pr / pr.sum()))
+    return SamplingCase(
+        parents=parents, node_offsets=offs, logits=lt[:total].contiguous(),
+        root_logits=lt[total:].contiguous(), draft_probs=q[:total].copy(),
+        root_draft_probs=q[total:].copy(), draft=draft,
+        u_accept=rng.random(total).astype(np.float32), u_final=rng.random(B).astype(np.float32),
+        temperature=float(temperature),
+        max_nodes=int(max_nodes if max_nodes is not None else max(1, max(sizes, default=1))))

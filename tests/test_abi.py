@@ -25,9 +25,9 @@ def test_header_declares_the_three_calls():
     names = _declared_functions()
     for n in ("tree_attn_build_mask", "tree_attn_forward", "tree_verify_greedy",
               "tree_attn_mask_and_forward", "tree_kv_commit", "tree_verify_greedy_next",
-              "tree_attn_forward_noalloc"):
+              "tree_attn_forward_noalloc", "tree_verify_sample"):
         assert n in names
-    assert len(names) == 10, names
+    assert len(names) == 12, names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -179,6 +179,33 @@ def test_verify_next_host_validation(lib):
     assert v(*bad) == 4
     bad = list(ok); bad[8] = 5000
     assert v(*bad) == 3
+
+
+def test_verify_sample_host_validation(lib):
+    v = lib.tree_verify_sample
+    #      dtype logits  root    q       q_root  draft   parents offsets B  N   maxn V
+    ok = [1, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 2, 64, 64, 1000,
+          #   T    u_acc    u_fin    alen     anodes   atok     bonus    ws       ws_bytes stream
+          0.7, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 16000, None]
+    bad = list(ok); bad[0] = 5
+    assert v(*bad) == 3
+    for i in (2, 4, 7, 14, 15, 16, 17, 18):        # always required
+        bad = list(ok); bad[i] = None
+        assert v(*bad) == 1, i
+    for i in (1, 3, 5, 6, 13):                     # required when there are nodes
+        bad = list(ok); bad[i] = None
+        assert v(*bad) == 1, i
+    for t in (0.0, -1.0, float("nan"), float("inf")):
+        bad = list(ok); bad[12] = t
+        assert v(*bad) == 1, t
+    bad = list(ok); bad[20] = 15999                 # two fp32 rows of V per sequence
+    assert v(*bad) == 4
+    bad = list(ok); bad[19] = (1 << 20) + 8         # misaligned workspace
+    assert v(*bad) == 4
+    bad = list(ok); bad[10] = 5000
+    assert v(*bad) == 3
+    assert lib.tree_verify_sample_workspace_size(2, 1000) == 16000
+    assert lib.tree_verify_sample_workspace_size(0, 1000) == 0
 
 
 def _noalloc(lib, **kw):

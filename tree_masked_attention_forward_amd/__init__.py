@@ -1,4 +1,5 @@
-"""Tree attention and greedy tree verification on AMD Instinct MI355X (gfx950).
+"""Tree attention and tree verification (greedy, and by rejection sampling) on
+AMD Instinct MI355X (gfx950).
 
 The computation lives in ``libtreeattn.so`` (hand-written HIP kernels behind
 the C ABI of ``include/tree_attn.h``); this package is its Python binding.
@@ -33,6 +34,8 @@ from ._binding import (  # noqa: F401
     status_string,
     verify_greedy,
     verify_greedy_next,
+    verify_sample,
+    verify_sample_workspace_size,
     verify_workspace_size,
 )
 
@@ -46,3 +49,4 @@ tree_attn_mask_and_forward = mask_and_forward
 tree_verify_greedy = verify_greedy
 tree_kv_commit = kv_commit
 tree_verify_greedy_next = verify_greedy_next
+tree_verify_sample = verify_sample

@@ -83,6 +83,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tree_verify_greedy_next.restype = ctypes.c_int
     lib.tree_verify_greedy_next.argtypes = [ctypes.c_int] + [_c_void_p] * 5 + [_i32] * 4 + [
         _c_void_p] * 6 + [ctypes.c_size_t, _c_void_p]
+    lib.tree_verify_sample_workspace_size.restype = ctypes.c_size_t
+    lib.tree_verify_sample_workspace_size.argtypes = [_i32, _i32]
+    lib.tree_verify_sample.restype = ctypes.c_int
+    lib.tree_verify_sample.argtypes = [ctypes.c_int] + [_c_void_p] * 7 + [_i32] * 4 + [
+        ctypes.c_float] + [_c_void_p] * 7 + [ctypes.c_size_t, _c_void_p]
     lib.tree_kv_commit.restype = ctypes.c_int
     lib.tree_kv_commit.argtypes = [ctypes.c_int] + [_c_void_p] * 5 + [_i32] * 5 + [
         _c_void_p] * 4 + [_i64, _c_void_p, _c_void_p]
@@ -421,6 +426,65 @@ def verify_greedy_next(logits: torch.Tensor, root_logits: torch.Tensor,
         B, total, int(max_nodes), V, _ptr(target_argmax), _ptr(accept_len), _ptr(accept_nodes),
         _ptr(accept_tokens), _ptr(bonus_token), _ptr(workspace), ws_len, _stream(dev)))
     return target_argmax, accept_len, accept_nodes, accept_tokens, bonus_token
+
+
+def verify_sample_workspace_size(B: int, V: int) -> int:
+    return int(load_library().tree_verify_sample_workspace_size(B, V))
+
+
+def verify_sample(logits: torch.Tensor, root_logits: torch.Tensor, draft_probs: torch.Tensor,
+                  root_draft_probs: torch.Tensor, draft_tokens: torch.Tensor,
+                  parents: torch.Tensor, node_offsets: torch.Tensor, max_nodes: int,
+                  temperature: float, u_accept: torch.Tensor, u_final: torch.Tensor, *,
+                  workspace: Optional[torch.Tensor] = None,
+                  accept_len: Optional[torch.Tensor] = None,
+                  accept_nodes: Optional[torch.Tensor] = None,
+                  accept_tokens: Optional[torch.Tensor] = None,
+                  bonus_token: Optional[torch.Tensor] = None):
+    """tree_verify_sample (rejection sampling down the tree; the random numbers
+    are inputs).  Returns (accept_len, accept_nodes, accept_tokens,
+    bonus_token)."""
+    dev = _device_of(logits)
+    if logits.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("logits must be bfloat16 or float32")
+    _need(logits, "logits", logits.dtype, dev, 2)
+    _need(root_logits, "root_logits", logits.dtype, dev, 2)
+    total, V = logits.shape
+    _need(draft_probs, "draft_probs", torch.float32, dev, 2)
+    _need(root_draft_probs, "root_draft_probs", torch.float32, dev, 2)
+    _need(draft_tokens, "draft_tokens", torch.int32, dev, 1)
+    _need(parents, "parents", torch.int32, dev, 1)
+    _need(node_offsets, "node_offsets", torch.int32, dev, 1)
+    _need(u_accept, "u_accept", torch.float32, dev, 1)
+    _need(u_final, "u_final", torch.float32, dev, 1)
+    B = node_offsets.numel() - 1
+    if tuple(root_logits.shape) != (B, V) or tuple(root_draft_probs.shape) != (B, V):
+        raise ValueError("root_logits and root_draft_probs must be [B, V]")
+    if tuple(draft_probs.shape) != (total, V):
+        raise ValueError("draft_probs must match the logits rows")
+    if draft_tokens.numel() != total or parents.numel() != total or u_accept.numel() != total:
+        raise ValueError("draft_tokens/parents/u_accept must have one entry per node")
+    if u_final.numel() != B:
+        raise ValueError("u_final must have one entry per sequence")
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if accept_nodes is None:
+        accept_nodes = torch.empty((B, max_nodes), dtype=torch.int32, device=dev)
+    if accept_tokens is None:
+        accept_tokens = torch.empty((B, max_nodes), dtype=torch.int32, device=dev)
+    if bonus_token is None:
+        bonus_token = torch.empty(B, dtype=torch.int32, device=dev)
+    ws_bytes = verify_sample_workspace_size(B, V)
+    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws_len = workspace.numel() * workspace.element_size()
+    code = TA_BF16 if logits.dtype == torch.bfloat16 else TA_F32
+    _check("tree_verify_sample", load_library().tree_verify_sample(
+        code, _ptr(logits), _ptr(root_logits), _ptr(draft_probs), _ptr(root_draft_probs),
+        _ptr(draft_tokens), _ptr(parents), _ptr(node_offsets), B, total, int(max_nodes), V,
+        float(temperature), _ptr(u_accept), _ptr(u_final), _ptr(accept_len), _ptr(accept_nodes),
+        _ptr(accept_tokens), _ptr(bonus_token), _ptr(workspace), ws_len, _stream(dev)))
+    return accept_len, accept_nodes, accept_tokens, bonus_token
 
 
 def kv_commit(k_tree: torch.Tensor, v_tree: torch.Tensor, node_offsets: torch.Tensor,

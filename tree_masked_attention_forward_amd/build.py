@@ -31,7 +31,7 @@ LIB = os.path.join(PKG, "libtreeattn.so")
 PROBE_LIB = os.path.join(PKG, "libtaprobes.so")
 PROBE_SOURCES = ["probes.hip"]
 SOURCES = ["api.cpp", "mask_build.hip", "attn_fwd.hip", "attn_fwd_f32.hip", "verify.hip",
-           "kv_commit.hip"]
+           "kv_commit.hip", "sample.hip"]
 ARCH = os.environ.get("TREE_ATTN_ARCH", "gfx950")
 # Extra flags per source file.
 SOURCE_FLAGS = {"attn_fwd.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"]}

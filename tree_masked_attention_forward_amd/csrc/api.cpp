@@ -395,4 +395,36 @@ int tree_kv_commit(int dtype, const void* k_tree, const void* v_tree,
                                          static_cast<hipStream_t>(stream)));
 }
 
+size_t tree_verify_sample_workspace_size(int32_t B, int32_t V) {
+  if (B <= 0 || V <= 0) return 0;
+  return (size_t)B * 2 * (size_t)V * sizeof(float);
+}
+
+int tree_verify_sample(int logits_dtype, const void* logits, const void* root_logits,
+                       const float* draft_probs, const float* root_draft_probs,
+                       const int32_t* draft_tokens, const int32_t* parents,
+                       const int32_t* node_offsets, int32_t B, int32_t total_nodes,
+                       int32_t max_nodes, int32_t V, float temperature, const float* u_accept,
+                       const float* u_final, int32_t* accept_len, int32_t* accept_nodes,
+                       int32_t* accept_tokens, int32_t* bonus_token, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (logits_dtype != TA_BF16 && logits_dtype != TA_F32) return TA_ERR_UNSUPPORTED;
+  if (B <= 0 || total_nodes < 0 || max_nodes < 1 || V <= 0) return TA_ERR_INVALID_ARG;
+  if (!(temperature > 0.f) || temperature > 3.0e38f) return TA_ERR_INVALID_ARG;
+  if (max_nodes > TA_MAX_NODES) return TA_ERR_UNSUPPORTED;
+  if (!root_logits || !root_draft_probs || !u_final || !node_offsets || !accept_len ||
+      !accept_nodes || !accept_tokens || !bonus_token)
+    return TA_ERR_INVALID_ARG;
+  if (total_nodes > 0 && (!logits || !draft_probs || !draft_tokens || !parents || !u_accept))
+    return TA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < tree_verify_sample_workspace_size(B, V) ||
+      misaligned16(workspace))
+    return TA_ERR_WORKSPACE;
+  return hip_status(ta::launch_verify_sample(
+      logits_dtype == TA_BF16, logits, root_logits, draft_probs, root_draft_probs, draft_tokens,
+      parents, node_offsets, B, total_nodes, max_nodes, V, temperature, u_accept, u_final,
+      accept_len, accept_nodes, accept_tokens, bonus_token, workspace,
+      static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

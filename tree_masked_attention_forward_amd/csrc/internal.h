@@ -115,4 +115,15 @@ hipError_t launch_kv_commit(const void* k_tree, const void* v_tree, const int32_
                             void* v_cache, const int64_t* cache_offsets, int64_t* cache_lens,
                             long long total_cache, int32_t* status, hipStream_t stream);
 
+// Stochastic verification (tree_verify_sample): one workgroup per sequence;
+// workspace = two fp32 rows of V per sequence.
+hipError_t launch_verify_sample(bool bf16, const void* logits, const void* root_logits,
+                                const float* draft_probs, const float* root_draft_probs,
+                                const int32_t* draft, const int32_t* parents,
+                                const int32_t* node_offsets, int B, int total_nodes,
+                                int max_nodes, int V, float temperature, const float* u_accept,
+                                const float* u_final, int32_t* accept_len, int32_t* accept_nodes,
+                                int32_t* accept_tokens, int32_t* bonus_token, void* workspace,
+                                hipStream_t stream);
+
 }  // namespace ta

@@ -1,0 +1,457 @@
+// Stochastic tree verification (rejection sampling down the tree).
+//
+// "Speculative Tree Attention" (news.premlal.in), Production Inference
+// Runtimes: a speculative step leaves the target model's output distribution
+// unchanged.  The pages give no rule; this is the published one that makes it
+// so: speculative sampling's accept test and residual (Leviathan et al. 2023;
+// Chen et al. 2023) walked child by child down the tree, as in SpecInfer's
+// multi-step speculative sampling (Miao et al. 2024).
+//
+// One workgroup per sequence walks its tree.  The current distribution P is
+// either the softmax of a target logits row at the given temperature, kept
+// implicit (its row, max and sum), or an explicit residual in a per-sequence
+// scratch row.  Testing child c with draft token x reads P(x) and the draft
+// probability Q(x); it is accepted iff u_c * Q(x) < P(x).  An accepted child
+// becomes the current node (one pass over its logits row for the max and
+// sum); a rejected one turns P into max(0, P - Q) renormalised (one pass that
+// writes the other scratch row, so P survives when that residual is all
+// zero).  The bonus token is drawn from P by inversion: wave totals over
+// contiguous vocabulary segments, then a scan of the one segment holding
+// u_final * sum(P).  The walk's decisions are uniform: every thread takes them
+// from values in LDS.
+#include "internal.h"
+
+namespace ta {
+namespace {
+
+constexpr int kSThreads = 1024;
+constexpr int kSWaves = kSThreads / 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInfS = -__builtin_inff();
+
+__device__ inline float wave_sum_f(float x) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ inline float wave_max_f(float x) {
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// Workgroup-wide sum (every thread gets the result).
+__device__ inline float block_sum(float x, float* red) {
+  x = wave_sum_f(x);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < kSWaves; ++w) s += red[w];
+  return s;
+}
+template <bool BF16>
+__device__ inline float logit(const void* row, int v) {
+  if constexpr (BF16) {
+    const uint16_t h = static_cast<const uint16_t*>(row)[v];
+    return __uint_as_float((uint32_t)h << 16);
+  } else {
+    return static_cast<const float*>(row)[v];
+  }
+}
+
+// The current distribution: P(v) = exp2(s_v - m) / Z with s_v = logit * kc
+// (implicit), or P(v) = R[v] / Z (explicit).
+struct Dist {
+  const void* row;   // logits row (implicit) or nullptr
+  const float* R;    // residual row (explicit)
+  float m, Z;
+};
+
+template <bool BF16>
+__device__ inline float dist_at(const Dist& d, int v, float kc) {
+  if (d.row) return __builtin_amdgcn_exp2f(logit<BF16>(d.row, v) * kc - d.m);
+  return d.R[v];
+}
+
+typedef uint32_t u32x4s_t __attribute__((ext_vector_type(4)));
+typedef float f32x4s_t __attribute__((ext_vector_type(4)));
+
+// Eight entries v .. v+7 of a row (entries past V read as `pad`).  VEC: the
+// row is 16-byte aligned and V % 8 == 0, so a whole group is one (bf16) or
+// two (fp32) 16-byte loads.
+template <bool BF16, bool VEC>
+__device__ inline void load8_logits(const void* row, int v, int V, float (&x)[8]) {
+  if (VEC && v + 8 <= V) {
+    if constexpr (BF16) {
+      const u32x4s_t w = *reinterpret_cast<const u32x4s_t*>(static_cast<const uint16_t*>(row) + v);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = __uint_as_float(w[k] << 16);
+        x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+      }
+    } else {
+      const f32x4s_t a = *reinterpret_cast<const f32x4s_t*>(static_cast<const float*>(row) + v);
+      const f32x4s_t c = *reinterpret_cast<const f32x4s_t*>(static_cast<const float*>(row) + v + 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[k] = a[k];
+        x[4 + k] = c[k];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = v + k < V ? logit<BF16>(row, v + k) : kNegInfS;
+  }
+}
+template <bool VEC>
+__device__ inline void load8_f32(const float* row, int v, int V, float (&x)[8]) {
+  if (VEC && v + 8 <= V) {
+    const f32x4s_t a = *reinterpret_cast<const f32x4s_t*>(row + v);
+    const f32x4s_t c = *reinterpret_cast<const f32x4s_t*>(row + v + 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[k] = a[k];
+      x[4 + k] = c[k];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = v + k < V ? row[v + k] : 0.f;
+  }
+}
+template <bool VEC>
+__device__ inline void store8_f32(float* row, int v, int V, const float (&x)[8]) {
+  if (VEC && v + 8 <= V) {
+    *reinterpret_cast<f32x4s_t*>(row + v) = f32x4s_t{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4s_t*>(row + v + 4) = f32x4s_t{x[4], x[5], x[6], x[7]};
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (v + k < V) row[v + k] = x[k];
+  }
+}
+
+// Unnormalised P over eight entries: exp2(logit * kc - m), or the residual row.
+template <bool BF16, bool VEC>
+__device__ inline void dist8(const Dist& d, int v, int V, float kc, float (&x)[8]) {
+  if (d.row) {
+    load8_logits<BF16, VEC>(d.row, v, V, x);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = __builtin_amdgcn_exp2f(x[k] * kc - d.m);
+  } else {
+    load8_f32<VEC>(d.R, v, V, x);
+  }
+}
+
+// (max, sum of exp2(x - max)) pairs merged: the larger max, the other sum
+// rescaled to it.
+__device__ inline void merge_ms(float& m, float& s, float m2, float s2) {
+  const float mm = fmaxf(m, m2);
+  if (mm == kNegInfS) return;
+  s = s * __builtin_amdgcn_exp2f(m - mm) + s2 * __builtin_amdgcn_exp2f(m2 - mm);
+  m = mm;
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
+    const void* __restrict__ logits, const void* __restrict__ root_logits,
+    const float* __restrict__ qp, const float* __restrict__ root_qp,
+    const int32_t* __restrict__ draft, const int32_t* __restrict__ parents,
+    const int32_t* __restrict__ node_offsets, int total_nodes, int max_nodes, int V, float kc,
+    const float* __restrict__ u_accept, const float* __restrict__ u_final,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
+    int32_t* __restrict__ accept_tokens, int32_t* __restrict__ bonus_token,
+    float* __restrict__ scratch) {
+  __shared__ int32_t par[TA_MAX_NODES];
+  __shared__ int32_t jmp[TA_MAX_NODES];
+  __shared__ float red[kSWaves];
+  __shared__ float red2[kSWaves];
+  __shared__ int ired[kSWaves];
+  __shared__ int s_bad;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const size_t esz = BF16 ? 2 : 4;
+  int n0 = node_offsets[b];
+  const int n1 = node_offsets[b + 1];
+  int nn = n1 - n0;
+  if (n0 < 0 || nn < 0 || nn > max_nodes || n1 > total_nodes || max_nodes > TA_MAX_NODES) {
+    n0 = 0;
+    nn = 0;
+  }
+
+  // Tree check (as the oracle): every parent -1 or another node of the
+  // sequence, and every parent chain reaching -1 (pointer jumping: after
+  // ceil(log2 nn) + 1 doublings a chain of length < nn has ended).  An
+  // invalid tree is walked as an empty one.
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  for (int i = tid; i < nn; i += kSThreads) {
+    const int p = parents[n0 + i];
+    par[i] = p;
+    jmp[i] = p;
+    if (p < -1 || p >= nn || p == i) s_bad = 1;
+  }
+  __syncthreads();
+  if (!s_bad) {
+    for (int span = 1; span < 2 * nn; span <<= 1) {
+      int nj[TA_MAX_NODES / kSThreads];
+#pragma unroll
+      for (int k = 0; k < TA_MAX_NODES / kSThreads; ++k) {
+        const int i = tid + k * kSThreads;
+        nj[k] = (i < nn && jmp[i] >= 0) ? jmp[jmp[i]] : (i < nn ? jmp[i] : -1);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < TA_MAX_NODES / kSThreads; ++k) {
+        const int i = tid + k * kSThreads;
+        if (i < nn) jmp[i] = nj[k];
+      }
+      __syncthreads();
+    }
+    for (int i = tid; i < nn; i += kSThreads)
+      if (jmp[i] != -1) s_bad = 1;
+    __syncthreads();
+  }
+  if (s_bad) nn = 0;
+
+  // Two scratch rows per sequence; rsel: the one holding an explicit P.
+  float* const rows2 = scratch + (size_t)b * 2 * V;
+  int rsel = 0;
+
+  // Every pass over the vocabulary gives thread t the contiguous run
+  // [t*C, t*C + C) (C a multiple of 8), taken 8 entries at a time, four
+  // groups' loads issued before any is used.
+  const int C = ((V + kSThreads - 1) / kSThreads + 7) / 8 * 8;
+  const int r0 = tid * C;
+  const int r1 = min(V, r0 + C);
+  constexpr int kBatch = 4;
+
+  // Implicit softmax of a logits row: its max and sum in one pass (each
+  // thread keeps a running max and a sum rescaled when the max moves).
+  auto softmax_of = [&](const void* row) {
+    Dist d;
+    d.row = row;
+    d.R = nullptr;
+    float m = kNegInfS, s = 0.f;
+    for (int v0 = r0; v0 < r1; v0 += 8 * kBatch) {
+      float x[kBatch][8];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) load8_logits<BF16, VEC>(row, min(v0 + 8 * j, V), V, x[j]);
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (v0 + 8 * j >= r1) break;
+        float cm = kNegInfS;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          x[j][k] *= kc;
+          cm = fmaxf(cm, x[j][k]);
+        }
+        if (cm > m) {
+          s = m == kNegInfS ? 0.f : s * __builtin_amdgcn_exp2f(m - cm);
+          m = cm;
+        }
+        if (m != kNegInfS) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) s += __builtin_amdgcn_exp2f(x[j][k] - m);
+        }
+      }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+      merge_ms(m, s, m2, s2);
+    }
+    __syncthreads();
+    if (lane == 0) {
+      red[wave] = m;
+      red2[wave] = s;
+    }
+    __syncthreads();
+    float bm = red[0], bs = red2[0];
+    for (int w = 1; w < kSWaves; ++w) merge_ms(bm, bs, red[w], red2[w]);
+    d.m = bm;
+    d.Z = bs;
+    return d;
+  };
+
+  Dist P = softmax_of(static_cast<const unsigned char*>(root_logits) + (size_t)b * V * esz);
+  const float* Q = root_qp + (size_t)b * V;
+  int cur = -1;     // current node (-1: above the roots)
+  int after = -1;   // children of cur with index <= after are done
+  int len = 0;
+  int32_t* an = accept_nodes + (size_t)b * max_nodes;
+  int32_t* at = accept_tokens + (size_t)b * max_nodes;
+  for (;;) {
+    // Next child of cur: the lowest index above `after` whose parent is cur.
+    int c = 0x7fffffff;
+    for (int i = after + 1 + tid; i < nn; i += kSThreads)
+      if (par[i] == cur) {
+        c = i;
+        break;
+      }
+    for (int o = 32; o > 0; o >>= 1) c = min(c, __shfl_xor(c, o));
+    __syncthreads();
+    if (lane == 0) ired[wave] = c;
+    __syncthreads();
+    c = ired[0];
+#pragma unroll
+    for (int w = 1; w < kSWaves; ++w) c = min(c, ired[w]);
+    if (c >= nn) break;
+    after = c;
+    const int x = draft[n0 + c];
+    bool take = false;
+    if (x >= 0 && x < V) {
+      const float px = dist_at<BF16>(P, x, kc) / P.Z;
+      take = u_accept[n0 + c] * Q[x] < px;
+    }
+    if (take) {
+      if (tid == 0) {
+        an[len] = c;
+        at[len] = x;
+      }
+      ++len;
+      cur = c;
+      after = -1;
+      P = softmax_of(static_cast<const unsigned char*>(logits) + (size_t)(n0 + c) * V * esz);
+      Q = qp + (size_t)(n0 + c) * V;
+    } else {
+      // Residual max(0, P - Q) into the other scratch row.
+      float* out = rows2 + (size_t)(rsel ^ 1) * V;
+      const float inv = 1.f / P.Z;
+      float s = 0.f;
+      for (int v0 = r0; v0 < r1; v0 += 8 * kBatch) {
+        float x[kBatch][8], q[kBatch][8];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          dist8<BF16, VEC>(P, min(v0 + 8 * j, V), V, kc, x[j]);
+          load8_f32<VEC>(Q, min(v0 + 8 * j, V), V, q[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          if (v0 + 8 * j >= r1) break;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            x[j][k] = fmaxf(x[j][k] * inv - q[j][k], 0.f);
+            s += x[j][k];
+          }
+          store8_f32<VEC>(out, v0 + 8 * j, V, x[j]);
+        }
+      }
+      const float z = block_sum(s, red);   // its barriers also order the row's writes
+      if (z > 0.f) {
+        rsel ^= 1;
+        P.row = nullptr;
+        P.R = out;
+        P.m = 0.f;
+        P.Z = z;
+      }
+    }
+  }
+
+  // Bonus token by inversion: the lowest v with sum_{w<=v} P(w) > u * Z.
+  // Each thread's run total (and its last entry with mass), an exclusive scan
+  // of the totals across the workgroup, then the one thread whose run holds
+  // the threshold scans it entry by entry.
+  const float thr = u_final[b] * P.Z;
+  float tot = 0.f;
+  int last_nz = -1;
+  for (int v0 = r0; v0 < r1; v0 += 8 * kBatch) {
+    float x[kBatch][8];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) dist8<BF16, VEC>(P, min(v0 + 8 * j, V), V, kc, x[j]);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (v0 + 8 * j >= r1) break;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        tot += x[j][k];
+        if (x[j][k] > 0.f && v0 + 8 * j + k < r1) last_nz = v0 + 8 * j + k;
+      }
+    }
+  }
+  float incl = tot;   // inclusive scan of the run totals, in thread order
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  int lnz = last_nz;
+  for (int o = 32; o > 0; o >>= 1) lnz = max(lnz, __shfl_xor(lnz, o));
+  __syncthreads();
+  if (lane == 63) red[wave] = incl;
+  if (lane == 0) ired[wave] = lnz;
+  __syncthreads();
+  // Thread t's interval is [start_t, start_{t+1}): the next thread's start
+  // (the total for the last), so the intervals tile [0, total) exactly and
+  // at most one thread holds the threshold whatever the rounding.
+  float before = 0.f, total = 0.f;
+  for (int w = 0; w < kSWaves; ++w) {
+    if (w < wave) before += red[w];
+    total += red[w];
+  }
+  const float start = before + (incl - tot);
+  float end = __shfl_down(start, 1);
+  if (lane == 63) end = wave + 1 < kSWaves ? before + red[wave] : total;
+  int fallback = -1;
+  for (int w = 0; w < kSWaves; ++w) fallback = max(fallback, ired[w]);
+  __syncthreads();
+  if (tid == 0) ired[0] = -1;
+  __syncthreads();
+  if (start <= thr && thr < end) {
+    int pick = -1;
+    float run = start;
+    for (int v0 = r0; v0 < r1 && pick < 0; v0 += 8) {
+      float x[8];
+      dist8<BF16, VEC>(P, v0, V, kc, x);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        run += x[k];
+        if (pick < 0 && v0 + k < r1 && run > thr) pick = v0 + k;
+      }
+    }
+    ired[0] = pick >= 0 ? pick : last_nz;   // rounding: the run's last entry with mass
+  }
+  __syncthreads();
+  int pick = ired[0];
+  if (pick < 0) pick = fallback >= 0 ? fallback : V - 1;   // total at or below the threshold
+  for (int pos = len + tid; pos < max_nodes; pos += kSThreads) {
+    an[pos] = -1;
+    at[pos] = -1;
+  }
+  if (tid == 0) {
+    accept_len[b] = len;
+    bonus_token[b] = pick;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_verify_sample(bool bf16, const void* logits, const void* root_logits,
+                                const float* draft_probs, const float* root_draft_probs,
+                                const int32_t* draft, const int32_t* parents,
+                                const int32_t* node_offsets, int B, int total_nodes,
+                                int max_nodes, int V, float temperature, const float* u_accept,
+                                const float* u_final, int32_t* accept_len, int32_t* accept_nodes,
+                                int32_t* accept_tokens, int32_t* bonus_token, void* workspace,
+                                hipStream_t stream) {
+  const float kc = kLog2e / temperature;
+  float* scratch = static_cast<float*>(workspace);
+  const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool vec = V % 8 == 0 && a16(logits) && a16(root_logits) && a16(draft_probs) &&
+                   a16(root_draft_probs) && a16(workspace);
+#define TA_SAMPLE_LAUNCH(BF, VC)                                                                \
+  hipLaunchKernelGGL((spec_sample_kernel<BF, VC>), dim3(B), dim3(kSThreads), 0, stream, logits, \
+                     root_logits, draft_probs, root_draft_probs, draft, parents, node_offsets,  \
+                     total_nodes, max_nodes, V, kc, u_accept, u_final, accept_len, accept_nodes, \
+                     accept_tokens, bonus_token, scratch)
+  if (bf16) {
+    if (vec) TA_SAMPLE_LAUNCH(true, true);
+    else TA_SAMPLE_LAUNCH(true, false);
+  } else {
+    if (vec) TA_SAMPLE_LAUNCH(false, true);
+    else TA_SAMPLE_LAUNCH(false, false);
+  }
+#undef TA_SAMPLE_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace ta
