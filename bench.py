@@ -430,8 +430,9 @@ def summarize_profiles(root):
     # tree_attn_mask_and_forward (the mask is built inside the forward kernel,
     # or by build_mask_kernel within the call for trees above 128 nodes).
     groups = {"tree_attn_mask_and_forward": ("fwd_bf16_kernel", "merge_bf16_kernel",
-                                             "build_mask_kernel"),
-              "tree_verify_greedy": ("argmax_partial_kernel", "path_select")}
+                                             "build_mask_kernel", "build_mask_large_kernel"),
+              "tree_verify_greedy": ("argmax_partial_kernel", "path_select", "large_rows_kernel",
+                                     "large_accept_kernel", "large_place_kernel")}
     hashes = {"tree_attn_mask_and_forward": src_hash("attn_fwd.hip"),
               "tree_verify_greedy": src_hash("verify.hip")}
     rec = {"calibration": {"copy_bytes": CALIB_BYTES, "fetch_kib": copy_f, "write_kib": copy_w,
