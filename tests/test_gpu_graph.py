@@ -107,3 +107,76 @@ def test_step_graph_replays_match_eager(shape):
         got = snapshot()
         for k in bufs:
             assert torch.equal(got[k], ref[k]), f"replay {rep}: {k} differs from the eager step"
+
+
+def test_large_verifier_and_sampler_graph_replays_match_eager():
+    """The verifier's many-workgroup path (a 1500-node tree: four kernels with
+    node-indexed scratch in the workspace) and the stochastic verifier,
+    captured in one graph: every replay equals the eager calls bit for bit,
+    with eager calls on other inputs into the same buffers in between."""
+    ta = lib()
+    d = torch.device("cuda")
+    V = 3000
+
+    def inputs(seed):
+        rng = np.random.default_rng(seed)
+        tree = synthetic.random_tree(rng, 1500, 3, 12, None).tolist()
+        c = synthetic.make_case("graph_large", prefix_lens=[0], trees=[tree], Hq=1, Hkv=1, D=8,
+                                dtype=torch.bfloat16, seed=seed, vocab=V, p_match=0.9)
+        s = synthetic.make_sampling_case([tree[:200], tree[:50]], V, seed=seed)
+        t = {"parents": torch.from_numpy(c.parents).to(d),
+             "noffs": torch.from_numpy(c.node_offsets).to(d),
+             "logits": c.logits.to(d), "draft": torch.from_numpy(c.draft).to(d),
+             "s_lg": s.logits.to(d), "s_rl": s.root_logits.to(d),
+             "s_q": torch.from_numpy(s.draft_probs).to(d),
+             "s_rq": torch.from_numpy(s.root_draft_probs).to(d),
+             "s_d": torch.from_numpy(s.draft).to(d), "s_p": torch.from_numpy(s.parents).to(d),
+             "s_o": torch.from_numpy(s.node_offsets).to(d),
+             "s_ua": torch.from_numpy(s.u_accept).to(d), "s_uf": torch.from_numpy(s.u_final).to(d)}
+        return c, s, t
+
+    ca, sa, a = inputs(21)
+    cb, sb, b = inputs(22)
+    n, mx = ca.total_nodes, ca.max_nodes
+    bufs = {"mask": torch.empty((n, ta.mask_words(mx)), dtype=torch.uint64, device=d),
+            "depth": torch.empty(n, dtype=torch.int32, device=d),
+            "status": torch.empty(1, dtype=torch.int32, device=d),
+            "pred": torch.empty(n, dtype=torch.int32, device=d),
+            "alen": torch.empty(1, dtype=torch.int32, device=d),
+            "anodes": torch.empty((1, mx), dtype=torch.int32, device=d),
+            "atok": torch.empty((1, mx), dtype=torch.int32, device=d),
+            "s_alen": torch.empty(2, dtype=torch.int32, device=d),
+            "s_anodes": torch.empty((2, sa.max_nodes), dtype=torch.int32, device=d),
+            "s_atok": torch.empty((2, sa.max_nodes), dtype=torch.int32, device=d),
+            "s_bonus": torch.empty(2, dtype=torch.int32, device=d)}
+    vws = torch.empty(ta.verify_workspace_size(n, mx, V), dtype=torch.uint8, device=d)
+    sws = torch.empty(ta.verify_sample_workspace_size(2, V), dtype=torch.uint8, device=d)
+
+    def step(t, s):
+        ta.build_mask(t["parents"], t["noffs"], mx, mask=bufs["mask"], depth=bufs["depth"],
+                      status=bufs["status"])
+        ta.verify_greedy(t["logits"], t["draft"], bufs["mask"], t["noffs"], mx, workspace=vws,
+                         target_argmax=bufs["pred"], accept_len=bufs["alen"],
+                         accept_nodes=bufs["anodes"], accept_tokens=bufs["atok"])
+        ta.verify_sample(t["s_lg"], t["s_rl"], t["s_q"], t["s_rq"], t["s_d"], t["s_p"], t["s_o"],
+                         s.max_nodes, s.temperature, t["s_ua"], t["s_uf"], workspace=sws,
+                         accept_len=bufs["s_alen"], accept_nodes=bufs["s_anodes"],
+                         accept_tokens=bufs["s_atok"], bonus_token=bufs["s_bonus"])
+
+    step(a, sa)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in bufs.items()}
+    _, rlen, rnodes, _ = oracle.verify_greedy(ca.logits, ca.draft, ca.parents, ca.node_offsets, mx)
+    np.testing.assert_array_equal(ref["alen"].cpu().numpy(), rlen)
+    np.testing.assert_array_equal(ref["anodes"].cpu().numpy(), rnodes)
+    assert int(rlen[0]) >= 2
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(a, sa)
+    for rep in range(4):
+        step(b, sb)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in bufs:
+            assert torch.equal(bufs[k], ref[k]), f"replay {rep}: {k} differs from the eager call"
