@@ -939,7 +939,7 @@ def main():
               for k, v in (("lg", sc.logits), ("rl", sc.root_logits), ("q", sc.draft_probs),
                            ("rq", sc.root_draft_probs), ("d", sc.draft), ("p", sc.parents),
                            ("o", sc.node_offsets), ("ua", sc.u_accept), ("uf", sc.u_final))}
-        sws = torch.empty(max(ta.verify_sample_workspace_size(B, V), 16), dtype=torch.uint8,
+        sws = torch.empty(max(ta.verify_sample_workspace_size(B, sum_n, V), 16), dtype=torch.uint8,
                           device=dev)
         so = [torch.empty(B, dtype=torch.int32, device=dev),
               torch.empty((B, max_nodes), dtype=torch.int32, device=dev),

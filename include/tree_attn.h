@@ -386,10 +386,11 @@ TA_API int tree_kv_commit(int dtype, const void* k_tree, const void* v_tree,
                           int64_t total_cache, int32_t* commit_status, void* stream);
 
 /*
- * Bytes of device workspace tree_verify_sample needs (two fp32 rows of V per
- * sequence).  Pure host arithmetic.
+ * Bytes of device workspace tree_verify_sample needs: two fp32 rows of V per
+ * sequence, then 256 (max, sum) float pairs per logits row (sum_N + B rows).
+ * Pure host arithmetic.
  */
-TA_API size_t tree_verify_sample_workspace_size(int32_t B, int32_t V);
+TA_API size_t tree_verify_sample_workspace_size(int32_t B, int32_t total_nodes, int32_t V);
 
 /*
  * Stochastic verification: rejection sampling down the tree, which keeps the
@@ -423,8 +424,8 @@ TA_API size_t tree_verify_sample_workspace_size(int32_t B, int32_t V);
  *                  [B][max_nodes]: the accepted path, local ids root first,
  *                  and its draft tokens, -1 padded.
  *   bonus_token    out int32 [B]: the token drawn after the accepted path.
- *   workspace      at least tree_verify_sample_workspace_size(B, V) bytes,
- *                  16-byte aligned, any content.
+ *   workspace      at least tree_verify_sample_workspace_size(B, sum_N, V)
+ *                  bytes, 16-byte aligned, any content.
  * The walk: with P the target's and Q the draft's distribution above the
  * roots, the children of the current node are tested in increasing index
  * order; child c with token x is accepted iff u_accept[c] * Q(x) < P(x) and
@@ -435,7 +436,8 @@ TA_API size_t tree_verify_sample_workspace_size(int32_t B, int32_t V);
  * two sides of a test, or u_final and a cumulative boundary, are within
  * rounding of each other).  A tree with an out-of-range parent or a cycle,
  * or a sequence whose offsets do not decode, is walked as empty.  Asynchronous
- * on `stream`; one workgroup per sequence.
+ * on `stream`: one workgroup per logits row computes its softmax statistics
+ * per vocabulary segment, then one workgroup per sequence walks the tree.
  */
 TA_API int tree_verify_sample(int logits_dtype, const void* logits, const void* root_logits,
                               const float* draft_probs, const float* root_draft_probs,

@@ -150,7 +150,7 @@ def test_large_verifier_and_sampler_graph_replays_match_eager():
             "s_atok": torch.empty((2, sa.max_nodes), dtype=torch.int32, device=d),
             "s_bonus": torch.empty(2, dtype=torch.int32, device=d)}
     vws = torch.empty(ta.verify_workspace_size(n, mx, V), dtype=torch.uint8, device=d)
-    sws = torch.empty(ta.verify_sample_workspace_size(2, V), dtype=torch.uint8, device=d)
+    sws = torch.empty(ta.verify_sample_workspace_size(2, 250, V), dtype=torch.uint8, device=d)
 
     def step(t, s):
         ta.build_mask(t["parents"], t["noffs"], mx, mask=bufs["mask"], depth=bufs["depth"],

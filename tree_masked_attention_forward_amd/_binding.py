@@ -84,7 +84,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tree_verify_greedy_next.argtypes = [ctypes.c_int] + [_c_void_p] * 5 + [_i32] * 4 + [
         _c_void_p] * 6 + [ctypes.c_size_t, _c_void_p]
     lib.tree_verify_sample_workspace_size.restype = ctypes.c_size_t
-    lib.tree_verify_sample_workspace_size.argtypes = [_i32, _i32]
+    lib.tree_verify_sample_workspace_size.argtypes = [_i32, _i32, _i32]
     lib.tree_verify_sample.restype = ctypes.c_int
     lib.tree_verify_sample.argtypes = [ctypes.c_int] + [_c_void_p] * 7 + [_i32] * 4 + [
         ctypes.c_float] + [_c_void_p] * 7 + [ctypes.c_size_t, _c_void_p]
@@ -428,8 +428,8 @@ def verify_greedy_next(logits: torch.Tensor, root_logits: torch.Tensor,
     return target_argmax, accept_len, accept_nodes, accept_tokens, bonus_token
 
 
-def verify_sample_workspace_size(B: int, V: int) -> int:
-    return int(load_library().tree_verify_sample_workspace_size(B, V))
+def verify_sample_workspace_size(B: int, total_nodes: int, V: int) -> int:
+    return int(load_library().tree_verify_sample_workspace_size(B, total_nodes, V))
 
 
 def verify_sample(logits: torch.Tensor, root_logits: torch.Tensor, draft_probs: torch.Tensor,
@@ -474,7 +474,7 @@ def verify_sample(logits: torch.Tensor, root_logits: torch.Tensor, draft_probs: 
         accept_tokens = torch.empty((B, max_nodes), dtype=torch.int32, device=dev)
     if bonus_token is None:
         bonus_token = torch.empty(B, dtype=torch.int32, device=dev)
-    ws_bytes = verify_sample_workspace_size(B, V)
+    ws_bytes = verify_sample_workspace_size(B, total, V)
     if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     ws_len = workspace.numel() * workspace.element_size()

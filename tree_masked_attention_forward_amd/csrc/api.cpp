@@ -395,9 +395,9 @@ int tree_kv_commit(int dtype, const void* k_tree, const void* v_tree,
                                          static_cast<hipStream_t>(stream)));
 }
 
-size_t tree_verify_sample_workspace_size(int32_t B, int32_t V) {
-  if (B <= 0 || V <= 0) return 0;
-  return (size_t)B * 2 * (size_t)V * sizeof(float);
+size_t tree_verify_sample_workspace_size(int32_t B, int32_t total_nodes, int32_t V) {
+  if (B <= 0 || total_nodes < 0 || V <= 0) return 0;
+  return ta::verify_sample_workspace_bytes(B, total_nodes, V);
 }
 
 int tree_verify_sample(int logits_dtype, const void* logits, const void* root_logits,
@@ -417,7 +417,7 @@ int tree_verify_sample(int logits_dtype, const void* logits, const void* root_lo
     return TA_ERR_INVALID_ARG;
   if (total_nodes > 0 && (!logits || !draft_probs || !draft_tokens || !parents || !u_accept))
     return TA_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < tree_verify_sample_workspace_size(B, V) ||
+  if (!workspace || workspace_bytes < tree_verify_sample_workspace_size(B, total_nodes, V) ||
       misaligned16(workspace))
     return TA_ERR_WORKSPACE;
   return hip_status(ta::launch_verify_sample(

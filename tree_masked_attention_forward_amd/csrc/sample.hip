@@ -7,18 +7,27 @@
 // Chen et al. 2023) walked child by child down the tree, as in SpecInfer's
 // multi-step speculative sampling (Miao et al. 2024).
 //
-// One workgroup per sequence walks its tree.  The current distribution P is
-// either the softmax of a target logits row at the given temperature, kept
-// implicit (its row, max and sum), or an explicit residual in a per-sequence
-// scratch row.  Testing child c with draft token x reads P(x) and the draft
-// probability Q(x); it is accepted iff u_c * Q(x) < P(x).  An accepted child
-// becomes the current node (one pass over its logits row for the max and
-// sum); a rejected one turns P into max(0, P - Q) renormalised (one pass that
-// writes the other scratch row, so P survives when that residual is all
-// zero).  The bonus token is drawn from P by inversion: wave totals over
-// contiguous vocabulary segments, then a scan of the one segment holding
-// u_final * sum(P).  The walk's decisions are uniform: every thread takes them
-// from values in LDS.
+// Two kernels.  softmax_stats_kernel (one workgroup per logits row, all rows
+// at once) leaves, for every row, the softmax statistics of each vocabulary
+// segment: (max, sum of exp2 relative to it) in log2 units at the given
+// temperature.  spec_sample_kernel (one workgroup per sequence) then walks the
+// tree: the current distribution P is either a target row's softmax, kept
+// implicit (its row, max and sum, merged from the segment statistics without
+// touching the row), or an explicit residual in a per-sequence scratch row;
+// LDS keeps P's mass per segment.  Testing child c with draft token x reads
+// P(x) and the draft probability Q(x) and accepts iff u_c * Q(x) < P(x).  An
+// accepted child becomes the current node (its statistics merged); a rejected
+// one turns P into max(0, P - Q) renormalised (one pass over the vocabulary,
+// written to the other scratch row so that P survives when the residual is
+// all zero).  The bonus token is drawn from P by inversion: the segment
+// holding u_final * sum(P) from the segment masses, then one wave scans that
+// segment.  The walk's decisions are uniform: every thread takes them from
+// values in LDS.
+//
+// Vocabulary layout shared by both kernels: thread t of a 1024-thread
+// workgroup owns the run [t*C, t*C + C), C = ceil(V / 1024) rounded up to 8;
+// a segment is four consecutive runs (4C entries), so V has at most 256
+// segments and a segment's statistics combine four neighbouring lanes.
 #include "internal.h"
 
 namespace ta {
@@ -26,6 +35,8 @@ namespace {
 
 constexpr int kSThreads = 1024;
 constexpr int kSWaves = kSThreads / 64;
+constexpr int kRunsPerSeg = 4;
+constexpr int kMaxSeg = kSThreads / kRunsPerSeg;   // 256
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInfS = -__builtin_inff();
 
@@ -151,6 +162,97 @@ __device__ inline void merge_ms(float& m, float& s, float m2, float s2) {
   m = mm;
 }
 
+// Running (max, sum of exp2(x - max)) over this thread's run of a logits row
+// (x = logit * kc): a bf16 row with aligned 16-byte groups in one batch of raw
+// loads (4 registers per group, unpacked one at a time), anything else in
+// batches of four groups.
+template <bool BF16, bool VEC>
+__device__ inline void run_stats(const void* row, int r0, int r1, int V, float kc, float& m,
+                                 float& s) {
+  m = kNegInfS;
+  s = 0.f;
+  auto absorb = [&](float (&x)[8]) {
+    float cm = kNegInfS;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      x[k] *= kc;
+      cm = fmaxf(cm, x[k]);
+    }
+    if (cm > m) {
+      s = m == kNegInfS ? 0.f : s * __builtin_amdgcn_exp2f(m - cm);
+      m = cm;
+    }
+    if (m != kNegInfS) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s += __builtin_amdgcn_exp2f(x[k] - m);
+    }
+  };
+  if constexpr (BF16 && VEC) {
+    constexpr int kB = 16;
+    for (int v0 = r0; v0 < r1; v0 += 8 * kB) {
+      u32x4s_t w[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j)
+        w[j] = *reinterpret_cast<const u32x4s_t*>(static_cast<const uint16_t*>(row) +
+                                                  min(v0 + 8 * j, V - 8));
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        if (v0 + 8 * j >= r1) break;
+        float x[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[2 * k] = __uint_as_float(w[j][k] << 16);
+          x[2 * k + 1] = __uint_as_float(w[j][k] & 0xffff0000u);
+        }
+        absorb(x);
+      }
+    }
+  } else {
+    constexpr int kB = 4;
+    for (int v0 = r0; v0 < r1; v0 += 8 * kB) {
+      float x[kB][8];
+#pragma unroll
+      for (int j = 0; j < kB; ++j) load8_logits<BF16, VEC>(row, min(v0 + 8 * j, V), V, x[j]);
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        if (v0 + 8 * j >= r1) break;
+        absorb(x[j]);
+      }
+    }
+  }
+}
+
+__device__ inline int run_len(int V) { return ((V + kSThreads - 1) / kSThreads + 7) / 8 * 8; }
+
+// Segment statistics of every logits row: row r < total_nodes is node row r,
+// the rest are the prefix rows.  stats[r][k] = (max, sum) of segment k.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kSThreads) void softmax_stats_kernel(
+    const void* __restrict__ logits, const void* __restrict__ root_logits, int total_nodes,
+    int V, float kc, float2* __restrict__ stats) {
+  const int r = blockIdx.x;
+  const size_t esz = BF16 ? 2 : 4;
+  const void* row = r < total_nodes
+                        ? static_cast<const void*>(static_cast<const unsigned char*>(logits) +
+                                                   (size_t)r * V * esz)
+                        : static_cast<const void*>(static_cast<const unsigned char*>(root_logits) +
+                                                   (size_t)(r - total_nodes) * V * esz);
+  const int C = run_len(V);
+  const int tid = threadIdx.x;
+  const int r0 = tid * C;
+  const int r1 = min(V, r0 + C);
+  float m, s;
+  run_stats<BF16, VEC>(row, r0, r1, V, kc, m, s);
+  // the four runs of a segment sit in lanes 4k .. 4k+3 of one wave
+  for (int o = 1; o < kRunsPerSeg; o <<= 1) {
+    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+    merge_ms(m, s, m2, s2);
+  }
+  const int nseg = (V + kRunsPerSeg * C - 1) / (kRunsPerSeg * C);
+  if ((tid & (kRunsPerSeg - 1)) == 0 && tid / kRunsPerSeg < nseg)
+    stats[(size_t)r * kMaxSeg + tid / kRunsPerSeg] = make_float2(m, s);
+}
+
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
     const void* __restrict__ logits, const void* __restrict__ root_logits,
@@ -160,9 +262,10 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
     const float* __restrict__ u_accept, const float* __restrict__ u_final,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
     int32_t* __restrict__ accept_tokens, int32_t* __restrict__ bonus_token,
-    float* __restrict__ scratch) {
+    float* __restrict__ scratch, const float2* __restrict__ stats) {
   __shared__ int32_t par[TA_MAX_NODES];
   __shared__ int32_t jmp[TA_MAX_NODES];
+  __shared__ float segm[2][kMaxSeg];   // P's mass per segment (two copies, see sel)
   __shared__ float red[kSWaves];
   __shared__ float red2[kSWaves];
   __shared__ int ired[kSWaves];
@@ -218,63 +321,42 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
   // Two scratch rows per sequence; rsel: the one holding an explicit P.
   float* const rows2 = scratch + (size_t)b * 2 * V;
   int rsel = 0;
-
-  // Every pass over the vocabulary gives thread t the contiguous run
-  // [t*C, t*C + C) (C a multiple of 8), taken 8 entries at a time, four
-  // groups' loads issued before any is used.
-  const int C = ((V + kSThreads - 1) / kSThreads + 7) / 8 * 8;
+  int sel = 0;   // segm[sel]: the current P's segment masses
+  const int C = run_len(V);
+  const int SEG = kRunsPerSeg * C;
+  const int nseg = (V + SEG - 1) / SEG;
   const int r0 = tid * C;
   const int r1 = min(V, r0 + C);
-  constexpr int kBatch = 4;
+  constexpr int kBatch = 4;   // groups of 8 per batch in the residual pass
 
-  // Implicit softmax of a logits row: its max and sum in one pass (each
-  // thread keeps a running max and a sum rescaled when the max moves).
-  auto softmax_of = [&](const void* row) {
+  // Implicit softmax of logits row r: max and sum merged from its segment
+  // statistics, and the segment masses relative to that max.
+  auto softmax_of = [&](const void* row, int r) {
     Dist d;
     d.row = row;
     d.R = nullptr;
     float m = kNegInfS, s = 0.f;
-    for (int v0 = r0; v0 < r1; v0 += 8 * kBatch) {
-      float x[kBatch][8];
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) load8_logits<BF16, VEC>(row, min(v0 + 8 * j, V), V, x[j]);
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        if (v0 + 8 * j >= r1) break;
-        float cm = kNegInfS;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          x[j][k] *= kc;
-          cm = fmaxf(cm, x[j][k]);
-        }
-        if (cm > m) {
-          s = m == kNegInfS ? 0.f : s * __builtin_amdgcn_exp2f(m - cm);
-          m = cm;
-        }
-        if (m != kNegInfS) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) s += __builtin_amdgcn_exp2f(x[j][k] - m);
-        }
-      }
+    if (tid < nseg) {
+      const float2 st = stats[(size_t)r * kMaxSeg + tid];
+      m = st.x;
+      s = st.y;
     }
-    for (int o = 32; o > 0; o >>= 1) {
-      const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
-      merge_ms(m, s, m2, s2);
-    }
+    float mm = wave_max_f(m);
     __syncthreads();
-    if (lane == 0) {
-      red[wave] = m;
-      red2[wave] = s;
-    }
+    if (lane == 0) red[wave] = mm;
     __syncthreads();
-    float bm = red[0], bs = red2[0];
-    for (int w = 1; w < kSWaves; ++w) merge_ms(bm, bs, red[w], red2[w]);
-    d.m = bm;
-    d.Z = bs;
+    mm = red[0];
+#pragma unroll
+    for (int w = 1; w < kSWaves; ++w) mm = fmaxf(mm, red[w]);
+    const float mass = (tid < nseg && m != kNegInfS) ? s * __builtin_amdgcn_exp2f(m - mm) : 0.f;
+    if (tid < kMaxSeg) segm[sel][tid] = mass;
+    d.m = mm;
+    d.Z = block_sum(mass, red);   // its barriers also publish segm
     return d;
   };
 
-  Dist P = softmax_of(static_cast<const unsigned char*>(root_logits) + (size_t)b * V * esz);
+  Dist P = softmax_of(static_cast<const unsigned char*>(root_logits) + (size_t)b * V * esz,
+                      total_nodes + b);
   const float* Q = root_qp + (size_t)b * V;
   int cur = -1;     // current node (-1: above the roots)
   int after = -1;   // children of cur with index <= after are done
@@ -312,18 +394,20 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
       ++len;
       cur = c;
       after = -1;
-      P = softmax_of(static_cast<const unsigned char*>(logits) + (size_t)(n0 + c) * V * esz);
+      P = softmax_of(static_cast<const unsigned char*>(logits) + (size_t)(n0 + c) * V * esz,
+                     n0 + c);
       Q = qp + (size_t)(n0 + c) * V;
     } else {
-      // Residual max(0, P - Q) into the other scratch row.
+      // Residual max(0, P - Q) into the other scratch row, with its segment
+      // masses into the other copy of segm.
       float* out = rows2 + (size_t)(rsel ^ 1) * V;
       const float inv = 1.f / P.Z;
       float s = 0.f;
       for (int v0 = r0; v0 < r1; v0 += 8 * kBatch) {
-        float x[kBatch][8], q[kBatch][8];
+        float xv[kBatch][8], q[kBatch][8];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-          dist8<BF16, VEC>(P, min(v0 + 8 * j, V), V, kc, x[j]);
+          dist8<BF16, VEC>(P, min(v0 + 8 * j, V), V, kc, xv[j]);
           load8_f32<VEC>(Q, min(v0 + 8 * j, V), V, q[j]);
         }
 #pragma unroll
@@ -331,15 +415,19 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
           if (v0 + 8 * j >= r1) break;
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            x[j][k] = fmaxf(x[j][k] * inv - q[j][k], 0.f);
-            s += x[j][k];
+            xv[j][k] = fmaxf(xv[j][k] * inv - q[j][k], 0.f);
+            if (v0 + 8 * j + k < r1) s += xv[j][k];
           }
-          store8_f32<VEC>(out, v0 + 8 * j, V, x[j]);
+          store8_f32<VEC>(out, v0 + 8 * j, V, xv[j]);
         }
       }
+      float seg = s;
+      for (int o = 1; o < kRunsPerSeg; o <<= 1) seg += __shfl_xor(seg, o);
+      if ((tid & (kRunsPerSeg - 1)) == 0) segm[sel ^ 1][tid / kRunsPerSeg] = seg;
       const float z = block_sum(s, red);   // its barriers also order the row's writes
       if (z > 0.f) {
         rsel ^= 1;
+        sel ^= 1;
         P.row = nullptr;
         P.R = out;
         P.m = 0.f;
@@ -349,70 +437,92 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
   }
 
   // Bonus token by inversion: the lowest v with sum_{w<=v} P(w) > u * Z.
-  // Each thread's run total (and its last entry with mass), an exclusive scan
-  // of the totals across the workgroup, then the one thread whose run holds
-  // the threshold scans it entry by entry.
-  const float thr = u_final[b] * P.Z;
-  float tot = 0.f;
-  int last_nz = -1;
-  for (int v0 = r0; v0 < r1; v0 += 8 * kBatch) {
-    float x[kBatch][8];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) dist8<BF16, VEC>(P, min(v0 + 8 * j, V), V, kc, x[j]);
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      if (v0 + 8 * j >= r1) break;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        tot += x[j][k];
-        if (x[j][k] > 0.f && v0 + 8 * j + k < r1) last_nz = v0 + 8 * j + k;
-      }
-    }
-  }
-  float incl = tot;   // inclusive scan of the run totals, in thread order
+  // The segment holding the threshold from an exclusive scan of the segment
+  // masses (intervals [start_k, start_{k+1}) tile [0, total) exactly, so at
+  // most one segment holds it), then wave 0 scans that segment 512 entries at
+  // a time (8 per lane).  If rounding leaves the threshold at or past the
+  // total, or inside the segment past its recomputed entries, the last entry
+  // with mass of the last segment with mass is taken.
+  __shared__ int s_seg;
+  float mass = tid < nseg ? segm[sel][tid] : 0.f;
+  float incl = mass;
   for (int o = 1; o < 64; o <<= 1) {
     const float t = __shfl_up(incl, o);
     if (lane >= o) incl += t;
   }
-  int lnz = last_nz;
-  for (int o = 32; o > 0; o >>= 1) lnz = max(lnz, __shfl_xor(lnz, o));
   __syncthreads();
   if (lane == 63) red[wave] = incl;
-  if (lane == 0) ired[wave] = lnz;
+  if (tid == 0) s_seg = -1;
   __syncthreads();
-  // Thread t's interval is [start_t, start_{t+1}): the next thread's start
-  // (the total for the last), so the intervals tile [0, total) exactly and
-  // at most one thread holds the threshold whatever the rounding.
   float before = 0.f, total = 0.f;
   for (int w = 0; w < kSWaves; ++w) {
     if (w < wave) before += red[w];
     total += red[w];
   }
-  const float start = before + (incl - tot);
+  const float start = before + (incl - mass);
   float end = __shfl_down(start, 1);
   if (lane == 63) end = wave + 1 < kSWaves ? before + red[wave] : total;
-  int fallback = -1;
-  for (int w = 0; w < kSWaves; ++w) fallback = max(fallback, ired[w]);
+  const float thr = u_final[b] * total;
+  if (tid < nseg && start <= thr && thr < end) s_seg = tid;
+  // the last segment with mass, for the rounding case
+  int lastm = (tid < nseg && mass > 0.f) ? tid : -1;
+  for (int o = 32; o > 0; o >>= 1) lastm = max(lastm, __shfl_xor(lastm, o));
+  if (lane == 0) ired[wave] = lastm;
   __syncthreads();
-  if (tid == 0) ired[0] = -1;
+  int kseg = s_seg;
+  const bool exact = kseg >= 0;
+  if (!exact) {
+    for (int w = 0; w < kSWaves; ++w) kseg = max(kseg, ired[w]);
+  }
+  int pick = -1;
   __syncthreads();
-  if (start <= thr && thr < end) {
-    int pick = -1;
-    float run = start;
-    for (int v0 = r0; v0 < r1 && pick < 0; v0 += 8) {
-      float x[8];
-      dist8<BF16, VEC>(P, v0, V, kc, x);
+  if (exact && tid == kseg) red[1] = start;   // the mass before the segment
+  __syncthreads();
+  if (wave == 0 && kseg >= 0) {
+    float run = exact ? red[1] : 0.f;
+    const int e0 = kseg * SEG;
+    const int e1 = min(V, e0 + SEG);
+    int lastnz = -1;
+    for (int v0 = e0; v0 < e1; v0 += 512) {
+      const int v = v0 + 8 * lane;
+      float xv[8];
+      dist8<BF16, VEC>(P, min(v, V), V, kc, xv);
+      float ls = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        run += x[k];
-        if (pick < 0 && v0 + k < r1 && run > thr) pick = v0 + k;
+        if (v + k >= e1) xv[k] = 0.f;
+        ls += xv[k];
+        if (xv[k] > 0.f) lastnz = max(lastnz, v + k);
       }
+      float li = ls;   // inclusive scan over the lanes, in lane order
+      for (int o = 1; o < 64; o <<= 1) {
+        const float t = __shfl_up(li, o);
+        if (lane >= o) li += t;
+      }
+      if (exact && pick < 0) {
+        const uint64_t hit = __ballot(run + li > thr);
+        if (hit) {
+          const int hl = __builtin_ctzll(hit);
+          if (lane == hl) {
+            float r = run + li - ls;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              r += xv[k];
+              if (pick < 0 && r > thr) pick = v + k;
+            }
+            if (pick < 0) pick = v + 7 < e1 ? v + 7 : e1 - 1;
+          }
+          pick = __shfl(pick, hl);
+        }
+      }
+      run += __shfl(li, 63);
     }
-    ired[0] = pick >= 0 ? pick : last_nz;   // rounding: the run's last entry with mass
+    for (int o = 32; o > 0; o >>= 1) lastnz = max(lastnz, __shfl_xor(lastnz, o));
+    if (pick < 0) pick = lastnz >= 0 ? lastnz : e1 - 1;
+    if (lane == 0) ired[0] = pick;
   }
   __syncthreads();
-  int pick = ired[0];
-  if (pick < 0) pick = fallback >= 0 ? fallback : V - 1;   // total at or below the threshold
+  pick = kseg >= 0 ? ired[0] : V - 1;
   for (int pos = len + tid; pos < max_nodes; pos += kSThreads) {
     an[pos] = -1;
     at[pos] = -1;
@@ -425,6 +535,11 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
 
 }  // namespace
 
+size_t verify_sample_workspace_bytes(int B, int total_nodes, int V) {
+  const size_t rows = ((size_t)B * 2 * V * sizeof(float) + 255) & ~(size_t)255;
+  return rows + ((size_t)total_nodes + B) * kMaxSeg * sizeof(float2);
+}
+
 hipError_t launch_verify_sample(bool bf16, const void* logits, const void* root_logits,
                                 const float* draft_probs, const float* root_draft_probs,
                                 const int32_t* draft, const int32_t* parents,
@@ -434,15 +549,24 @@ hipError_t launch_verify_sample(bool bf16, const void* logits, const void* root_
                                 int32_t* accept_tokens, int32_t* bonus_token, void* workspace,
                                 hipStream_t stream) {
   const float kc = kLog2e / temperature;
+  // [two residual rows per sequence | segment statistics per logits row]
   float* scratch = static_cast<float*>(workspace);
+  float2* stats = reinterpret_cast<float2*>(
+      static_cast<unsigned char*>(workspace) +
+      (((size_t)B * 2 * V * sizeof(float) + 255) & ~(size_t)255));
   const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   const bool vec = V % 8 == 0 && a16(logits) && a16(root_logits) && a16(draft_probs) &&
                    a16(root_draft_probs) && a16(workspace);
+  const unsigned rows = (unsigned)(total_nodes + B);
 #define TA_SAMPLE_LAUNCH(BF, VC)                                                                \
-  hipLaunchKernelGGL((spec_sample_kernel<BF, VC>), dim3(B), dim3(kSThreads), 0, stream, logits, \
-                     root_logits, draft_probs, root_draft_probs, draft, parents, node_offsets,  \
-                     total_nodes, max_nodes, V, kc, u_accept, u_final, accept_len, accept_nodes, \
-                     accept_tokens, bonus_token, scratch)
+  do {                                                                                         \
+    hipLaunchKernelGGL((softmax_stats_kernel<BF, VC>), dim3(rows), dim3(kSThreads), 0, stream, \
+                       logits, root_logits, total_nodes, V, kc, stats);                        \
+    hipLaunchKernelGGL((spec_sample_kernel<BF, VC>), dim3(B), dim3(kSThreads), 0, stream,      \
+                       logits, root_logits, draft_probs, root_draft_probs, draft, parents,     \
+                       node_offsets, total_nodes, max_nodes, V, kc, u_accept, u_final,         \
+                       accept_len, accept_nodes, accept_tokens, bonus_token, scratch, stats);  \
+  } while (0)
   if (bf16) {
     if (vec) TA_SAMPLE_LAUNCH(true, true);
     else TA_SAMPLE_LAUNCH(true, false);
