@@ -117,6 +117,21 @@ def test_sample_many_sequences_and_reranked_orders(ta):
     assert checked >= 28
 
 
+@pytest.mark.parametrize("dtype,V,noise,scale", [(torch.bfloat16, 128256, 6.0, 4.0),
+                                                 (torch.float32, 999, 3.0, 2.0)])
+def test_sample_wide_fanout_many_rejections(ta, dtype, V, noise, scale):
+    """Forty roots and forty children under root 0 (a forest plus a wide
+    node), with a draft far from the target: long runs of rejections at one
+    node, past the kernel's chain of eight kept residual steps (the ninth
+    writes the residual out and the chain restarts from it)."""
+    trees = [[-1] * 40 + [0] * 40, [-1] + [0] * 30 + list(range(1, 31))]
+    c = synthetic.make_sampling_case(trees, V, dtype=dtype, seed=5, temperature=1.0,
+                                     noise=noise, scale=scale)
+    got = _run(ta, c)
+    checked, ralen = _compare(got, c, f"wide fan-out {dtype} V={V}")
+    assert checked == 2   # (41 rejections in both cases, margins above the bar)
+
+
 def test_sample_draft_equal_to_target_accepts_first_children(ta):
     """With the draft given as the target's own distribution every tested
     child is accepted (u < 0.999 and the two sides differ only by rounding),

@@ -328,6 +328,24 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
   const int r0 = tid * C;
   const int r1 = min(V, r0 + C);
   constexpr int kBatch = 4;   // groups of 8 per batch in the residual pass
+  // Rejections since P's base (an implicit softmax row or an explicit
+  // residual row) are kept as a chain of normalisers rather than written out:
+  // P(v) = base(v) / Z_base, then max(0, p - Q(v)) * izc[i] for each of the
+  // `chain` steps, all with the current node's Q.  The rejection after
+  // kChain steps writes the residual out as a new explicit base instead.
+  constexpr int kChain = 8;
+  int chain = 0;
+  float izc[kChain];
+#pragma unroll
+  for (int i = 0; i < kChain; ++i) izc[i] = 0.f;
+  // Normalised P after `steps` chain steps, from the base's unnormalised value.
+  auto pchain = [&](float bv, float q, float invb, int steps) {
+    float p = bv * invb;
+#pragma unroll
+    for (int i = 0; i < kChain; ++i)
+      if (i < steps) p = fmaxf(p - q, 0.f) * izc[i];
+    return p;
+  };
 
   // Implicit softmax of logits row r: max and sum merged from its segment
   // statistics, and the segment masses relative to that max.
@@ -383,8 +401,9 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
     const int x = draft[n0 + c];
     bool take = false;
     if (x >= 0 && x < V) {
-      const float px = dist_at<BF16>(P, x, kc) / P.Z;
-      take = u_accept[n0 + c] * Q[x] < px;
+      const float qx = Q[x];
+      const float px = pchain(dist_at<BF16>(P, x, kc), qx, 1.f / P.Z, chain);
+      take = u_accept[n0 + c] * qx < px;
     }
     if (take) {
       if (tid == 0) {
@@ -394,14 +413,17 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
       ++len;
       cur = c;
       after = -1;
+      chain = 0;
       P = softmax_of(static_cast<const unsigned char*>(logits) + (size_t)(n0 + c) * V * esz,
                      n0 + c);
       Q = qp + (size_t)(n0 + c) * V;
     } else {
-      // Residual max(0, P - Q) into the other scratch row, with its segment
-      // masses into the other copy of segm.
+      // Residual max(0, P - Q): its sum and segment masses (into the other
+      // copy of segm); written out to the other scratch row only when the
+      // chain is full.
+      const bool spill = chain == kChain;
       float* out = rows2 + (size_t)(rsel ^ 1) * V;
-      const float inv = 1.f / P.Z;
+      const float invb = 1.f / P.Z;
       float s = 0.f;
       for (int v0 = r0; v0 < r1; v0 += 8 * kBatch) {
         float xv[kBatch][8], q[kBatch][8];
@@ -415,10 +437,10 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
           if (v0 + 8 * j >= r1) break;
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            xv[j][k] = fmaxf(xv[j][k] * inv - q[j][k], 0.f);
+            xv[j][k] = fmaxf(pchain(xv[j][k], q[j][k], invb, chain) - q[j][k], 0.f);
             if (v0 + 8 * j + k < r1) s += xv[j][k];
           }
-          store8_f32<VEC>(out, v0 + 8 * j, V, xv[j]);
+          if (spill) store8_f32<VEC>(out, v0 + 8 * j, V, xv[j]);
         }
       }
       float seg = s;
@@ -426,12 +448,20 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
       if ((tid & (kRunsPerSeg - 1)) == 0) segm[sel ^ 1][tid / kRunsPerSeg] = seg;
       const float z = block_sum(s, red);   // its barriers also order the row's writes
       if (z > 0.f) {
-        rsel ^= 1;
         sel ^= 1;
-        P.row = nullptr;
-        P.R = out;
-        P.m = 0.f;
-        P.Z = z;
+        if (spill) {
+          rsel ^= 1;
+          P.row = nullptr;
+          P.R = out;
+          P.m = 0.f;
+          P.Z = z;
+          chain = 0;
+        } else {
+#pragma unroll
+          for (int i = 0; i < kChain; ++i)
+            if (i == chain) izc[i] = 1.f / z;
+          ++chain;
+        }
       }
     }
   }
@@ -483,10 +513,18 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
     const int e0 = kseg * SEG;
     const int e1 = min(V, e0 + SEG);
     int lastnz = -1;
+    const float invb = 1.f / P.Z;
     for (int v0 = e0; v0 < e1; v0 += 512) {
       const int v = v0 + 8 * lane;
       float xv[8];
       dist8<BF16, VEC>(P, min(v, V), V, kc, xv);
+      if (chain > 0) {
+        // the segment masses are those of the last residual, max(0, P' - Q)
+        float q[8];
+        load8_f32<VEC>(Q, min(v, V), V, q);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) xv[k] = fmaxf(pchain(xv[k], q[k], invb, chain - 1) - q[k], 0.f);
+      }
       float ls = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
