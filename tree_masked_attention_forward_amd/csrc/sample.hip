@@ -226,11 +226,19 @@ __device__ inline int run_len(int V) { return ((V + kSThreads - 1) / kSThreads +
 
 // Segment statistics of every logits row: row r < total_nodes is node row r,
 // the rest are the prefix rows.  stats[r][k] = (max, sum) of segment k.
+// Segment statistics of every logits row: row r < total_nodes is node row r,
+// the rest are the prefix rows.  stats[r][k] = (max, sum) of segment k.  Four
+// 256-thread workgroups per row, workgroup q taking runs 256q .. 256q + 255
+// (segments 64q .. 64q + 63), so a row's exponentials spread over four CUs.
+constexpr int kStatsThreads = 256;
+constexpr int kStatsSplit = kSThreads / kStatsThreads;
+
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kSThreads) void softmax_stats_kernel(
+__global__ __launch_bounds__(kStatsThreads) void softmax_stats_kernel(
     const void* __restrict__ logits, const void* __restrict__ root_logits, int total_nodes,
     int V, float kc, float2* __restrict__ stats) {
-  const int r = blockIdx.x;
+  const int r = blockIdx.x / kStatsSplit;
+  const int t = (blockIdx.x % kStatsSplit) * kStatsThreads + threadIdx.x;   // run index
   const size_t esz = BF16 ? 2 : 4;
   const void* row = r < total_nodes
                         ? static_cast<const void*>(static_cast<const unsigned char*>(logits) +
@@ -238,8 +246,7 @@ __global__ __launch_bounds__(kSThreads) void softmax_stats_kernel(
                         : static_cast<const void*>(static_cast<const unsigned char*>(root_logits) +
                                                    (size_t)(r - total_nodes) * V * esz);
   const int C = run_len(V);
-  const int tid = threadIdx.x;
-  const int r0 = tid * C;
+  const int r0 = t * C;
   const int r1 = min(V, r0 + C);
   float m, s;
   run_stats<BF16, VEC>(row, r0, r1, V, kc, m, s);
@@ -249,8 +256,8 @@ __global__ __launch_bounds__(kSThreads) void softmax_stats_kernel(
     merge_ms(m, s, m2, s2);
   }
   const int nseg = (V + kRunsPerSeg * C - 1) / (kRunsPerSeg * C);
-  if ((tid & (kRunsPerSeg - 1)) == 0 && tid / kRunsPerSeg < nseg)
-    stats[(size_t)r * kMaxSeg + tid / kRunsPerSeg] = make_float2(m, s);
+  if ((t & (kRunsPerSeg - 1)) == 0 && t / kRunsPerSeg < nseg)
+    stats[(size_t)r * kMaxSeg + t / kRunsPerSeg] = make_float2(m, s);
 }
 
 template <bool BF16, bool VEC>
@@ -265,6 +272,8 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
     float* __restrict__ scratch, const float2* __restrict__ stats) {
   __shared__ int32_t par[TA_MAX_NODES];
   __shared__ int32_t jmp[TA_MAX_NODES];
+  __shared__ int32_t s_tok[TA_MAX_NODES];   // the sequence's draft tokens
+  __shared__ float s_u[TA_MAX_NODES];       // and its uniforms
   __shared__ float segm[2][kMaxSeg];   // P's mass per segment (two copies, see sel)
   __shared__ float red[kSWaves];
   __shared__ float red2[kSWaves];
@@ -293,6 +302,8 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
     const int p = parents[n0 + i];
     par[i] = p;
     jmp[i] = p;
+    s_tok[i] = draft[n0 + i];
+    s_u[i] = u_accept[n0 + i];
     if (p < -1 || p >= nn || p == i) s_bad = 1;
   }
   __syncthreads();
@@ -349,16 +360,16 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
 
   // Implicit softmax of logits row r: max and sum merged from its segment
   // statistics, and the segment masses relative to that max.
-  auto softmax_of = [&](const void* row, int r) {
+  // This thread's segment statistics of logits row r (issued early, used by
+  // softmax_of).
+  auto load_stats = [&](int r) {
+    return tid < nseg ? stats[(size_t)r * kMaxSeg + tid] : make_float2(kNegInfS, 0.f);
+  };
+  auto softmax_of = [&](const void* row, float2 st) {
     Dist d;
     d.row = row;
     d.R = nullptr;
-    float m = kNegInfS, s = 0.f;
-    if (tid < nseg) {
-      const float2 st = stats[(size_t)r * kMaxSeg + tid];
-      m = st.x;
-      s = st.y;
-    }
+    const float m = st.x, s = st.y;
     float mm = wave_max_f(m);
     __syncthreads();
     if (lane == 0) red[wave] = mm;
@@ -374,7 +385,7 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
   };
 
   Dist P = softmax_of(static_cast<const unsigned char*>(root_logits) + (size_t)b * V * esz,
-                      total_nodes + b);
+                      load_stats(total_nodes + b));
   const float* Q = root_qp + (size_t)b * V;
   int cur = -1;     // current node (-1: above the roots)
   int after = -1;   // children of cur with index <= after are done
@@ -398,13 +409,14 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
     for (int w = 1; w < kSWaves; ++w) c = min(c, ired[w]);
     if (c >= nn) break;
     after = c;
-    const int x = draft[n0 + c];
-    bool take = false;
-    if (x >= 0 && x < V) {
-      const float qx = Q[x];
-      const float px = pchain(dist_at<BF16>(P, x, kc), qx, 1.f / P.Z, chain);
-      take = u_accept[n0 + c] * qx < px;
-    }
+    // The test's loads and, in the same round trip, the child's statistics
+    // (used if it is accepted).
+    const int x = s_tok[c];
+    const bool xin = x >= 0 && x < V;
+    const float qx = xin ? Q[x] : 0.f;
+    const float bx = xin ? dist_at<BF16>(P, x, kc) : 0.f;
+    const float2 cst = load_stats(n0 + c);
+    const bool take = xin && s_u[c] * qx < pchain(bx, qx, 1.f / P.Z, chain);
     if (take) {
       if (tid == 0) {
         an[len] = c;
@@ -414,8 +426,7 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
       cur = c;
       after = -1;
       chain = 0;
-      P = softmax_of(static_cast<const unsigned char*>(logits) + (size_t)(n0 + c) * V * esz,
-                     n0 + c);
+      P = softmax_of(static_cast<const unsigned char*>(logits) + (size_t)(n0 + c) * V * esz, cst);
       Q = qp + (size_t)(n0 + c) * V;
     } else {
       // Residual max(0, P - Q): its sum and segment masses (into the other
@@ -598,7 +609,8 @@ hipError_t launch_verify_sample(bool bf16, const void* logits, const void* root_
   const unsigned rows = (unsigned)(total_nodes + B);
 #define TA_SAMPLE_LAUNCH(BF, VC)                                                                \
   do {                                                                                         \
-    hipLaunchKernelGGL((softmax_stats_kernel<BF, VC>), dim3(rows), dim3(kSThreads), 0, stream, \
+    hipLaunchKernelGGL((softmax_stats_kernel<BF, VC>), dim3(rows * kStatsSplit),              \
+                       dim3(kStatsThreads), 0, stream,                                         \
                        logits, root_logits, total_nodes, V, kc, stats);                        \
     hipLaunchKernelGGL((spec_sample_kernel<BF, VC>), dim3(B), dim3(kSThreads), 0, stream,      \
                        logits, root_logits, draft_probs, root_draft_probs, draft, parents,     \
