@@ -274,6 +274,8 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
   __shared__ int32_t jmp[TA_MAX_NODES];
   __shared__ int32_t s_tok[TA_MAX_NODES];   // the sequence's draft tokens
   __shared__ float s_u[TA_MAX_NODES];       // and its uniforms
+  __shared__ float s_qx[TA_MAX_NODES];      // Q(x_i) and logit(x_i) in node i's parent's rows
+  __shared__ float s_lx[TA_MAX_NODES];
   __shared__ float segm[2][kMaxSeg];   // P's mass per segment (two copies, see sel)
   __shared__ float red[kSWaves];
   __shared__ float red2[kSWaves];
@@ -302,8 +304,20 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
     const int p = parents[n0 + i];
     par[i] = p;
     jmp[i] = p;
-    s_tok[i] = draft[n0 + i];
+    const int x = draft[n0 + i];
+    s_tok[i] = x;
     s_u[i] = u_accept[n0 + i];
+    // Each node is tested at most once, against its parent's rows: the two
+    // values its test reads come in one round trip for the whole tree.
+    float qx = 0.f, lx = kNegInfS;
+    if (x >= 0 && x < V && p >= -1 && p < nn) {
+      const size_t rowi = p < 0 ? (size_t)b : (size_t)(n0 + p);
+      qx = (p < 0 ? root_qp : qp)[rowi * V + x];
+      lx = logit<BF16>(static_cast<const unsigned char*>(p < 0 ? root_logits : logits) +
+                           rowi * V * esz, x);
+    }
+    s_qx[i] = qx;
+    s_lx[i] = lx;
     if (p < -1 || p >= nn || p == i) s_bad = 1;
   }
   __syncthreads();
@@ -413,8 +427,11 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
     // (used if it is accepted).
     const int x = s_tok[c];
     const bool xin = x >= 0 && x < V;
-    const float qx = xin ? Q[x] : 0.f;
-    const float bx = xin ? dist_at<BF16>(P, x, kc) : 0.f;
+    const float qx = s_qx[c];
+    // base(x): from the prefetched logit while P's base is the current node's
+    // row, read from the written-out residual otherwise
+    const float bx = !xin ? 0.f
+                     : P.row ? __builtin_amdgcn_exp2f(s_lx[c] * kc - P.m) : P.R[x];
     const float2 cst = load_stats(n0 + c);
     const bool take = xin && s_u[c] * qx < pchain(bx, qx, 1.f / P.Z, chain);
     if (take) {
