@@ -417,6 +417,26 @@ def summarize_profiles(root):
     if stats:
         with open(os.path.join(PROFILES, "tree_attn_step_llama3_8b_kernel_trace.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
+    # the calls outside the step (commit, next-token and stochastic verifiers)
+    extra = _read_csvs(os.path.join(root, "prof_trace_extra"), "kernel_stats.csv")
+    if extra:
+        lines = ["# Kernel trace: the standalone calls, Llama-3-8B-shaped step (N=64, V=128256)", "",
+                 "The same step as the main trace plus the calls timed beside it: the commit of",
+                 "the accepted path (`kv_commit_kernel`), the next-token verifier (the argmax over",
+                 "node and prefix rows, `path_select_kernel<true>`) and stochastic verification",
+                 "(`softmax_stats_kernel` over the 65 rows, then `spec_sample_kernel`).", "",
+                 "Command (run from the repository root on the MI355X box):", "",
+                 "    " + PROFILE_CMDS["prof_trace_extra"], "",
+                 "| kernel | calls | avg us | min us | max us | % |", "|---|---|---|---|---|---|"]
+        for r in extra:
+            if "ta::" not in r["Name"]:
+                continue
+            lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | "
+                         f"{float(r['AverageNs'])/1e3:.3f} | {float(r['MinNs'])/1e3:.3f} | "
+                         f"{float(r['MaxNs'])/1e3:.3f} | {float(r['Percentage']):.1f} |")
+        with open(os.path.join(PROFILES, "tree_attn_extra_calls_llama3_8b_kernel_trace.md"),
+                  "w") as f:
+            f.write("\n".join(lines) + "\n")
     # HBM traffic from FETCH_SIZE / WRITE_SIZE, scaled by the copy calibration
     cf = _pmc_means(os.path.join(root, "prof_calib_fetch"), "FETCH_SIZE")
     cw = _pmc_means(os.path.join(root, "prof_calib_write"), "WRITE_SIZE")
@@ -493,6 +513,9 @@ PROFILE_CMDS = {
     "prof_trace": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o run -- "
                   "python -u bench.py --steps 50 --warmup 5 --no-cpu-baseline --no-extra-calls "
                   "--no-m3",
+    "prof_trace_extra": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace_extra "
+                        "-o run -- python -u bench.py --steps 20 --warmup 2 --no-cpu-baseline "
+                        "--no-m3",
     "prof_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch_{name} -o run -- "
                   "python -u bench.py --config {name} --steps 10 --warmup 2 --no-cpu-baseline "
                   "--no-extra-calls --no-m3",
