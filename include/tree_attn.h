@@ -387,7 +387,7 @@ TA_API int tree_kv_commit(int dtype, const void* k_tree, const void* v_tree,
 
 /*
  * Bytes of device workspace tree_verify_sample needs: two fp32 rows of V per
- * sequence, then 256 (max, sum) float pairs per logits row (sum_N + B rows).
+ * sequence, then 260 (max, sum) float pairs per logits row (sum_N + B rows).
  * Pure host arithmetic.
  */
 TA_API size_t tree_verify_sample_workspace_size(int32_t B, int32_t total_nodes, int32_t V);

@@ -186,7 +186,7 @@ def test_verify_sample_host_validation(lib):
     #      dtype logits  root    q       q_root  draft   parents offsets B  N   maxn V
     ok = [1, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 2, 64, 64, 1000,
           #   T    u_acc    u_fin    alen     anodes   atok     bonus    ws       ws_bytes stream
-          0.7, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 151296, None]
+          0.7, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 153408, None]
     bad = list(ok); bad[0] = 5
     assert v(*bad) == 3
     for i in (2, 4, 7, 14, 15, 16, 17, 18):        # always required
@@ -198,14 +198,14 @@ def test_verify_sample_host_validation(lib):
     for t in (0.0, -1.0, float("nan"), float("inf")):
         bad = list(ok); bad[12] = t
         assert v(*bad) == 1, t
-    bad = list(ok); bad[20] = 151295                # rows and segment statistics
+    bad = list(ok); bad[20] = 153407                # rows and segment statistics
     assert v(*bad) == 4
     bad = list(ok); bad[19] = (1 << 20) + 8         # misaligned workspace
     assert v(*bad) == 4
     bad = list(ok); bad[10] = 5000
     assert v(*bad) == 3
-    # two fp32 rows of V per sequence (256-byte aligned), then 256 float2 per row
-    assert lib.tree_verify_sample_workspace_size(2, 64, 1000) == 16128 + 66 * 256 * 8
+    # two fp32 rows of V per sequence (256-byte aligned), then 260 float2 per row
+    assert lib.tree_verify_sample_workspace_size(2, 64, 1000) == 16128 + 66 * 260 * 8
     assert lib.tree_verify_sample_workspace_size(0, 64, 1000) == 0
 
 

@@ -117,7 +117,7 @@ hipError_t launch_kv_commit(const void* k_tree, const void* v_tree, const int32_
 
 // Stochastic verification (tree_verify_sample): segment statistics of every
 // logits row, then one workgroup per sequence; workspace = two fp32 rows of V
-// per sequence, then 256 (max, sum) pairs per logits row.
+// per sequence, then 256 + 4 (max, sum) pairs per logits row.
 size_t verify_sample_workspace_bytes(int B, int total_nodes, int V);
 hipError_t launch_verify_sample(bool bf16, const void* logits, const void* root_logits,
                                 const float* draft_probs, const float* root_draft_probs,

@@ -236,7 +236,8 @@ constexpr int kStatsSplit = kSThreads / kStatsThreads;
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kStatsThreads) void softmax_stats_kernel(
     const void* __restrict__ logits, const void* __restrict__ root_logits, int total_nodes,
-    int V, float kc, float2* __restrict__ stats) {
+    int V, float kc, float2* __restrict__ stats, float2* __restrict__ wgstats) {
+  __shared__ float2 wred[kStatsThreads / 64];
   const int r = blockIdx.x / kStatsSplit;
   const int t = (blockIdx.x % kStatsSplit) * kStatsThreads + threadIdx.x;   // run index
   const size_t esz = BF16 ? 2 : 4;
@@ -258,6 +259,29 @@ __global__ __launch_bounds__(kStatsThreads) void softmax_stats_kernel(
   const int nseg = (V + kRunsPerSeg * C - 1) / (kRunsPerSeg * C);
   if ((t & (kRunsPerSeg - 1)) == 0 && t / kRunsPerSeg < nseg)
     stats[(size_t)r * kMaxSeg + t / kRunsPerSeg] = make_float2(m, s);
+  // and this workgroup's quarter of the row as one pair (wgstats[r][q])
+  for (int o = kRunsPerSeg; o < 64; o <<= 1) {
+    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+    merge_ms(m, s, m2, s2);
+  }
+  if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = make_float2(m, s);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float bm = wred[0].x, bs = wred[0].y;
+    for (int w = 1; w < kStatsThreads / 64; ++w) merge_ms(bm, bs, wred[w].x, wred[w].y);
+    wgstats[(size_t)r * kStatsSplit + blockIdx.x % kStatsSplit] = make_float2(bm, bs);
+  }
+}
+
+// A row's (max, sum) from its four quarters.
+__device__ inline float2 row_stats(const float2* wgstats, size_t r) {
+  float m = kNegInfS, s = 0.f;
+#pragma unroll
+  for (int q = 0; q < kStatsSplit; ++q) {
+    const float2 p = wgstats[r * kStatsSplit + q];
+    merge_ms(m, s, p.x, p.y);
+  }
+  return make_float2(m, s);
 }
 
 template <bool BF16, bool VEC>
@@ -269,13 +293,16 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
     const float* __restrict__ u_accept, const float* __restrict__ u_final,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
     int32_t* __restrict__ accept_tokens, int32_t* __restrict__ bonus_token,
-    float* __restrict__ scratch, const float2* __restrict__ stats) {
+    float* __restrict__ scratch, const float2* __restrict__ stats,
+    const float2* __restrict__ wgstats) {
   __shared__ int32_t par[TA_MAX_NODES];
   __shared__ int32_t jmp[TA_MAX_NODES];
   __shared__ int32_t s_tok[TA_MAX_NODES];   // the sequence's draft tokens
   __shared__ float s_u[TA_MAX_NODES];       // and its uniforms
   __shared__ float s_qx[TA_MAX_NODES];      // Q(x_i) and logit(x_i) in node i's parent's rows
   __shared__ float s_lx[TA_MAX_NODES];
+  __shared__ float s_rm[TA_MAX_NODES];      // node i's own row: softmax max and sum
+  __shared__ float s_rz[TA_MAX_NODES];
   __shared__ float segm[2][kMaxSeg];   // P's mass per segment (two copies, see sel)
   __shared__ float red[kSWaves];
   __shared__ float red2[kSWaves];
@@ -318,6 +345,10 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
     }
     s_qx[i] = qx;
     s_lx[i] = lx;
+    // and node i's own row statistics, for when it is accepted
+    const float2 rs = row_stats(wgstats, (size_t)(n0 + i));
+    s_rm[i] = rs.x;
+    s_rz[i] = rs.y;
     if (p < -1 || p >= nn || p == i) s_bad = 1;
   }
   __syncthreads();
@@ -374,32 +405,21 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
 
   // Implicit softmax of logits row r: max and sum merged from its segment
   // statistics, and the segment masses relative to that max.
-  // This thread's segment statistics of logits row r (issued early, used by
-  // softmax_of).
-  auto load_stats = [&](int r) {
-    return tid < nseg ? stats[(size_t)r * kMaxSeg + tid] : make_float2(kNegInfS, 0.f);
-  };
-  auto softmax_of = [&](const void* row, float2 st) {
+  // Implicit softmax of a logits row from its (max, sum).  Its segment masses
+  // (segm) are filled only when the bonus is drawn from it (seg_fresh).
+  auto softmax_of = [&](const void* row, float m, float z) {
     Dist d;
     d.row = row;
     d.R = nullptr;
-    const float m = st.x, s = st.y;
-    float mm = wave_max_f(m);
-    __syncthreads();
-    if (lane == 0) red[wave] = mm;
-    __syncthreads();
-    mm = red[0];
-#pragma unroll
-    for (int w = 1; w < kSWaves; ++w) mm = fmaxf(mm, red[w]);
-    const float mass = (tid < nseg && m != kNegInfS) ? s * __builtin_amdgcn_exp2f(m - mm) : 0.f;
-    if (tid < kMaxSeg) segm[sel][tid] = mass;
-    d.m = mm;
-    d.Z = block_sum(mass, red);   // its barriers also publish segm
+    d.m = m;
+    d.Z = z;
     return d;
   };
-
+  bool seg_fresh = false;   // segm[sel] holds the masses of P
+  const float2 rootst = row_stats(wgstats, (size_t)(total_nodes + b));
   Dist P = softmax_of(static_cast<const unsigned char*>(root_logits) + (size_t)b * V * esz,
-                      load_stats(total_nodes + b));
+                      rootst.x, rootst.y);
+  int prow = total_nodes + b;   // logits row of P's implicit base
   const float* Q = root_qp + (size_t)b * V;
   int cur = -1;     // current node (-1: above the roots)
   int after = -1;   // children of cur with index <= after are done
@@ -432,7 +452,6 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
     // row, read from the written-out residual otherwise
     const float bx = !xin ? 0.f
                      : P.row ? __builtin_amdgcn_exp2f(s_lx[c] * kc - P.m) : P.R[x];
-    const float2 cst = load_stats(n0 + c);
     const bool take = xin && s_u[c] * qx < pchain(bx, qx, 1.f / P.Z, chain);
     if (take) {
       if (tid == 0) {
@@ -443,7 +462,10 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
       cur = c;
       after = -1;
       chain = 0;
-      P = softmax_of(static_cast<const unsigned char*>(logits) + (size_t)(n0 + c) * V * esz, cst);
+      P = softmax_of(static_cast<const unsigned char*>(logits) + (size_t)(n0 + c) * V * esz,
+                     s_rm[c], s_rz[c]);
+      prow = n0 + c;
+      seg_fresh = false;
       Q = qp + (size_t)(n0 + c) * V;
     } else {
       // Residual max(0, P - Q): its sum and segment masses (into the other
@@ -477,6 +499,7 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
       const float z = block_sum(s, red);   // its barriers also order the row's writes
       if (z > 0.f) {
         sel ^= 1;
+        seg_fresh = true;
         if (spill) {
           rsel ^= 1;
           P.row = nullptr;
@@ -502,6 +525,16 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
   // total, or inside the segment past its recomputed entries, the last entry
   // with mass of the last segment with mass is taken.
   __shared__ int s_seg;
+  if (!seg_fresh) {
+    // P is a row's softmax: its segment masses relative to the row's max
+    float mass0 = 0.f;
+    if (tid < nseg) {
+      const float2 st = stats[(size_t)prow * kMaxSeg + tid];
+      if (st.x != kNegInfS) mass0 = st.y * __builtin_amdgcn_exp2f(st.x - P.m);
+    }
+    if (tid < kMaxSeg) segm[sel][tid] = mass0;
+    __syncthreads();
+  }
   float mass = tid < nseg ? segm[sel][tid] : 0.f;
   float incl = mass;
   for (int o = 1; o < 64; o <<= 1) {
@@ -603,7 +636,7 @@ __global__ __launch_bounds__(kSThreads) void spec_sample_kernel(
 
 size_t verify_sample_workspace_bytes(int B, int total_nodes, int V) {
   const size_t rows = ((size_t)B * 2 * V * sizeof(float) + 255) & ~(size_t)255;
-  return rows + ((size_t)total_nodes + B) * kMaxSeg * sizeof(float2);
+  return rows + ((size_t)total_nodes + B) * (kMaxSeg + kStatsSplit) * sizeof(float2);
 }
 
 hipError_t launch_verify_sample(bool bf16, const void* logits, const void* root_logits,
@@ -620,6 +653,7 @@ hipError_t launch_verify_sample(bool bf16, const void* logits, const void* root_
   float2* stats = reinterpret_cast<float2*>(
       static_cast<unsigned char*>(workspace) +
       (((size_t)B * 2 * V * sizeof(float) + 255) & ~(size_t)255));
+  float2* wgstats = stats + ((size_t)total_nodes + B) * kMaxSeg;
   const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   const bool vec = V % 8 == 0 && a16(logits) && a16(root_logits) && a16(draft_probs) &&
                    a16(root_draft_probs) && a16(workspace);
@@ -628,11 +662,12 @@ hipError_t launch_verify_sample(bool bf16, const void* logits, const void* root_
   do {                                                                                         \
     hipLaunchKernelGGL((softmax_stats_kernel<BF, VC>), dim3(rows * kStatsSplit),              \
                        dim3(kStatsThreads), 0, stream,                                         \
-                       logits, root_logits, total_nodes, V, kc, stats);                        \
+                       logits, root_logits, total_nodes, V, kc, stats, wgstats);               \
     hipLaunchKernelGGL((spec_sample_kernel<BF, VC>), dim3(B), dim3(kSThreads), 0, stream,      \
                        logits, root_logits, draft_probs, root_draft_probs, draft, parents,     \
                        node_offsets, total_nodes, max_nodes, V, kc, u_accept, u_final,         \
-                       accept_len, accept_nodes, accept_tokens, bonus_token, scratch, stats);  \
+                       accept_len, accept_nodes, accept_tokens, bonus_token, scratch, stats,   \
+                       wgstats);                                                               \
   } while (0)
   if (bf16) {
     if (vec) TA_SAMPLE_LAUNCH(true, true);
