@@ -692,11 +692,15 @@ void fwd_bf16_kernel(KParams P) {
   int n_g = 0;               // gathered keys
   int g_lo = 0;              // the workgroup's first node (rows of s_gbits)
   bool compact = false, gather = false;
+  const bool sparse_tree = SKIP && !MR && sq.nn > 128 && t_hi > Lt;
+  if (sparse_tree) n_pre = max(0, min(t_hi, Lt) - t_lo);
+  // Run below: after the first stages are requested when those are all
+  // prefix tiles (their loads then overlap the mask reads), else before.
+  auto gather_setup = [&]() {
   if constexpr (SKIP && !MR) {
-    if (sq.nn > 128 && t_hi > Lt) {
+    {
       const int ta0 = max(t_lo, Lt) - Lt;   // the split's tree tiles: [ta0, ta0 + nt)
       const int nt = t_hi - Lt - ta0;
-      n_pre = max(0, min(t_hi, Lt) - t_lo);
       const int n_lo = row0 / P.G;
       const int nodes = rgn.n_hi - n_lo + 1;
       const uint64_t* mrows = P.mask + (size_t)(sq.n0 + n_lo) * P.W;
@@ -707,19 +711,34 @@ void fwd_bf16_kernel(KParams P) {
       const int nw = (k_hi + 63) / 64 - w_lo;
       for (int w = tid; w < nw; w += NT) s_u[w] = 0ull;
       __syncthreads();
-      // Union of the rows' words, four loads in flight per thread.
+      // Union of the rows' words.  When they fit (at most kHeld per thread,
+      // e.g. 64 nodes x 64 words) each thread loads its words once, all in
+      // flight together, and keeps them for the visibility bits below;
+      // otherwise two passes over memory, four loads in flight per thread.
       const int total = nodes * nw;
-      for (int q0 = 0; q0 < total; q0 += NT * 4) {
-        uint64_t v[4];
+      auto word_at = [&](int q) { return mrows[(size_t)(q / nw) * P.W + w_lo + q % nw]; };
+      constexpr int kHeld = 8;
+      const bool held = total <= NT * kHeld;
+      uint64_t vh[kHeld];
+      if (held) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int q = min(q0 + u * NT + tid, total - 1);
-          v[u] = mrows[(size_t)(q / nw) * P.W + w_lo + q % nw];
+        for (int u = 0; u < kHeld; ++u) {
+          const int q = u * NT + tid;
+          vh[u] = q < total ? word_at(q) : 0ull;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int q = q0 + u * NT + tid;
-          if (q < total && v[u]) atomicOr(&s_u[q % nw], (unsigned long long)v[u]);
+        for (int u = 0; u < kHeld; ++u)
+          if (vh[u]) atomicOr(&s_u[(u * NT + tid) % nw], (unsigned long long)vh[u]);
+      } else {
+        for (int q0 = 0; q0 < total; q0 += NT * 4) {
+          uint64_t v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = word_at(min(q0 + u * NT + tid, total - 1));
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int q = q0 + u * NT + tid;
+            if (q < total && v[u]) atomicOr(&s_u[q % nw], (unsigned long long)v[u]);
+          }
         }
       }
       __syncthreads();
@@ -765,26 +784,31 @@ void fwd_bf16_kernel(KParams P) {
         // Visibility bits: for each (row node, word) pair, each key the node
         // sees in the word (a node sees few keys, so few steps) set at its
         // position in the list: the word's start plus the union's bits below.
-        for (int q0 = 0; q0 < total; q0 += NT * 4) {
-          uint64_t v[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int q = min(q0 + u * NT + tid, total - 1);
-            v[u] = mrows[(size_t)(q / nw) * P.W + w_lo + q % nw];
+        auto set_bits = [&](int q, uint64_t v) {
+          const int nd = q / nw;
+          const int w = q % nw;
+          const uint64_t uu = s_u[w];
+          uint64_t vv = v & uu;
+          while (vv) {
+            const int b = __builtin_ctzll(vv);
+            vv &= vv - 1ull;
+            const int pos = s_ust[w] + __popcll(uu & ((1ull << b) - 1ull));
+            atomicOr(&s_gbits[nd * n_gt + (pos >> 5)], 1u << (pos & 31));
           }
+        };
+        if (held) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int q = q0 + u * NT + tid;
-            if (q >= total) continue;
-            const int nd = q / nw;
-            const int w = q % nw;
-            const uint64_t uu = s_u[w];
-            uint64_t vv = v[u] & uu;
-            while (vv) {
-              const int b = __builtin_ctzll(vv);
-              vv &= vv - 1ull;
-              const int pos = s_ust[w] + __popcll(uu & ((1ull << b) - 1ull));
-              atomicOr(&s_gbits[nd * n_gt + (pos >> 5)], 1u << (pos & 31));
+          for (int u = 0; u < kHeld; ++u)
+            if (vh[u]) set_bits(u * NT + tid, vh[u]);
+        } else {
+          for (int q0 = 0; q0 < total; q0 += NT * 4) {
+            uint64_t v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = word_at(min(q0 + u * NT + tid, total - 1));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int q = q0 + u * NT + tid;
+              if (q < total) set_bits(q, v[u]);
             }
           }
         }
@@ -819,7 +843,7 @@ void fwd_bf16_kernel(KParams P) {
       }
     }
   }
-  const int n_log = max(1, n_pre + (gather ? n_gt : n_act));
+  };
   // Tile of the split's li-th step: prefix tiles in order, then the gathered
   // or kept tree tiles; past the end, t_hi (loaded in bounds, masked as
   // inactive).
@@ -1010,7 +1034,6 @@ void fwd_bf16_kernel(KParams P) {
       voff[e] = (4 * hh + r) * kRow + (((4 * (e ^ r)) + clo) << 4) + 8 * (lane & 1);
   }
 
-  const int n_iter = (n_log + kTilesPerStage - 1) / kTilesPerStage;
 
   // S^T = K Q^T for one tile's 32 keys x this wave's 32 rows.  Accumulator v
   // of this lane holds key 8*(v/4) + 4*hh + v%4 of the tile.
@@ -1132,11 +1155,23 @@ void fwd_bf16_kernel(KParams P) {
   // retires them.
   uint32_t mw[4] = {0u, 0u, 0u, 0u};   // MR: this lane's mask row, 32 nodes per dword
   bool tree_bad = false;               // built mask: the sequence's parents are invalid
-  issue_aux();
-  issue_q();
+  const bool early = sparse_tree && n_pre >= kDepth * kTilesPerStage;
+  if (early) {
+    issue_aux();
+    issue_q();
 #pragma unroll
-  for (int k = 0; k < kDepth; ++k)
-    if (k < n_iter) issue_stage(k);
+    for (int k = 0; k < kDepth; ++k) issue_stage(k);
+  }
+  if (sparse_tree) gather_setup();
+  const int n_log = max(1, n_pre + (gather ? n_gt : n_act));
+  const int n_iter = (n_log + kTilesPerStage - 1) / kTilesPerStage;
+  if (!early) {
+    issue_aux();
+    issue_q();
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k)
+      if (k < n_iter) issue_stage(k);
+  }
   if constexpr (MR) {
     if (P.build) {
       // Wave 0's parent loads were issued first: wait for them alone (the
