@@ -436,7 +436,7 @@ TA_API size_t tree_verify_sample_workspace_size(int32_t B, int32_t total_nodes, 
  * two sides of a test, or u_final and a cumulative boundary, are within
  * rounding of each other).  A tree with an out-of-range parent or a cycle,
  * or a sequence whose offsets do not decode, is walked as empty.  Asynchronous
- * on `stream`: one workgroup per logits row computes its softmax statistics
+ * on `stream`: four workgroups per logits row compute its softmax statistics
  * per vocabulary segment, then one workgroup per sequence walks the tree.
  */
 TA_API int tree_verify_sample(int logits_dtype, const void* logits, const void* root_logits,
