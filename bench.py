@@ -153,6 +153,9 @@ def _probes():
     lib.ta_probe_valu.restype = ctypes.c_int
     lib.ta_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                   ctypes.c_void_p]
+    lib.ta_probe_lds.restype = ctypes.c_int
+    lib.ta_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p]
     return lib
 
 
@@ -201,6 +204,18 @@ def compute_ceiling():
         instr = grid * 8 * 8 * iters   # wave64 instructions
         out[name] = {"s": t, "wave_instr_per_s": instr / t,
                      "cycles_per_wave_instr_per_simd": round(SIMDS * CLOCK_HZ * t / instr, 2)}
+    # LDS: 16-byte reads alone, then each feeding an MFMA (the score step's pattern).
+    iters = 4096
+    for op, name in ((0, "lds_read_b128"), (1, "mfma_from_lds")):
+        t = timed(lambda: check(probes.ta_probe_lds(grid, iters, op, sink.data_ptr(),
+                                                    stream.cuda_stream), "ta_probe_lds"))
+        reads = grid * 8 * 8 * iters   # wave64 16-byte reads, 1 KB each
+        rec = {"s": t, "bytes_per_clk_per_cu": round(reads * 1024 / t / 256 / CLOCK_HZ, 1)}
+        if op == 1:
+            flops = reads * 32768
+            rec.update({"TFLOPs": round(flops / t / 1e12, 1),
+                        "frac_of_2500": round(flops / t / 2.5e15, 3)})
+        out[name] = rec
     print(json.dumps({"compute_ceiling": out}))
 
 
@@ -220,6 +235,17 @@ def summarize_compute(path):
              f"instr/s | {fma['cycles_per_wave_instr_per_simd']} |",
              f"| `v_exp_f32` (exp2), 8 chains per thread | {ex['wave_instr_per_s'] / 1e12:.2f} T wave "
              f"instr/s | {ex['cycles_per_wave_instr_per_simd']} |"]
+    if "lds_read_b128" in rec:
+        lr, ml = rec["lds_read_b128"], rec["mfma_from_lds"]
+        lines += ["", "LDS (`ta_probe_lds`, same grid): 16-byte reads with no bank conflicts, eight "
+                  "in flight per wave; then the same reads each feeding one "
+                  "`v_mfma_f32_32x32x16_bf16` as its A operand (two accumulator chains per wave, "
+                  "B in registers), the attention's score-step pattern.", "",
+                  "| probe | rate | LDS bytes per clock per CU (2.4 GHz) |", "|---|---|---|",
+                  f"| LDS reads alone | {lr['bytes_per_clk_per_cu'] * 256 * CLOCK_HZ / 1e12:.1f} TB/s "
+                  f"| {lr['bytes_per_clk_per_cu']} |",
+                  f"| MFMA fed from LDS | {ml['TFLOPs']} TFLOP/s ({ml['frac_of_2500']} of 2.5 "
+                  f"PFLOP/s) | {ml['bytes_per_clk_per_cu']} |"]
     with open(os.path.join(PROFILES, "compute_ceiling.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))

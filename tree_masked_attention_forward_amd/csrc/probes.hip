@@ -10,6 +10,11 @@
 //   ta_probe_mfma   back-to-back independent v_mfma_f32_32x32x16_bf16 chains:
 //                   the matrix units' sustained bf16 rate.
 //   ta_probe_valu   independent fp32 FMA or exp2 chains: VALU issue rates.
+//   ta_probe_lds    16-byte LDS reads with no bank conflicts (op 0), or the
+//                   same reads each feeding a v_mfma_f32_32x32x16_bf16 as its
+//                   A operand, eight per 32x128 tile as the attention's score
+//                   step does (op 1): the LDS read rate, and the matrix rate
+//                   when every operand tile comes from LDS.
 //
 // None is on the tree attention path.  Each returns 0, or the HIP error.
 #include <hip/hip_runtime.h>
@@ -96,6 +101,51 @@ __global__ __launch_bounds__(512) void valu_kernel(int iters, int op, float* __r
   if (t == 1.2345f) sink[blockIdx.x] = t;
 }
 
+// LDS reads.  Each wave walks 64 KB of LDS in 1 KB steps (lane i reads bytes
+// 16i .. 16i+15 of the step: consecutive lanes, consecutive banks); eight
+// reads per iteration, each from its own KB.  op 0 XOR-folds the data; op 1
+// passes each read to an MFMA (two accumulator chains, B operand fixed in
+// registers), the pattern of the attention's score step.
+constexpr int kLdsProbeBytes = 64 * 1024;
+
+__global__ __launch_bounds__(512) void lds_kernel(int iters, int op, float* __restrict__ sink) {
+  __shared__ __align__(16) unsigned char buf[kLdsProbeBytes];
+  for (int i = threadIdx.x * 16; i < kLdsProbeBytes; i += 512 * 16)
+    *reinterpret_cast<u32x4_t*>(buf + i) =
+        u32x4_t{(unsigned)i, (unsigned)i * 3u, (unsigned)i ^ 0x3c00u, 0x3c003c00u};
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  unsigned off = (unsigned)(wave * 8 * 1024) % kLdsProbeBytes;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  bf16x8_t b;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) b[k] = (__bf16)(0.001f * (lane + k));
+  f32x16_t c0 = {}, c1 = {};
+  for (int i = 0; i < iters; ++i) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      v[k] = *reinterpret_cast<const u32x4_t*>(buf + ((off + k * 1024u) % kLdsProbeBytes) + lane * 16);
+    if (op == 0) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc ^= v[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; k += 2) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v[k]), b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v[k + 1]), b, c1,
+                                                     0, 0, 0);
+      }
+    }
+    off = (off + 8u * 1024u) % kLdsProbeBytes;
+  }
+  float t = (float)(acc.x ^ acc.y ^ acc.z ^ acc.w);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) t += c0[v] + c1[v];
+  if (t == 1.2345f) sink[blockIdx.x] = t;   // keeps the work live; never true in practice
+}
+
 }  // namespace
 
 // src: device buffer of `bytes` bytes (16-byte aligned; bytes a multiple of
@@ -134,6 +184,17 @@ PROBE_API int ta_probe_valu(int grid, int iters, int op, void* sink, void* strea
   if (grid < 1 || grid > (1 << 20) || iters < 1 || (op != 0 && op != 1) || !sink)
     return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(valu_kernel, dim3((unsigned)grid), dim3(512), 0,
+                     static_cast<hipStream_t>(stream), iters, op, static_cast<float*>(sink));
+  return (int)hipGetLastError();
+}
+
+// grid workgroups of 512 threads (8 waves, two per SIMD), each wave issuing
+// 8 * iters 16-byte LDS reads (1 KB per wave instruction), op 0 alone, op 1
+// each feeding one 32x32x16 MFMA.  sink: grid floats.
+PROBE_API int ta_probe_lds(int grid, int iters, int op, void* sink, void* stream) {
+  if (grid < 1 || grid > (1 << 20) || iters < 1 || (op != 0 && op != 1) || !sink)
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(lds_kernel, dim3((unsigned)grid), dim3(512), 0,
                      static_cast<hipStream_t>(stream), iters, op, static_cast<float*>(sink));
   return (int)hipGetLastError();
 }
