@@ -7,7 +7,7 @@
 // Chen et al. 2023) walked child by child down the tree, as in SpecInfer's
 // multi-step speculative sampling (Miao et al. 2024).
 //
-// Two kernels.  softmax_stats_kernel (one workgroup per logits row, all rows
+// Two kernels.  softmax_stats_kernel (four workgroups per logits row, all rows
 // at once) leaves, for every row, the softmax statistics of each vocabulary
 // segment: (max, sum of exp2 relative to it) in log2 units at the given
 // temperature.  spec_sample_kernel (one workgroup per sequence) then walks the
@@ -224,8 +224,6 @@ __device__ inline void run_stats(const void* row, int r0, int r1, int V, float k
 
 __device__ inline int run_len(int V) { return ((V + kSThreads - 1) / kSThreads + 7) / 8 * 8; }
 
-// Segment statistics of every logits row: row r < total_nodes is node row r,
-// the rest are the prefix rows.  stats[r][k] = (max, sum) of segment k.
 // Segment statistics of every logits row: row r < total_nodes is node row r,
 // the rest are the prefix rows.  stats[r][k] = (max, sum) of segment k.  Four
 // 256-thread workgroups per row, workgroup q taking runs 256q .. 256q + 255
