@@ -1493,25 +1493,32 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
   const long long item0 = item_index(P, b, g, 0, r);
   const long long split_stride = item_index(P, b, g, 1, r) - item0;
 
-  // The partial slots do not depend on the offsets: issue the loads of the
-  // first kPre splits before decoding the sequence, so both round trips
-  // overlap.  Slots past this row tile's split count are never written by
-  // this call and are ignored below.
+  // The partial slots do not depend on the offsets: with equal prefix
+  // lengths (every group split alike) issue the loads of the first kPre
+  // splits before decoding the sequence, so both round trips overlap.  Slots
+  // past this row tile's split count are never written by this call and are
+  // ignored below.  A ragged batch leaves many groups whole (nothing to
+  // merge), so there the loads wait for the decode instead of fetching slots
+  // no one wrote.
   constexpr int kPre = 8;
   float2 ml[kPre];
   u32x2_t h[kPre][4];
   auto oslot = [&](long long it, int e) {
     return (((size_t)it * RG + rg) * 16 + 4 * e + j) * 64 + lane;
   };
+  auto load_first = [&](int n) {
 #pragma unroll
-  for (int k = 0; k < kPre; ++k) {
-    if (k < P.S) {
-      const long long it = item0 + k * split_stride;
-      ml[k] = P.ws_ml[(size_t)it * P.rows_wg + rl];
+    for (int k = 0; k < kPre; ++k) {
+      if (k < n) {
+        const long long it = item0 + k * split_stride;
+        ml[k] = P.ws_ml[(size_t)it * P.rows_wg + rl];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) h[k][e] = P.ws_o[oslot(it, e)];
+        for (int e = 0; e < 4; ++e) h[k][e] = P.ws_o[oslot(it, e)];
+      }
     }
-  }
+  };
+  const bool early = P.piece == 0;
+  if (early) load_first(P.S);
 
   Seq sq;
   if (!decode_seq(P, b, sq)) return;
@@ -1520,6 +1527,7 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(KParams P) {
   if (rgn.Sb <= 1 || rl >= rgn.rows_here) return;
   const float c2 = P.scale_log2;
   const int Sb = rgn.Sb;
+  if (!early) load_first(Sb);
 
   MergeAcc ma[4];
 #pragma unroll
