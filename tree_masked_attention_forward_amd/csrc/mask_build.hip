@@ -40,8 +40,12 @@
 namespace ta {
 namespace {
 
+// Threads per workgroup: 256, or 1024 for trees whose rows span more than
+// 2048 (node, word) pairs (e.g. 512 nodes of 8 words), so every pointer-
+// jumping round takes a few steps per thread.
 constexpr int kThreads = 256;
-constexpr int kPerThread = kLdsTreeMaxNodes / kThreads;
+constexpr int kThreadsWide = 1024;
+constexpr int kWideFrom = 2048;
 
 __device__ inline uint64_t lds_load(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -50,10 +54,12 @@ __device__ inline void lds_store(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-__global__ __launch_bounds__(kThreads) void build_mask_kernel(
+template <int NT>
+__global__ __launch_bounds__(NT) void build_mask_kernel(
     const int32_t* __restrict__ parents, const int32_t* __restrict__ node_offsets,
     int total_nodes, int max_nodes, int W, uint64_t* __restrict__ mask,
     int32_t* __restrict__ depth, int32_t* __restrict__ status) {
+  constexpr int kPerThread = (kLdsTreeMaxNodes + NT - 1) / NT;
   extern __shared__ uint64_t smem[];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -63,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
   int pv[kPerThread];
 #pragma unroll
   for (int k = 0; k < kPerThread; ++k) {
-    const int i = tid + k * kThreads;
+    const int i = tid + k * NT;
     pv[k] = (b == 0 && i < spec_n) ? parents[i] : -1;
   }
   const int n0 = node_offsets[b];
@@ -76,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
   if (b != 0 || n0 != 0) {
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
-      const int i = tid + k * kThreads;
+      const int i = tid + k * NT;
       pv[k] = i < n ? parents[n0 + i] : -1;
     }
   }
@@ -88,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
   int any = 0;
 #pragma unroll
   for (int k = 0; k < kPerThread; ++k) {
-    const int i = tid + k * kThreads;
+    const int i = tid + k * NT;
     if (i < n) {
       const int p = pv[k];
       bad |= (p < -1 || p >= n || p == i);
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
   }
   bad = __syncthreads_or(bad);
   auto invalid = [&]() {
-    for (int i = tid; i < n; i += kThreads) {
+    for (int i = tid; i < n; i += NT) {
       for (int w = 0; w < W; ++w) mask[(size_t)(n0 + i) * W + w] = 0ull;
       if (depth) depth[n0 + i] = -1;
     }
@@ -122,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
       invalid();
       return;
     }
-    for (int idx = tid; idx < n * W; idx += kThreads) {
+    for (int idx = tid; idx < n * W; idx += NT) {
       const int i = idx / W;
       const int j = jcur[i];
       if (j >= 0) {
@@ -131,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
       }
     }
     int more = 0;
-    for (int i = tid; i < n; i += kThreads) {
+    for (int i = tid; i < n; i += NT) {
       const int j = jcur[i];
       const int jj = j >= 0 ? jcur[j] : -1;
       jnext[i] = jj;
@@ -143,9 +149,9 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(
     jnext = t;
   }
 
-  for (int idx = tid; idx < n * W; idx += kThreads) mask[(size_t)n0 * W + idx] = rows[idx];
+  for (int idx = tid; idx < n * W; idx += NT) mask[(size_t)n0 * W + idx] = rows[idx];
   if (depth)
-    for (int i = tid; i < n; i += kThreads) {
+    for (int i = tid; i < n; i += NT) {
       int c = 0;
       for (int w = 0; w < W; ++w) c += __popcll(rows[i * W + w]);
       depth[n0 + i] = c - 1;
@@ -252,13 +258,18 @@ hipError_t launch_build_mask(const int32_t* parents, const int32_t* node_offsets
     return hipGetLastError();
   }
   const size_t lds = (size_t)max_nodes * W * sizeof(uint64_t) + 2 * (size_t)max_nodes * sizeof(int32_t);
-  if (lds > 64 * 1024) {
-    hipError_t e = raise_dynamic_lds(reinterpret_cast<const void*>(&build_mask_kernel), (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(build_mask_kernel, dim3(B), dim3(kThreads), lds, stream, parents,
-                     node_offsets, total_nodes, max_nodes, W, mask, depth, status);
-  return hipGetLastError();
+  auto launch = [&](auto kernel, int threads) -> hipError_t {
+    if (lds > 64 * 1024) {
+      hipError_t e = raise_dynamic_lds(reinterpret_cast<const void*>(kernel), (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kernel, dim3(B), dim3(threads), lds, stream, parents, node_offsets,
+                       total_nodes, max_nodes, W, mask, depth, status);
+    return hipGetLastError();
+  };
+  if ((long long)max_nodes * W > kWideFrom)
+    return launch(&build_mask_kernel<kThreadsWide>, kThreadsWide);
+  return launch(&build_mask_kernel<kThreads>, kThreads);
 }
 
 }  // namespace ta
