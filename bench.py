@@ -72,6 +72,12 @@ def parse():
                    help="time the MFMA and VALU rate probes and print one JSON line")
     p.add_argument("--summarize-compute", metavar="FILE",
                    help="write profiles/compute_ceiling.md from the --compute-ceiling output in FILE")
+    p.add_argument("--timeline", metavar="WORKLOAD",
+                   help="per-workgroup timeline of one forward call on WORKLOAD from the timeline "
+                        "build (build.py --timeline); print one JSON line")
+    p.add_argument("--summarize-timeline", metavar="DIR",
+                   help="write profiles/tree_attn_forward_timeline.md from the --timeline outputs "
+                        "(timeline_*.json) in DIR")
     p.add_argument("--no-m3", action="store_true",
                    help="skip the one-node-tree variant of the workload")
     p.add_argument("--calib-copy", action="store_true",
@@ -247,6 +253,155 @@ def summarize_compute(path):
                   f"| MFMA fed from LDS | {ml['TFLOPs']} TFLOP/s ({ml['frac_of_2500']} of 2.5 "
                   f"PFLOP/s) | {ml['bytes_per_clk_per_cu']} |"]
     with open(os.path.join(PROFILES, "compute_ceiling.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+TIMELINE_CMD = "python -u bench.py --timeline {name} > gpurun_out/timeline_{name}.json"
+TIMELINE_WORKLOADS = ["llama3_8b", "batched", "llama3_70b", "tree_4096"]
+
+
+def timeline(name):
+    """Per-workgroup timeline of one tree_attn_mask_and_forward call on a
+    workload, from the timeline build of the library (csrc/attn_fwd.hip with
+    TA_TIMELINE: thread 0 of every forward workgroup stamps a 100 MHz counter
+    at fixed points, see the slot list there).  Twelve input copies rotate in
+    a captured graph, as the benchmark replays them; the stamps are those of
+    the graph's last call."""
+    import ctypes
+    import numpy as np
+    import torch
+    import synthetic
+    import tree_masked_attention_forward_amd  # noqa: F401  (loads the library first)
+    import tree_masked_attention_forward_amd._binding as tb
+    path = os.path.join(ROOT, "tree_masked_attention_forward_amd", "libtreeattn_timeline.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: run tree_masked_attention_forward_amd/build.py "
+                         "--timeline")
+    lib = tb.load_library(path)
+    tb._lib = lib   # the binding's calls now go to the timeline build
+    lib.ta_timeline_set.restype = ctypes.c_int
+    lib.ta_timeline_set.argtypes = [ctypes.c_void_p, ctypes.c_longlong]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = synthetic.make_config_case(name, with_logits=False)
+    cap = 1 << 16
+    buf = torch.zeros(cap * 16, dtype=torch.int64, device=dev)
+    sets = []
+    for _ in range(12):
+        sets.append((torch.from_numpy(case.parents).to(dev), case.q.to(dev), case.k_tree.to(dev),
+                     case.v_tree.to(dev), case.k_prefix.to(dev), case.v_prefix.to(dev),
+                     torch.from_numpy(case.prefix_offsets).to(dev),
+                     torch.from_numpy(case.node_offsets).to(dev)))
+    n = tb.forward_workspace_size(torch.bfloat16, case.B, case.total_nodes, case.max_nodes,
+                                  case.Hq, case.Hkv, case.D, case.total_prefix, case.max_prefix)
+    ws = torch.zeros(max(n, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(sets[0][1])
+
+    def call(i):
+        tb.mask_and_forward(*sets[i % len(sets)], case.max_nodes, case.max_prefix, case.scale,
+                            out=out, workspace=ws)
+    for i in range(30):
+        call(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(len(sets)):
+            call(i)
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    if lib.ta_timeline_set(buf.data_ptr(), cap) != 0:
+        raise SystemExit("ta_timeline_set failed")
+    buf.zero_()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    lib.ta_timeline_set(None, 0)
+    t = buf.view(cap, 16).cpu().numpy().astype(np.int64)
+    t = t[t[:, 0] != 0]
+    print(json.dumps({"timeline": {"workload": name, **timeline_summary(t)}}))
+
+
+def timeline_summary(t):
+    """Percentiles (us from the call's first workgroup start) of each stamp,
+    and the per-CU picture (CU from HW_REG_HW_ID bits: CU 8-11, SH 12, SE 13-15)."""
+    import numpy as np
+    kind = t[:, 6] & 255
+    sp, mg = kind == 1, kind == 2
+    t0 = t[:, 0].min()
+
+    def us(c):
+        return (t[:, c] - t0) / 100.0
+
+    def pct(x):
+        x = np.asarray(x, dtype=float)
+        if x.size == 0:
+            return None
+        return {q: round(float(np.percentile(x, p)), 2)
+                for q, p in (("p0", 0), ("p10", 10), ("p50", 50), ("p90", 90), ("p100", 100))}
+    tiles = t[:, 14] & 0xffff
+    end_split = us(5)[sp]
+    res = {"workgroups": int(len(t)), "splits": int(sp.sum()), "merge_workgroups": int(mg.sum()),
+           "span_us": round(float(us(5).max()), 2),
+           "split": {"start": pct(us(0)[sp]), "offsets_decoded": pct(us(1)[sp]),
+                     "first_stage": pct(us(2)[sp]), "loop_done": pct(us(3)[sp]),
+                     "end": pct(end_split),
+                     "loop_us_per_tile": pct((us(3) - us(2))[sp] / np.maximum(tiles[sp], 1)),
+                     "before_loop_us": pct((us(2) - us(0))[sp]),
+                     "after_loop_us": pct((us(5) - us(3))[sp])}}
+    if mg.any():
+        res["merge"] = {"start": pct(us(0)[mg]), "group_seen_complete": pct(us(4)[mg]),
+                        "end": pct(us(5)[mg])}
+    hw = t[:, 15]
+    xcc = (t[:, 6] >> 8) & 255
+    cu = xcc * 1000 + ((hw >> 13) & 7) * 100 + ((hw >> 12) & 1) * 16 + ((hw >> 8) & 15)
+    ends, ntiles, nwg = {}, {}, {}
+    for i in np.flatnonzero(sp):
+        k = int(cu[i])
+        ends[k] = max(ends.get(k, 0.0), float(us(5)[i]))
+        ntiles[k] = ntiles.get(k, 0) + int(tiles[i])
+        nwg[k] = nwg.get(k, 0) + 1
+    res["cus"] = {"used": len(ends), "split_workgroups_per_cu": pct(list(nwg.values())),
+                  "tiles_per_cu": pct(list(ntiles.values())),
+                  "last_split_end_per_cu": pct(list(ends.values()))}
+    return res
+
+
+def summarize_timeline(root):
+    recs = []
+    for name in TIMELINE_WORKLOADS:
+        path = os.path.join(root, f"timeline_{name}.json")
+        if os.path.exists(path):
+            with open(path) as f:
+                recs.append(json.loads(f.read().strip().splitlines()[-1])["timeline"])
+
+    def p(d, key="p50"):
+        return "" if d is None else f"{d[key]:.1f}"
+    lines = ["# Per-workgroup timeline of one forward call", "",
+             "Build and commands (repository root; the timeline build is "
+             "`csrc/attn_fwd.hip` compiled with `TA_TIMELINE`, whose workgroups stamp a 100 MHz "
+             "counter at fixed points; the product library has no trace code):", "",
+             "    python tree_masked_attention_forward_amd/build.py --timeline",
+             *["    " + TIMELINE_CMD.format(name=n) for n in TIMELINE_WORKLOADS], "",
+             "Times in microseconds from the call's first workgroup start, p50 over the split "
+             "workgroups (p10 / p90 where given); the last call of a replayed graph of twelve.", "",
+             "| workload | split wgs | offsets decoded | first stage in LDS | loop done | split end "
+             "(p50 / p100) | us per 32-key tile | before loop | merge wgs: group complete / end "
+             "(p50 / p100) | CUs: tiles per CU (p0 / p50 / p100) | call span |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in recs:
+        s = r["split"]
+        m = r.get("merge")
+        mtxt = (f"{p(m['group_seen_complete'])} / {p(m['end'])} / {p(m['end'], 'p100')}"
+                if m else "separate kernel")
+        c = r["cus"]["tiles_per_cu"]
+        lines.append(f"| {r['workload']} | {r['splits']} | {p(s['offsets_decoded'])} | "
+                     f"{p(s['first_stage'])} | {p(s['loop_done'])} | {p(s['end'])} / "
+                     f"{p(s['end'], 'p100')} | {s['loop_us_per_tile']['p50']:.3f} | "
+                     f"{p(s['before_loop_us'])} | {mtxt} | {c['p0']:.0f} / {c['p50']:.0f} / "
+                     f"{c['p100']:.0f} | {r['span_us']:.1f} |")
+    with open(os.path.join(PROFILES, "tree_attn_forward_timeline.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -729,6 +884,12 @@ def main():
         return
     if args.summarize_compute:
         summarize_compute(args.summarize_compute)
+        return
+    if args.timeline:
+        timeline(args.timeline)
+        return
+    if args.summarize_timeline:
+        summarize_timeline(args.summarize_timeline)
         return
     if args.summarize_ceiling:
         summarize_ceiling(args.summarize_ceiling, os.path.join(

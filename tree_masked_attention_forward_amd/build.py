@@ -1,6 +1,7 @@
 """Build libtreeattn.so in-tree with hipcc for gfx950.
 
     python tree_masked_attention_forward_amd/build.py
+    python tree_masked_attention_forward_amd/build.py --timeline   # the timeline build
 
 Each source is compiled to an object file in parallel, then linked into
 ``tree_masked_attention_forward_amd/libtreeattn.so``; the benchmark's
@@ -29,6 +30,10 @@ LIB = os.path.join(PKG, "libtreeattn.so")
 # The benchmark's measurement probes (streaming read, empty launch) live in a
 # library of their own, never loaded by the package.
 PROBE_LIB = os.path.join(PKG, "libtaprobes.so")
+# The timeline build (attn_fwd.hip with TA_TIMELINE: per-workgroup timestamps
+# of the forward kernel), a measurement tool that `bench.py --timeline` loads
+# in place of the library; built only on request (`build.py --timeline`).
+TIMELINE_LIB = os.path.join(PKG, "libtreeattn_timeline.so")
 PROBE_SOURCES = ["probes.hip"]
 SOURCES = ["api.cpp", "mask_build.hip", "attn_fwd.hip", "attn_fwd_f32.hip", "verify.hip",
            "kv_commit.hip", "sample.hip"]
@@ -57,13 +62,18 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-def _build_one(sources, lib, verbose):
+def build_timeline(verbose: bool = False) -> str:
+    _build_one(SOURCES, TIMELINE_LIB, verbose, {"attn_fwd.hip": ["-DTA_TIMELINE"]})
+    return TIMELINE_LIB
+
+
+def _build_one(sources, lib, verbose, defines=None):
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="treeattn_build_") as tmp:
         def one(src):
             obj = os.path.join(tmp, src + ".o")
-            cmd = [hipcc, *compile_flags(), *SOURCE_FLAGS.get(src, []), "-c",
-                   os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc, *compile_flags(), *SOURCE_FLAGS.get(src, []),
+                   *(defines or {}).get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
                 raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
@@ -84,4 +94,4 @@ def _build_one(sources, lib, verbose):
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build_timeline(verbose=True) if "--timeline" in sys.argv[1:] else build(verbose=True))

@@ -65,6 +65,29 @@
 #include <type_traits>
 
 namespace ta {
+
+// Timeline build (TA_TIMELINE defined: libtreeattn_timeline.so, a measurement
+// tool that `bench.py --timeline` loads; the product library has no trace
+// code).  Thread 0 of each workgroup of the forward kernel stamps
+// s_memrealtime (a 100 MHz counter) into 16 slots per workgroup:
+//   0 start, 1 offsets decoded, 2 first stage in LDS, 3 key loop done,
+//   4 arrival issued (split) or group seen complete (merge), 5 end,
+//   6 kind (1 split, 2 merge) | XCD << 8, 7 partial stores issued,
+//   14 key tiles walked | sequence << 16 | KV head << 24 | split << 32,
+//   15 HW_REG_HW_ID.
+#ifdef TA_TIMELINE
+__device__ unsigned long long* g_timeline = nullptr;
+__device__ long long g_timeline_cap = 0;
+#define TA_TL(slot, value)                                                              \
+  do {                                                                                \
+    if (g_timeline && threadIdx.x == 0 && (long long)blockIdx.x < g_timeline_cap)     \
+      g_timeline[(long long)blockIdx.x * 16 + (slot)] = (unsigned long long)(value);  \
+  } while (0)
+#define TA_TL_NOW() __builtin_amdgcn_s_memrealtime()
+#else
+#define TA_TL(slot, value) ((void)0)
+#endif
+
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -436,6 +459,7 @@ __device__ void merge_in_kernel(const KParams& P, long long m) {
     timed_out = n == kSpinMax;
   }
   __syncthreads();
+  TA_TL(4, TA_TL_NOW());
   const int xcc = xcc_id();
   const bool coherent = !timed_out && seen_word == group_complete(rgn.Sb, xcc, seen_epoch);
   // Every merge workgroup counts itself done as soon as it has seen its group
@@ -590,8 +614,13 @@ void fwd_bf16_kernel(KParams P) {
   const int hh = lane >> 5;   // lane half: which 8 of each 16 contraction elements
   const int l32 = lane & 31;
 
+  TA_TL(0, TA_TL_NOW());
+  TA_TL(15, (unsigned)__builtin_amdgcn_s_getreg(4 | (0 << 6) | (31 << 11)));
+  TA_TL(6, (unsigned)xcc_id() << 8);
   if (blockIdx.x >= P.n_split_blocks) {
+    TA_TL(6, 2u | ((unsigned)xcc_id() << 8));
     merge_in_kernel<RG, NW>(P, (long long)blockIdx.x - P.n_split_blocks);
+    TA_TL(5, TA_TL_NOW());
     return;
   }
 
@@ -648,6 +677,8 @@ void fwd_bf16_kernel(KParams P) {
   Range rgn;
   if (!row_tile_range(P, sq, r, rgn)) return;
   if (s >= rgn.Sb) return;
+  TA_TL(1, TA_TL_NOW());
+  TA_TL(6, 1u | ((unsigned)xcc_id() << 8));
   // In-kernel merge: this group's words, and its epoch, read now so that the
   // arrival after the key loop does not wait for it.
   unsigned long long* grp_word = nullptr;
@@ -1165,6 +1196,8 @@ void fwd_bf16_kernel(KParams P) {
   if (sparse_tree) gather_setup();
   const int n_log = max(1, n_pre + (gather ? n_gt : n_act));
   const int n_iter = (n_log + kTilesPerStage - 1) / kTilesPerStage;
+  TA_TL(14, (unsigned long long)n_log | ((unsigned long long)b << 16) |
+                ((unsigned long long)g << 24) | ((unsigned long long)s << 32));
   if (!early) {
     issue_aux();
     issue_q();
@@ -1234,6 +1267,7 @@ void fwd_bf16_kernel(KParams P) {
   int slot = 0;   // it % NS, kept in a scalar register
   for (int it = 0; it < n_iter; ++it) {
     wait_stage(it, n_iter);
+    if (it == 0) TA_TL(2, TA_TL_NOW());
     if (it == 0) {
       const unsigned char* qb = lds + Map::kQOff + rg * 32 * kRow;
 #pragma unroll
@@ -1292,6 +1326,7 @@ void fwd_bf16_kernel(KParams P) {
     }
     if (any) softmax_pv(sc, vbs);
   }
+  TA_TL(3, TA_TL_NOW());
   if (MR && P.build && g == 0 && s == 0) {
     // One writer per node: the workgroups of KV head 0 and split 0, the lane
     // holding the node's first query head.  An invalid tree's rows are zero,
@@ -1462,6 +1497,7 @@ void fwd_bf16_kernel(KParams P) {
     if (grp_word) {
       // Arrival: every thread's partial is in this XCD's L2 (its stores are
       // acknowledged) before the group's counter moves.
+      TA_TL(7, TA_TL_NOW());
       __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
       __syncthreads();
       // The epoch was requested before the key loop; the empty asm keeps the
@@ -1470,8 +1506,10 @@ void fwd_bf16_kernel(KParams P) {
       if (tid == 0)
         __hip_atomic_fetch_add(grp_word, arrival_word(xcc_id(), epoch), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
+      TA_TL(4, TA_TL_NOW());
     }
   }
+  TA_TL(5, TA_TL_NOW());
 }
 
 // Separate merge kernel: one workgroup per (sequence, KV head, row tile, row
@@ -1749,5 +1787,16 @@ hipError_t launch_forward_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t s
     default: return hipErrorInvalidValue;
   }
 }
+
+#ifdef TA_TIMELINE
+// Points the timeline at `buf` (cap workgroups of 16 uint64 slots), or turns
+// it off (buf null).  Synchronous; returns 0 or the HIP error.
+extern "C" __attribute__((visibility("default"))) int ta_timeline_set(unsigned long long* buf,
+                                                                      long long cap) {
+  hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(g_timeline), &buf, sizeof(buf));
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(g_timeline_cap), &cap, sizeof(cap));
+  return (int)e;
+}
+#endif
 
 }  // namespace ta
