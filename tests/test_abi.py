@@ -36,6 +36,50 @@ def test_library_exports_every_declared_symbol(lib):
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
 
 
+def test_product_library_carries_no_timeline_code(lib):
+    """The per-workgroup timestamps exist only in the timeline build
+    (libtreeattn_timeline.so, a measurement tool); the library the package
+    loads exports no timeline entry."""
+    assert not hasattr(lib, "ta_timeline_set")
+
+
+def test_timeline_summary_on_a_made_up_stamp_table():
+    """bench.py's timeline summary (host arithmetic only) on stamps whose
+    answers are known: 256 split workgroups with a 10 us loop over 8 tiles
+    on 16 CUs, and 128 merge workgroups."""
+    import importlib.util
+    import sys
+
+    import numpy as np
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    argv = sys.argv
+    try:
+        sys.argv = ["bench.py"]
+        spec.loader.exec_module(bench)
+    finally:
+        sys.argv = argv
+    n = 384
+    t = np.zeros((n, 16), np.int64)
+    t[:, 0] = 1000
+    t[:, 1] = t[:, 0] + 100        # 1 us
+    t[:, 2] = t[:, 1] + 300        # 4 us
+    t[:, 3] = t[:, 2] + 1000       # 14 us: a 10 us loop
+    t[:, 4] = t[:, 3] + 100
+    t[:, 5] = t[:, 4] + 100        # 16 us
+    t[:256, 6] = 1
+    t[256:, 6] = 2
+    t[:, 14] = 8
+    t[:, 15] = (np.arange(n) % 16) << 8
+    r = bench.timeline_summary(t)
+    assert r["splits"] == 256 and r["merge_workgroups"] == 128
+    assert r["span_us"] == 16.0
+    assert r["split"]["loop_us_per_tile"]["p50"] == 1.25
+    assert r["split"]["before_loop_us"]["p50"] == 4.0
+    assert r["cus"]["used"] == 16
+    assert r["cus"]["tiles_per_cu"]["p50"] == 16 * 8
+
+
 def test_status_strings(lib):
     from tree_masked_attention_forward_amd import _binding as b
     for code in range(6):
